@@ -1,0 +1,168 @@
+"""Plain fp64 CPU oracle for one tensor-parallel rank's layer share.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
+leg of the benchmark are the only users.  The product path never imports it.
+
+``oracle.c`` holds the arithmetic (fp64, increasing-index sums, OpenMP over
+independent outputs); this module only marshals numpy arrays to float64 and
+calls it through ctypes.  Functions take the FULL (unsharded) weights plus the
+rank (t, r) and cut the rank's block themselves, so their slicing is
+independent of the harness that prepares per-rank GPU buffers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import pathlib
+import subprocess
+
+import numpy as np
+
+HERE = pathlib.Path(__file__).resolve().parent
+SRC = HERE / "oracle.c"
+LIB = HERE / "liboracle.so"
+
+CFLAGS = ["-O2", "-fopenmp", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
+          "-shared", "-std=c11", "-Wall"]
+
+_i64 = ctypes.c_int64
+_pd = ctypes.POINTER(ctypes.c_double)
+_pi64 = ctypes.POINTER(ctypes.c_int64)
+
+
+def build(src: pathlib.Path = SRC, out: pathlib.Path = LIB) -> pathlib.Path:
+    """Compile the oracle with gcc (always recompiles)."""
+    tmp = out.with_suffix(".so.tmp")
+    subprocess.run(["gcc", *CFLAGS, str(src), "-o", str(tmp), "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library."""
+
+    def __init__(self, path: pathlib.Path | str = LIB):
+        path = pathlib.Path(path)
+        if not path.exists():
+            build(out=path)
+        self.lib = lib = ctypes.CDLL(str(path))
+        lib.orc_silu.restype = ctypes.c_double
+        lib.orc_silu.argtypes = [ctypes.c_double]
+        lib.orc_shard_range.restype = None
+        lib.orc_shard_range.argtypes = [_i64, _i64, _i64, _pi64, _pi64]
+        lib.orc_mlp_rank.restype = None
+        lib.orc_mlp_rank.argtypes = [_i64] * 5 + [_pd] * 6 + [_pi64, _i64]
+        lib.orc_reduce.restype = None
+        lib.orc_reduce.argtypes = [_i64, _i64, _pd, _pd]
+        lib.orc_qkv_rank.restype = None
+        lib.orc_qkv_rank.argtypes = [_i64] * 7 + [_pd] * 5
+        lib.orc_attn_core.restype = None
+        lib.orc_attn_core.argtypes = [_i64] * 5 + [_pd] * 2
+        lib.orc_oproj_rank.restype = None
+        lib.orc_oproj_rank.argtypes = [_i64] * 6 + [_pd] * 3
+
+    # ------------------------------------------------------------ helpers
+    @staticmethod
+    def _f64(a) -> np.ndarray:
+        return np.ascontiguousarray(a, dtype=np.float64)
+
+    @staticmethod
+    def _p(a: np.ndarray):
+        return a.ctypes.data_as(_pd)
+
+    # ------------------------------------------------------------ API
+    def silu(self, z: float) -> float:
+        return self.lib.orc_silu(float(z))
+
+    def shard_range(self, n: int, t: int, r: int):
+        lo, hi = ctypes.c_int64(), ctypes.c_int64()
+        self.lib.orc_shard_range(n, t, r, ctypes.byref(lo), ctypes.byref(hi))
+        return lo.value, hi.value
+
+    def mlp_rank(self, X, Wg, Wu, Wd, t: int = 1, r: int = 0, rows=None):
+        """Rank r's (H_r [I', F/t], P_r [I', D]) from full weights; rows selects
+        a subset of token rows (I' = len(rows)), None = all."""
+        X, Wg, Wu, Wd = (self._f64(a) for a in (X, Wg, Wu, Wd))
+        I, D = X.shape
+        F = Wg.shape[0]
+        assert Wg.shape == (F, D) and Wu.shape == (F, D) and Wd.shape == (D, F)
+        assert F % t == 0 and 0 <= r < t
+        if rows is None:
+            n_out, rp = I, None
+        else:
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+            assert rows.min() >= 0 and rows.max() < I
+            n_out, rp = len(rows), rows.ctypes.data_as(_pi64)
+        H = np.empty((n_out, F // t))
+        P = np.empty((n_out, D))
+        self.lib.orc_mlp_rank(I, D, F, t, r, self._p(X), self._p(Wg), self._p(Wu),
+                              self._p(Wd), self._p(H), self._p(P), rp, n_out)
+        return H, P
+
+    def mlp_full(self, X, Wg, Wu, Wd, rows=None):
+        return self.mlp_rank(X, Wg, Wu, Wd, 1, 0, rows)
+
+    def reduce(self, partials) -> np.ndarray:
+        P = self._f64(partials)
+        t = P.shape[0]
+        n = P[0].size
+        Y = np.empty(P.shape[1:])
+        self.lib.orc_reduce(t, n, self._p(P), self._p(Y))
+        return Y
+
+    def qkv_rank(self, X, Wq, Wk, Wv, n_q: int, n_kv: int, hd: int, t: int = 1,
+                 r: int = 0) -> np.ndarray:
+        X, Wq, Wk, Wv = (self._f64(a) for a in (X, Wq, Wk, Wv))
+        I, D = X.shape
+        assert Wq.shape == (n_q * hd, D) and Wk.shape == (n_kv * hd, D)
+        assert Wv.shape == (n_kv * hd, D)
+        assert n_q % t == 0 and n_kv % t == 0
+        N = (n_q // t + 2 * (n_kv // t)) * hd
+        out = np.empty((I, N))
+        self.lib.orc_qkv_rank(I, D, n_q, n_kv, hd, t, r, self._p(X), self._p(Wq),
+                              self._p(Wk), self._p(Wv), self._p(out))
+        return out
+
+    def attn_core(self, qkv, S: int, nq_l: int, nkv_l: int, hd: int) -> np.ndarray:
+        qkv = self._f64(qkv)
+        I = qkv.shape[0]
+        assert qkv.shape[1] == (nq_l + 2 * nkv_l) * hd and I % S == 0
+        A = np.empty((I, nq_l * hd))
+        self.lib.orc_attn_core(I, S, nq_l, nkv_l, hd, self._p(qkv), self._p(A))
+        return A
+
+    def oproj_rank(self, A_r, Wo, n_q: int, hd: int, t: int = 1, r: int = 0):
+        A_r, Wo = self._f64(A_r), self._f64(Wo)
+        I = A_r.shape[0]
+        D = Wo.shape[0]
+        assert Wo.shape == (D, n_q * hd) and A_r.shape[1] == (n_q // t) * hd
+        P = np.empty((I, D))
+        self.lib.orc_oproj_rank(I, D, n_q, hd, t, r, self._p(A_r), self._p(Wo),
+                                self._p(P))
+        return P
+
+    # ------------------------------------------------------------ chains
+    def attn_block_rank(self, X, Wq, Wk, Wv, Wo, n_q, n_kv, hd, S, t=1, r=0):
+        """QKV (column) -> attention core -> o_proj (row): rank r's partial."""
+        qkv = self.qkv_rank(X, Wq, Wk, Wv, n_q, n_kv, hd, t, r)
+        A = self.attn_core(qkv, S, n_q // t, n_kv // t, hd)
+        return qkv, A, self.oproj_rank(A, Wo, n_q, hd, t, r)
+
+
+_default: Oracle | None = None
+
+
+def get() -> Oracle:
+    """The oracle built from ``oracle.c`` in this directory."""
+    global _default
+    if _default is None:
+        _default = Oracle(LIB)
+    return _default
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle uses (OMP_NUM_THREADS, else all CPUs it may run on)."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env:
+        return int(env)
+    return len(os.sched_getaffinity(0))

@@ -1,0 +1,203 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle for one tensor-parallel rank's
+ * share of a Megatron-style transformer layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file: only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header or helper with the
+ * HIP library.
+ *
+ * Every value is read as the exact fp64 of its (bf16 or fp32) input and every
+ * sum runs in increasing index order in fp64.  There is no blocking, fusion or
+ * reordering: each output element is one plain loop.  OpenMP only spreads
+ * independent output elements over threads; it never splits a sum.
+ *
+ * Notation follows "Lecture 4 - Distributed Serving" (cs349e notes), §3.1:
+ * A[I_X, J] means dimension I of A is split over mesh axis X.  Weights are
+ * stored output-major, one contiguous K-vector per output channel, the way the
+ * vLLM ColumnParallelLinear keeps its [output_size_per_partition, input_size]
+ * parameter (intelliparadigm vLLM article, §2.1).  So a logical W[D, F] is the
+ * array Ws[F][D] with W[d, f] == Ws[f][d].
+ *
+ * Shards are contiguous blocks in rank order (the plainest reading of the
+ * "I/|X| rows per device" statement of §3.1): rank r of t owns
+ * [r*N/t, (r+1)*N/t) of a split dimension of size N.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* SiLU, the gate nonlinearity of the SwiGLU MLP (lecture §4.1 names SwiGLU
+ * but not its form; the Llama form silu(gate) * up is taken):
+ * silu(z) = z * sigmoid(z) = z / (1 + exp(-z)). */
+double orc_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* Contiguous rank block [lo, hi) of a dimension of size n split t ways. */
+void orc_shard_range(int64_t n, int64_t t, int64_t r, int64_t *lo, int64_t *hi) {
+  *lo = r * (n / t);
+  *hi = (r + 1) * (n / t);
+}
+
+/* Dot product of two K-vectors, increasing k, fp64. */
+static double dot(const double *a, const double *b, int64_t K) {
+  double s = 0.0;
+  for (int64_t k = 0; k < K; ++k) s += a[k] * b[k];
+  return s;
+}
+
+/*
+ * One rank's MLP share, lecture §4.1 ("MLP: column then row").
+ *   gate/up are column-parallel (case 1 of §3.2): rank r owns output columns
+ *   F_r of W_gate[D, F_X] and W_up[D, F_X], needs the replicated input, and
+ *   computes h[i, f] = silu(g) * u locally for f in F_r.
+ *   down is row-parallel (case 3 of §3.2): rank r owns rows F_r of
+ *   W_down[F_X, D] and produces the unreduced partial p_r[I, D]{U_X}.
+ *
+ * Full (unsharded) weights are passed; the rank indexes its block itself.
+ *   X   [I, D]
+ *   Wg  [F, D]   (stores logical W_gate[D, F])
+ *   Wu  [F, D]   (stores logical W_up[D, F])
+ *   Wd  [D, F]   (stores logical W_down[F, D])
+ *   H   [I, F/t] out: silu(x.Wg[:,f]) * (x.Wu[:,f]) for f in F_r
+ *   P   [I, D]   out: sum over f in F_r of H[i,f] * W_down[f, n]
+ * rows: optional list of nrows token rows to compute (NULL = all I rows);
+ * H and P are then [nrows, ...], in list order.
+ * With t = 1, r = 0 this is the unsharded layer.
+ */
+void orc_mlp_rank(int64_t I, int64_t D, int64_t F, int64_t t, int64_t r,
+                  const double *X, const double *Wg, const double *Wu,
+                  const double *Wd, double *H, double *P,
+                  const int64_t *rows, int64_t nrows) {
+  int64_t f0, f1;
+  orc_shard_range(F, t, r, &f0, &f1);
+  const int64_t Fl = f1 - f0;
+  const int64_t n_out = rows ? nrows : I;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t q = 0; q < n_out; ++q)
+    for (int64_t f = f0; f < f1; ++f) {
+      const int64_t i = rows ? rows[q] : q;
+      const double g = dot(X + i * D, Wg + f * D, D);
+      const double u = dot(X + i * D, Wu + f * D, D);
+      H[q * Fl + (f - f0)] = orc_silu(g) * u;
+    }
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t q = 0; q < n_out; ++q)
+    for (int64_t n = 0; n < D; ++n) {
+      double s = 0.0;
+      for (int64_t f = f0; f < f1; ++f) s += H[q * Fl + (f - f0)] * Wd[n * F + f];
+      P[q * D + n] = s;
+    }
+}
+
+/*
+ * Sum of the t rank partials in rank order 0..t-1: what the all-reduce after
+ * a row-parallel block delivers (lecture §3.3: all-reduce sums the partials;
+ * §4.3: the sharded result equals the single-device one up to the order of
+ * that sum).  partials [t, n] -> Y [n].
+ */
+void orc_reduce(int64_t t, int64_t n, const double *partials, double *Y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < n; ++j) {
+    double s = 0.0;
+    for (int64_t r = 0; r < t; ++r) s += partials[r * n + j];
+    Y[j] = s;
+  }
+}
+
+/*
+ * Column-parallel QKV projection split by heads, lecture §4.2: rank r owns
+ * query heads [r*nq/t, (r+1)*nq/t) and KV groups [r*nkv/t, (r+1)*nkv/t)
+ * (lecture §4.4: KV follows the heads while t <= number of groups).
+ *   X   [I, D]
+ *   Wq  [nq*hd, D], Wk [nkv*hd, D], Wv [nkv*hd, D]   (output-major)
+ *   out [I, (nq/t + 2*nkv/t)*hd], columns laid out [q heads | k heads | v heads]
+ */
+void orc_qkv_rank(int64_t I, int64_t D, int64_t nq, int64_t nkv, int64_t hd,
+                  int64_t t, int64_t r, const double *X, const double *Wq,
+                  const double *Wk, const double *Wv, double *out) {
+  int64_t q0, q1, g0, g1;
+  orc_shard_range(nq, t, r, &q0, &q1);
+  orc_shard_range(nkv, t, r, &g0, &g1);
+  const int64_t nql = q1 - q0, nkl = g1 - g0;
+  const int64_t Nq = nql * hd, Nk = nkl * hd, N = Nq + 2 * Nk;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t i = 0; i < I; ++i)
+    for (int64_t c = 0; c < N; ++c) {
+      const double *w;
+      if (c < Nq)
+        w = Wq + (q0 * hd + c) * D;
+      else if (c < Nq + Nk)
+        w = Wk + (g0 * hd + (c - Nq)) * D;
+      else
+        w = Wv + (g0 * hd + (c - Nq - Nk)) * D;
+      out[i * N + c] = dot(X + i * D, w, D);
+    }
+}
+
+/*
+ * Attention core of one rank (lecture §4.2: each device computes its own
+ * heads' attention completely).  Not on the projection hot path; it joins
+ * QKV to o_proj.  The pages do not fix its details; taken here: scaled dot
+ * product with scale 1/sqrt(hd), causal mask inside each sequence, no
+ * rotary embedding, grouped-query map: local head j reads local KV group
+ * floor(j * nkv_l / nq_l).  Tokens form I/S sequences of S consecutive rows.
+ *   qkv [I, (nq_l + 2*nkv_l)*hd] as produced by orc_qkv_rank
+ *   A   [I, nq_l*hd]
+ */
+void orc_attn_core(int64_t I, int64_t S, int64_t nql, int64_t nkl, int64_t hd,
+                   const double *qkv, double *A) {
+  const int64_t N = (nql + 2 * nkl) * hd;
+  const double scale = 1.0 / sqrt((double)hd);
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t i = 0; i < I; ++i)
+    for (int64_t j = 0; j < nql; ++j) {
+      const int64_t g = (j * nkl) / nql;
+      const int64_t s0 = (i / S) * S; /* first token of i's sequence */
+      const double *q = qkv + i * N + j * hd;
+      /* scores over the causal window s0..i, softmax with the max taken
+       * out first, then the probability-weighted sum of the values */
+      const int64_t L = i - s0 + 1;
+      double *w = (double *)malloc((size_t)L * sizeof(double));
+      double m = -INFINITY;
+      for (int64_t p = s0; p <= i; ++p) {
+        w[p - s0] = dot(q, qkv + p * N + nql * hd + g * hd, hd) * scale;
+        if (w[p - s0] > m) m = w[p - s0];
+      }
+      double den = 0.0;
+      for (int64_t p = 0; p < L; ++p) {
+        w[p] = exp(w[p] - m);
+        den += w[p];
+      }
+      for (int64_t c = 0; c < hd; ++c) {
+        double acc = 0.0;
+        for (int64_t p = s0; p <= i; ++p)
+          acc += (w[p - s0] / den) * qkv[p * N + (nql + nkl) * hd + g * hd + c];
+        A[i * (nql * hd) + j * hd + c] = acc;
+      }
+      free(w);
+    }
+}
+
+/*
+ * Row-parallel output projection, lecture §4.2: W_o is split by rows (its
+ * input dimension, the concatenated heads), so rank r multiplies its own
+ * heads' attention output by its row block of W_o and gets a partial
+ * p_r[I, D]{U_X}.
+ *   A_r [I, (nq/t)*hd]  this rank's attention output
+ *   Wo  [D, nq*hd]      output-major full weight (stores logical W_o[nq*hd, D])
+ *   P   [I, D]
+ */
+void orc_oproj_rank(int64_t I, int64_t D, int64_t nq, int64_t hd, int64_t t,
+                    int64_t r, const double *A_r, const double *Wo, double *P) {
+  int64_t q0, q1;
+  orc_shard_range(nq, t, r, &q0, &q1);
+  const int64_t Kl = (q1 - q0) * hd, K = nq * hd, c0 = q0 * hd;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t i = 0; i < I; ++i)
+    for (int64_t n = 0; n < D; ++n) {
+      double s = 0.0;
+      for (int64_t c = 0; c < Kl; ++c) s += A_r[i * Kl + c] * Wo[n * K + c0 + c];
+      P[i * D + n] = s;
+    }
+}

@@ -1,0 +1,47 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case copies oracle.c, plants one mistake by a text substitution (on the
+CPU, in a temporary directory), compiles the copy and runs every pin of
+test_oracle_pins against it: at least one pin has to fail.  The committed
+oracle itself is never modified."""
+import pathlib
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+MUTANTS = {
+    "gate_up_swapped": ("orc_silu(g) * u", "orc_silu(u) * g"),
+    "silu_sign": ("1.0 + exp(-z)", "1.0 + exp(z)"),
+    "dropped_last_k": ("for (int64_t k = 0; k < K; ++k)", "for (int64_t k = 0; k + 1 < K; ++k)"),
+    "down_shard_offset": ("Wd[n * F + f]", "Wd[n * F + (f - f0)]"),
+    "down_transposed": ("Wd[n * F + f]", "Wd[f * D + n]"),
+    "reduce_drops_rank": ("for (int64_t r = 0; r < t; ++r)", "for (int64_t r = 0; r + 1 < t; ++r)"),
+    "shard_start": ("*lo = r * (n / t);", "*lo = r * (n / t) + (r > 0);"),
+    "attn_no_scale": ("1.0 / sqrt((double)hd)", "1.0"),
+    "attn_not_causal_per_seq": ("const int64_t s0 = (i / S) * S;", "const int64_t s0 = 0;"),
+    "gqa_map": ("const int64_t g = (j * nkl) / nql;", "const int64_t g = j % nkl;"),
+    "qkv_k_from_v": ("w = Wk + (g0 * hd + (c - Nq)) * D;", "w = Wv + (g0 * hd + (c - Nq)) * D;"),
+    "oproj_offset": ("Wo[n * K + c0 + c]", "Wo[n * K + c]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path: pathlib.Path):
+    old, new = MUTANTS[name]
+    src = oracle.SRC.read_text()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = tmp_path / "oracle_mut.c"
+    mutated.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", *oracle.CFLAGS, str(mutated), "-o", str(lib), "-lm"], check=True)
+    mut = oracle.Oracle(lib)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mut)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"
