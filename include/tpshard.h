@@ -1,0 +1,158 @@
+/*
+ * tpshard.h -- C ABI of one tensor-parallel rank's share of a Megatron-style
+ * transformer layer, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the method (the pages this library follows):
+ *   [L4]  "Lecture 4 - Distributed Serving" (semidirectx.com, cs349e notes):
+ *         §3.1 sharding notation A[I_X, J]; §3.2 the four sharded-matmul
+ *         cases, case 1 (contracting dim unsplit: local, no communication)
+ *         and case 3 (contracting dim split the same way on both operands:
+ *         local partial sum C[I, K]{U_X}, then all-reduce); §4.1 the MLP
+ *         split column-then-row; §4.2 attention split by heads, W_o by rows.
+ *   [V]   "vLLM model parallelism" article (intelliparadigm.com), §2.1: a
+ *         column-parallel layer keeps its weight as
+ *         [output_size_per_partition, input_size].
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless said otherwise; every buffer is
+ *     owned by the caller (e.g. torch tensors).  The library allocates no
+ *     device memory and keeps no state: calls are reentrant.
+ *   - Every call enqueues its kernels on `stream` (a hipStream_t; NULL is
+ *     the null stream) and returns without synchronising.  A device fault
+ *     surfaces at the caller's next synchronisation.
+ *   - Row-major layouts.  Weights are output-major: each output channel's
+ *     K-vector is contiguous ([V] §2.1), so a logical W[K, N] is stored as
+ *     Ws[N][K].
+ *   - dt selects the element type of X, weights, H and bf16/f32 outputs:
+ *     TP_BF16 (inputs bf16, fp32 accumulation, bf16 outputs rounded to
+ *     nearest-even) or TP_F32 (fp32 throughout).  Partials P are always fp32.
+ *   - Alignment: every pointer 16-byte aligned; every contraction length and
+ *     every row length a multiple of 8 elements.
+ *   - I == 0 is a no-op returning TP_OK.  Every other size must be >= 1.
+ *   - On any error status nothing is launched and no output is touched.
+ *   - Outputs must not overlap inputs or each other.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype_t;
+
+typedef enum {
+  TP_OK = 0,
+  TP_ERR_INVALID = 1,     /* null pointer, size < 1, t does not divide, bad enum, overlap */
+  TP_ERR_MISALIGNED = 2,  /* pointer not 16-byte aligned, or a length not a multiple of 8 */
+  TP_ERR_UNSUPPORTED = 3, /* valid request outside the sizes this build handles */
+  TP_ERR_LAUNCH = 4,      /* the HIP runtime reported an error when enqueuing */
+  TP_ERR_WORKSPACE = 5    /* workspace smaller than the *_workspace_size query */
+} tp_status_t;
+
+typedef enum { TP_ATTN_QKV = 0, TP_ATTN_O = 1 } tp_attn_phase_t;
+
+/* Version of this ABI (bumped on any signature change). */
+int tp_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* tp_status_string(tp_status_t s);
+
+/*
+ * Device workspace, in bytes, that tp_shard_mlp needs for these sizes
+ * (0 if none).  Host-only; never touches the GPU.  Returns 0 for invalid
+ * sizes (the call itself then reports the error).
+ */
+size_t tp_shard_mlp_workspace_size(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt);
+
+/*
+ * One rank's share of the SwiGLU MLP, [L4] §4.1, with F split t ways
+ * (F_local = F / t):
+ *
+ *   H[I, F_X]     = silu(X . W_gate[D, F_X]) * (X . W_up[D, F_X])
+ *                   column-parallel: case 1 of [L4] §3.2, no communication;
+ *                   silu(z) = z / (1 + exp(-z)), the product elementwise.
+ *   P[I, D]{U_X}  = H[I, F_X] . W_down[F_X, D]
+ *                   row-parallel: case 3 of [L4] §3.2, an UNREDUCED partial;
+ *                   the t ranks' P summed (the all-reduce) give the layer's
+ *                   MLP output.
+ *
+ *   X       [I, D]        dt, the replicated layer input
+ *   W_gate  [F_local, D]  dt, stores logical W_gate[D, F_X] (K = D contiguous)
+ *   W_up    [F_local, D]  dt
+ *   W_down  [D, F_local]  dt, stores logical W_down[F_X, D] (K = F_local contiguous)
+ *   H       [I, F_local]  dt, written: the SwiGLU activations (bf16 rounded
+ *                         to nearest-even on the bf16 path)
+ *   P       [I, D]        fp32, overwritten (never accumulated into)
+ *   workspace, workspace_bytes: device scratch of at least
+ *           tp_shard_mlp_workspace_size(...) bytes (may be NULL when that is 0);
+ *           contents on entry are ignored, on return undefined.
+ * Errors: TP_ERR_INVALID, TP_ERR_MISALIGNED (D or F_local not a multiple of 8,
+ * a pointer not 16-byte aligned), TP_ERR_WORKSPACE, TP_ERR_LAUNCH.
+ */
+tp_status_t tp_shard_mlp(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt,
+                         const void* X, const void* W_gate, const void* W_up,
+                         const void* W_down, void* H, float* P,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes tp_shard_attn_proj needs (0 if none); host-only. */
+size_t tp_shard_attn_proj_workspace_size(tp_attn_phase_t phase, int64_t I, int64_t D,
+                                         int64_t n_q_local, int64_t n_kv_local,
+                                         int64_t head_dim, tp_dtype_t dt);
+
+/*
+ * Attention projections of one rank, split by heads, [L4] §4.2.  The rank
+ * holds n_q_local query heads and n_kv_local KV groups of head_dim each.
+ *
+ * phase TP_ATTN_QKV (column-parallel, [L4] §3.2 case 1):
+ *   out[I, N_qkv] = X[I, D] . W_qkv[D, N_qkv],  N_qkv = (n_q_local + 2 n_kv_local) head_dim
+ *   in   X      [I, D]      dt
+ *   W           [N_qkv, D]  dt; rows are this rank's q heads, then its k
+ *                           heads, then its v heads (each head head_dim rows)
+ *   out         [I, N_qkv]  dt, same column order
+ * phase TP_ATTN_O (row-parallel, [L4] §3.2 case 3):
+ *   out[I, D]{U_X} = A[I, K_o] . W_o[K_o, D],  K_o = n_q_local head_dim
+ *   in   A      [I, K_o]    dt, this rank's attention output (its heads)
+ *   W           [D, K_o]    dt, stores the rank's row block of logical W_o
+ *   out         [I, D]      fp32 partial, overwritten
+ * n_kv_local is ignored for TP_ATTN_O (pass any value >= 1).
+ * Errors as tp_shard_mlp; head_dim must be a multiple of 8.
+ */
+tp_status_t tp_shard_attn_proj(tp_attn_phase_t phase, int64_t I, int64_t D,
+                               int64_t n_q_local, int64_t n_kv_local, int64_t head_dim,
+                               tp_dtype_t dt, const void* in, const void* W, void* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sum of t rank partials in rank order 0..t-1, in fp32: the value the
+ * all-reduce after a row-parallel block delivers ([L4] §3.3; §4.3 notes the
+ * sharded layer equals the single-device one up to this summation order).
+ * It stands in for the collective when all t ranks run on one device.
+ *   partials [t, n] fp32 (rank r's partial at partials + r*n)
+ *   Y        [n]    out_dt: fp32, or bf16 rounded to nearest-even
+ * n counts elements (I*D for a layer output) and must be a multiple of 8.
+ */
+tp_status_t tp_partial_reduce(int32_t t, int64_t n, const float* partials,
+                              tp_dtype_t out_dt, void* Y, void* stream);
+
+/*
+ * Attention core of one rank (test support, not a projection): each rank
+ * computes its own heads' attention completely ([L4] §4.2).  Scaled dot
+ * product (scale 1/sqrt(head_dim)), causal inside each sequence, no rotary
+ * embedding; local head j reads local KV group floor(j n_kv_local / n_q_local).
+ * Tokens form I/S sequences of S consecutive rows.
+ *   qkv [I, (n_q_local + 2 n_kv_local) head_dim] bf16, as TP_ATTN_QKV writes it
+ *   A   [I, n_q_local head_dim] bf16 out
+ * bf16 only; head_dim a multiple of 8 and at most 256; S must divide I.
+ */
+tp_status_t tp_attn_core(int64_t I, int64_t S, int64_t n_q_local, int64_t n_kv_local,
+                         int64_t head_dim, const void* qkv, void* A, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPSHARD_H */

@@ -1,1 +1,195 @@
-"""One tensor-parallel rank's share of a Megatron-style layer on MI355X."""
+"""One tensor-parallel rank's share of a Megatron-style layer on MI355X.
+
+Thin Python binding of the C ABI in include/tpshard.h (libtpshard.so, built
+from csrc/ for gfx950).  It only checks and marshals arguments: every step of
+the computation runs in the library's HIP kernels.  torch supplies device
+memory and the stream.  There is no fallback: if the library is missing the
+calls raise.
+
+    shard_mlp(X, W_gate, W_up, W_down, H, P)         column gate/up, SwiGLU, row down
+    shard_attn_proj(QKV|O, X_or_A, W, out, ...)      head-split QKV / row-split o_proj
+    partial_reduce(partials, Y)                      sum of the t rank partials
+    attn_core(qkv, A, S, n_q_local, n_kv_local, hd)  per-rank attention (test support)
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+
+LIB_PATH = pathlib.Path(__file__).resolve().parent / "libtpshard.so"
+HEADER = pathlib.Path(__file__).resolve().parent.parent / "include" / "tpshard.h"
+
+TP_F32, TP_BF16 = 0, 1
+TP_ATTN_QKV, TP_ATTN_O = 0, 1
+STATUS = {0: "TP_OK", 1: "TP_ERR_INVALID", 2: "TP_ERR_MISALIGNED", 3: "TP_ERR_UNSUPPORTED",
+          4: "TP_ERR_LAUNCH", 5: "TP_ERR_WORKSPACE"}
+
+_i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+
+# name -> (restype, argtypes), mirroring include/tpshard.h
+SIGNATURES = {
+    "tp_abi_version": (ctypes.c_int, []),
+    "tp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "tp_shard_mlp_workspace_size": (_sz, [_i64, _i64, _i64, ctypes.c_int]),
+    "tp_shard_mlp": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, _vp, _sz, _vp]),
+    "tp_shard_attn_proj_workspace_size": (_sz, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
+                                                ctypes.c_int]),
+    "tp_shard_attn_proj": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
+                                          ctypes.c_int, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "tp_partial_reduce": (ctypes.c_int, [_i32, _i64, _vp, ctypes.c_int, _vp, _vp]),
+    "tp_attn_core": (ctypes.c_int, [_i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp]),
+}
+
+
+class TPError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m megatron_tensor_layer_amd.build`")
+        L = ctypes.CDLL(str(LIB_PATH))
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, code: int) -> None:
+    if code != 0:
+        raise TPError(fn, code)
+
+
+# ------------------------------------------------------------------ torch glue
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return TP_BF16
+    if t.dtype == torch.float32:
+        return TP_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if t.device.type != "cuda" or t.device != dev:
+            raise ValueError("all tensors must be on the same GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return dev
+
+
+def _stream(stream, dev):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def mlp_workspace_bytes(I: int, D: int, F_local: int, dtype: int = TP_BF16) -> int:
+    return lib().tp_shard_mlp_workspace_size(I, D, F_local, dtype)
+
+
+def shard_mlp(X, W_gate, W_up, W_down, H, P, workspace=None, stream=None) -> None:
+    """P[I,D]{U_X} = (silu(X W_gate[D,F_X]) * (X W_up[D,F_X])) W_down[F_X,D]; H gets
+    the SwiGLU activations.  Weights output-major: W_gate/W_up [F_local, D],
+    W_down [D, F_local]."""
+    torch = _torch()
+    dev = _dev(X, W_gate, W_up, W_down, H, P)
+    I, D = X.shape
+    F_local = W_gate.shape[0]
+    dt = _dt(X)
+    for t in (W_gate, W_up, W_down, H):
+        if _dt(t) != dt:
+            raise TypeError("X, weights and H must share one dtype")
+    if P.dtype != torch.float32:
+        raise TypeError("P must be float32")
+    if (W_gate.shape != (F_local, D) or W_up.shape != (F_local, D)
+            or W_down.shape != (D, F_local) or H.shape != (I, F_local) or P.shape != (I, D)):
+        raise ValueError("shape mismatch")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _dev(workspace)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    _check("tp_shard_mlp", lib().tp_shard_mlp(I, D, F_local, dt, _ptr(X), _ptr(W_gate),
+                                              _ptr(W_up), _ptr(W_down), _ptr(H), _ptr(P),
+                                              ws_ptr, ws_bytes, _stream(stream, dev)))
+
+
+def shard_attn_proj(phase: int, inp, W, out, n_q_local: int, n_kv_local: int, head_dim: int,
+                    workspace=None, stream=None) -> None:
+    """phase TP_ATTN_QKV: out[I, N_qkv] = X W_qkv (W [N_qkv, D], rows q|k|v heads);
+    phase TP_ATTN_O: out(fp32)[I, D] = A W_o (W [D, n_q_local*head_dim])."""
+    torch = _torch()
+    dev = _dev(inp, W, out)
+    dt = _dt(inp)
+    if _dt(W) != dt:
+        raise TypeError("input and weight must share one dtype")
+    I = inp.shape[0]
+    if phase == TP_ATTN_QKV:
+        D = inp.shape[1]
+        N = (n_q_local + 2 * n_kv_local) * head_dim
+        if W.shape != (N, D) or out.shape != (I, N) or _dt(out) != dt:
+            raise ValueError("shape/dtype mismatch (QKV)")
+    elif phase == TP_ATTN_O:
+        D = W.shape[0]
+        K = n_q_local * head_dim
+        if inp.shape != (I, K) or W.shape != (D, K) or out.shape != (I, D) \
+                or out.dtype != torch.float32:
+            raise ValueError("shape/dtype mismatch (O)")
+    else:
+        raise ValueError("bad phase")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    _check("tp_shard_attn_proj",
+           lib().tp_shard_attn_proj(phase, I, D, n_q_local, n_kv_local, head_dim, dt, _ptr(inp),
+                                    _ptr(W), _ptr(out), ws_ptr, ws_bytes, _stream(stream, dev)))
+
+
+def partial_reduce(partials, Y, stream=None) -> None:
+    """Y = sum over r of partials[r] (rank order, fp32); Y float32 or bfloat16."""
+    torch = _torch()
+    dev = _dev(partials, Y)
+    if partials.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    t = partials.shape[0]
+    n = partials[0].numel()
+    if Y.numel() != n:
+        raise ValueError("Y must hold one partial's elements")
+    _check("tp_partial_reduce", lib().tp_partial_reduce(t, n, _ptr(partials), _dt(Y), _ptr(Y),
+                                                        _stream(stream, dev)))
+
+
+def attn_core(qkv, A, S: int, n_q_local: int, n_kv_local: int, head_dim: int,
+              stream=None) -> None:
+    """Per-rank causal GQA attention over sequences of S tokens (bf16)."""
+    torch = _torch()
+    dev = _dev(qkv, A)
+    if qkv.dtype != torch.bfloat16 or A.dtype != torch.bfloat16:
+        raise TypeError("attn_core is bf16 only")
+    I = qkv.shape[0]
+    _check("tp_attn_core", lib().tp_attn_core(I, S, n_q_local, n_kv_local, head_dim, _ptr(qkv),
+                                              _ptr(A), _stream(stream, dev)))

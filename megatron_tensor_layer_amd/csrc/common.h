@@ -1,0 +1,62 @@
+// Device-side helpers shared by the gfx950 kernels of the TP-shard library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpk {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+// Output epilogues of a projection.
+enum Epi : int {
+  EPI_F32 = 0,     // fp32 store (row-parallel partials)
+  EPI_DT = 1,      // store in the input dtype (QKV)
+  EPI_SWIGLU = 2,  // two weight matrices (gate, up): store silu(g) * u in dtype
+};
+
+// fp32 -> bf16 bits, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// Buffer resource over [base, base + bytes): raw (stride 0) addressing, so a
+// 32-bit lane offset at or past `bytes` reads zero instead of memory.
+// Word 3 is the gfx9-family raw-buffer format word.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+constexpr int kAuxNT = 2;  // non-temporal hint: streamed once, do not keep in cache
+
+// 16-byte load at byte offset `off` of a buffer resource.
+template <int AUX = 0>
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
+}
+
+// silu(z) = z / (1 + exp(-z)), fp32.
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// 2-element bf16 dot product accumulated in fp32 (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+}  // namespace tpk

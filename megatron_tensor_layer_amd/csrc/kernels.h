@@ -1,0 +1,32 @@
+// Internal launchers of the gfx950 kernels (C++ linkage; not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpk {
+
+// Largest contraction length (elements) the few-token kernel handles:
+// 8 chunks of 16 bytes per lane, 512 lanes.
+constexpr int64_t kGemvMaxK16 = 8 * 512 * 8;   // bf16
+constexpr int64_t kGemvMaxK32 = 8 * 512 * 4;   // fp32
+constexpr int kGemvMaxTokens = 8;
+
+// y[i, n] = sum_k X[i, k] W0[n, k] for I <= 8 tokens (EPI_SWIGLU: W0 gate,
+// W1 up, y = silu(.) * (.)).  T = uint16_t (bf16 bits) or float.
+template <typename T, int EPI>
+hipError_t gemv_launch(int I, int K, int N, const T* X, int64_t ldx, const T* W0,
+                       const T* W1, void* out, int64_t ldo, hipStream_t stream);
+
+// Same product on bf16 MFMA for any M.
+template <int EPI>
+hipError_t gemm_launch(int M, int N, int K, const uint16_t* A, int64_t lda, const uint16_t* W0,
+                       const uint16_t* W1, void* out, int64_t ldo, hipStream_t stream);
+
+hipError_t reduce_launch(int t, int64_t n, const float* P, bool out_bf16, void* Y,
+                         hipStream_t stream);
+
+hipError_t attn_core_launch(int I, int S, int nq, int nkv, int hd, const uint16_t* qkv,
+                            uint16_t* A, hipStream_t stream);
+
+}  // namespace tpk

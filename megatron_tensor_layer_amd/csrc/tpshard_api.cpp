@@ -1,0 +1,201 @@
+// C ABI of the TP-shard library (declared in include/tpshard.h).
+//
+// Host side only: validates arguments without touching the GPU, picks a
+// kernel family by the token count and enqueues it on the caller's stream.
+//   bf16, I <= 8   few-token streaming kernel (VALU dot2), weights read once
+//   bf16, I > 8    MFMA tiled kernel
+//   fp32           few-token streaming kernel, 8 tokens per launch
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/tpshard.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 26;  // per-dimension limit (int indexing)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  const char* lo;
+  const char* hi;
+};
+Range rng(const void* p, int64_t bytes) {
+  const char* c = static_cast<const char*>(p);
+  return Range{c, c + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool dims_ok(int64_t v) { return v >= 1 && v <= kMaxDim; }
+
+tp_status_t launched(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_LAUNCH; }
+
+// One projection out[I, N] = in[I, K] . W[N, K]^T with epilogue EPI.
+template <int EPI>
+hipError_t project(int64_t I, int64_t K, int64_t N, tp_dtype_t dt, const void* in,
+                   const void* W0, const void* W1, void* out, hipStream_t s) {
+  using tpk::gemm_launch;
+  using tpk::gemv_launch;
+  // element size of the stored output (fp32 partial or dtype)
+  const int64_t osz = (EPI == tpk::EPI_F32 || dt == TP_F32) ? 4 : 2;
+  if (dt == TP_BF16) {
+    auto X = static_cast<const uint16_t*>(in);
+    auto A0 = static_cast<const uint16_t*>(W0);
+    auto A1 = static_cast<const uint16_t*>(W1);
+    // few tokens: weight streaming on VALU; past K = kGemvMaxK16 / 2 the
+    // 8-token variant runs out of registers, so 5..8 tokens go to MFMA there
+    const int64_t kmax = (I <= 4) ? tpk::kGemvMaxK16 : tpk::kGemvMaxK16 / 2;
+    if (I <= tpk::kGemvMaxTokens && K <= kmax)
+      return gemv_launch<uint16_t, EPI>((int)I, (int)K, (int)N, X, K, A0, A1, out, N, s);
+    return gemm_launch<EPI>((int)I, (int)N, (int)K, X, K, A0, A1, out, N, s);
+  }
+  auto X = static_cast<const float*>(in);
+  auto A0 = static_cast<const float*>(W0);
+  auto A1 = static_cast<const float*>(W1);
+  // tokens per launch: 8, or 4 where each lane holds 8 chunks (K > 8192)
+  const int64_t step = (K > tpk::kGemvMaxK32 / 2) ? 4 : tpk::kGemvMaxTokens;
+  for (int64_t i0 = 0; i0 < I; i0 += step) {
+    const int64_t n = (I - i0) < step ? (I - i0) : step;
+    hipError_t e = gemv_launch<float, EPI>((int)n, (int)K, (int)N, X + i0 * K, K, A0, A1,
+                                           static_cast<char*>(out) + i0 * N * osz, N, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+bool dtype_ok(tp_dtype_t dt) { return dt == TP_F32 || dt == TP_BF16; }
+int64_t esize(tp_dtype_t dt) { return dt == TP_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+int tp_abi_version(void) { return 1; }
+
+const char* tp_status_string(tp_status_t s) {
+  switch (s) {
+    case TP_OK: return "TP_OK";
+    case TP_ERR_INVALID: return "TP_ERR_INVALID";
+    case TP_ERR_MISALIGNED: return "TP_ERR_MISALIGNED";
+    case TP_ERR_UNSUPPORTED: return "TP_ERR_UNSUPPORTED";
+    case TP_ERR_LAUNCH: return "TP_ERR_LAUNCH";
+    case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE";
+  }
+  return "TP_ERR_UNKNOWN";
+}
+
+size_t tp_shard_mlp_workspace_size(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt) {
+  (void)I; (void)D; (void)F_local; (void)dt;
+  return 0;
+}
+
+tp_status_t tp_shard_mlp(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt, const void* X,
+                         const void* W_gate, const void* W_up, const void* W_down, void* H,
+                         float* P, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dt) || I < 0 || I > kMaxDim || !dims_ok(D) || !dims_ok(F_local))
+    return TP_ERR_INVALID;
+  if (I == 0) return TP_OK;
+  if (!X || !W_gate || !W_up || !W_down || !H || !P) return TP_ERR_INVALID;
+  if ((D % 8) || (F_local % 8)) return TP_ERR_MISALIGNED;
+  if (!aligned16(X) || !aligned16(W_gate) || !aligned16(W_up) || !aligned16(W_down) ||
+      !aligned16(H) || !aligned16(P))
+    return TP_ERR_MISALIGNED;
+  const int64_t es = esize(dt);
+  const Range rX = rng(X, I * D * es), rG = rng(W_gate, F_local * D * es),
+              rU = rng(W_up, F_local * D * es), rD = rng(W_down, D * F_local * es),
+              rH = rng(H, I * F_local * es), rP = rng(P, I * D * 4);
+  for (Range in : {rX, rG, rU, rD})
+    if (overlap(rH, in) || overlap(rP, in)) return TP_ERR_INVALID;
+  if (overlap(rH, rP)) return TP_ERR_INVALID;
+  const size_t need = tp_shard_mlp_workspace_size(I, D, F_local, dt);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  if (dt == TP_F32 && (D > tpk::kGemvMaxK32 || F_local > tpk::kGemvMaxK32))
+    return TP_ERR_UNSUPPORTED;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear a stale error so the checks below are ours
+  hipError_t e = project<tpk::EPI_SWIGLU>(I, D, F_local, dt, X, W_gate, W_up, H, s);
+  if (e != hipSuccess) return TP_ERR_LAUNCH;
+  e = project<tpk::EPI_F32>(I, F_local, D, dt, H, W_down, nullptr, P, s);
+  return launched(e);
+}
+
+size_t tp_shard_attn_proj_workspace_size(tp_attn_phase_t phase, int64_t I, int64_t D,
+                                         int64_t n_q_local, int64_t n_kv_local,
+                                         int64_t head_dim, tp_dtype_t dt) {
+  (void)phase; (void)I; (void)D; (void)n_q_local; (void)n_kv_local; (void)head_dim; (void)dt;
+  return 0;
+}
+
+tp_status_t tp_shard_attn_proj(tp_attn_phase_t phase, int64_t I, int64_t D, int64_t n_q_local,
+                               int64_t n_kv_local, int64_t head_dim, tp_dtype_t dt,
+                               const void* in, const void* W, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (phase != TP_ATTN_QKV && phase != TP_ATTN_O) return TP_ERR_INVALID;
+  if (!dtype_ok(dt) || I < 0 || I > kMaxDim || !dims_ok(D) || !dims_ok(n_q_local) ||
+      !dims_ok(head_dim) || (phase == TP_ATTN_QKV && !dims_ok(n_kv_local)))
+    return TP_ERR_INVALID;
+  const int64_t K = (phase == TP_ATTN_QKV) ? D : n_q_local * head_dim;
+  const int64_t N = (phase == TP_ATTN_QKV) ? (n_q_local + 2 * n_kv_local) * head_dim : D;
+  if (K > kMaxDim || N > kMaxDim) return TP_ERR_INVALID;
+  if (I == 0) return TP_OK;
+  if (!in || !W || !out) return TP_ERR_INVALID;
+  if ((D % 8) || (head_dim % 8)) return TP_ERR_MISALIGNED;
+  if (!aligned16(in) || !aligned16(W) || !aligned16(out)) return TP_ERR_MISALIGNED;
+  const int64_t es = esize(dt);
+  const int64_t osz = (phase == TP_ATTN_O) ? 4 : es;
+  const Range rIn = rng(in, I * K * es), rW = rng(W, N * K * es), rO = rng(out, I * N * osz);
+  if (overlap(rO, rIn) || overlap(rO, rW)) return TP_ERR_INVALID;
+  const size_t need =
+      tp_shard_attn_proj_workspace_size(phase, I, D, n_q_local, n_kv_local, head_dim, dt);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  if (dt == TP_F32 && K > tpk::kGemvMaxK32) return TP_ERR_UNSUPPORTED;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (phase == TP_ATTN_QKV)
+    return launched(project<tpk::EPI_DT>(I, K, N, dt, in, W, nullptr, out, s));
+  return launched(project<tpk::EPI_F32>(I, K, N, dt, in, W, nullptr, out, s));
+}
+
+tp_status_t tp_partial_reduce(int32_t t, int64_t n, const float* partials, tp_dtype_t out_dt,
+                              void* Y, void* stream) {
+  if (t < 1 || n < 0 || !dtype_ok(out_dt)) return TP_ERR_INVALID;
+  if (n == 0) return TP_OK;
+  if (!partials || !Y) return TP_ERR_INVALID;
+  if (n % 8) return TP_ERR_MISALIGNED;
+  if (!aligned16(partials) || !aligned16(Y)) return TP_ERR_MISALIGNED;
+  if ((int64_t)t * n / 4 > (int64_t(1) << 40)) return TP_ERR_UNSUPPORTED;
+  if ((n / 4 + 255) / 256 > INT32_MAX) return TP_ERR_UNSUPPORTED;
+  if (overlap(rng(Y, n * esize(out_dt)), rng(partials, (int64_t)t * n * 4)))
+    return TP_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  return launched(tpk::reduce_launch(t, n, partials, out_dt == TP_BF16, Y, s));
+}
+
+tp_status_t tp_attn_core(int64_t I, int64_t S, int64_t n_q_local, int64_t n_kv_local,
+                         int64_t head_dim, const void* qkv, void* A, void* stream) {
+  if (I < 0 || I > INT32_MAX || !dims_ok(S) || !dims_ok(n_kv_local) || n_q_local < 1 ||
+      n_q_local > 65535 || head_dim < 1 || n_kv_local > n_q_local)
+    return TP_ERR_INVALID;
+  if (I == 0) return TP_OK;
+  if (I % S) return TP_ERR_INVALID;
+  if (head_dim > 256) return TP_ERR_UNSUPPORTED;
+  if (!qkv || !A) return TP_ERR_INVALID;
+  if (head_dim % 8) return TP_ERR_MISALIGNED;
+  if (!aligned16(qkv) || !aligned16(A)) return TP_ERR_MISALIGNED;
+  const int64_t N = (n_q_local + 2 * n_kv_local) * head_dim;
+  if (overlap(rng(A, I * n_q_local * head_dim * 2), rng(qkv, I * N * 2))) return TP_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  return launched(tpk::attn_core_launch((int)I, (int)S, (int)n_q_local, (int)n_kv_local,
+                                        (int)head_dim, static_cast<const uint16_t*>(qkv),
+                                        static_cast<uint16_t*>(A), s));
+}
+
+}  // extern "C"

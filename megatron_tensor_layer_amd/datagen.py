@@ -6,10 +6,12 @@ rounds them to the storage type and cuts rank shards out of full tensors.
 
 Recipe (the same for every consumer):
 
-* Tensor ``name`` of workload pool ``pool`` is drawn from numpy's PCG64
-  generator seeded with ``SeedSequence([42, TENSOR_IDS[name], pool])``.  The
-  base 42 echoes the shared default sampling seed of the Pico-vLLM TP post
-  (koas-w blog, "Engine" section).
+* Tensor ``name`` of workload pool ``pool`` is drawn in chunks of 2**24
+  consecutive elements (row-major order); chunk k comes from numpy's PCG64
+  generator seeded with ``SeedSequence([42, TENSOR_IDS[name], pool, k])``, so
+  chunks can be drawn in parallel and the result does not depend on the
+  thread count.  The base 42 echoes the shared default sampling seed of the
+  Pico-vLLM TP post (koas-w blog, "Engine" section).
 * Activations are N(0, 1); every weight matrix is N(0, 1/D) (variance 1/D,
   sigma = D**-0.5, D the model width), drawn in float32 with numpy's ziggurat
   normal sampler, scaled in float32.
@@ -21,6 +23,9 @@ Recipe (the same for every consumer):
   so the union of the shards is exactly the unsharded weight.
 """
 from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -58,18 +63,28 @@ def gaussian(name: str, shape, sigma: float = 1.0, dtype: str = "bf16",
         raise ValueError(f"unsupported dtype {dtype!r}")
     shape = tuple(int(s) for s in shape)
     n = int(np.prod(shape)) if shape else 1
-    rng = np.random.Generator(np.random.PCG64(
-        np.random.SeedSequence([BASE_SEED, TENSOR_IDS[name], int(pool)])))
     out = np.empty(n, dtype=np.float32)
     s = np.float32(sigma)
-    for lo in range(0, n, _CHUNK):
-        hi = min(n, lo + _CHUNK)
+
+    def draw(k: int) -> None:
+        lo, hi = k * _CHUNK, min(n, (k + 1) * _CHUNK)
+        rng = np.random.Generator(np.random.PCG64(
+            np.random.SeedSequence([BASE_SEED, TENSOR_IDS[name], int(pool), k])))
         blk = out[lo:hi]
         rng.standard_normal(out=blk, dtype=np.float32)
         if s != np.float32(1.0):
             blk *= s
         if dtype == "bf16":
             _round_to_bf16_inplace(blk)
+
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+    if nchunks <= 1:
+        for k in range(nchunks):
+            draw(k)
+    else:
+        workers = min(nchunks, len(os.sched_getaffinity(0)), 16)
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(draw, range(nchunks)))
     return out.reshape(shape)
 
 

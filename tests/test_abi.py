@@ -1,0 +1,131 @@
+"""The C ABI library on the CPU: it loads, exports every function the header
+declares, and rejects bad arguments before touching the GPU.
+
+Every call here fails validation (or is a host-only query), so no HIP
+runtime call and no kernel launch happens: pointers are fake addresses that
+are never dereferenced."""
+import ctypes
+import re
+
+import pytest
+
+import megatron_tensor_layer_amd as tp
+
+OK, INVALID, MISALIGNED, UNSUPPORTED, LAUNCH, WORKSPACE = range(6)
+FAKE = 0x10000000          # 16-byte aligned, never dereferenced
+STEP = 1 << 32             # distinct fake buffers 4 GB apart
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not tp.LIB_PATH.exists():
+        from megatron_tensor_layer_amd import build
+        build.build()
+    return tp.lib()
+
+
+def header_functions():
+    src = tp.HEADER.read_text()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z_0-9]+)\s*\(", src)))
+
+
+def fake(k):
+    return ctypes.c_void_p(FAKE + k * STEP)
+
+
+def test_exports_every_header_function(lib):
+    names = header_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/tpshard.h but not exported"
+    # the binding declares exactly the header's functions
+    assert sorted(tp.SIGNATURES) == names
+
+
+def test_version_and_status_strings(lib):
+    assert lib.tp_abi_version() == 1
+    for code, name in tp.STATUS.items():
+        assert lib.tp_status_string(code).decode() == name
+    assert lib.tp_status_string(99).decode() == "TP_ERR_UNKNOWN"
+
+
+def mlp(lib, I=4, D=256, F=512, dt=tp.TP_BF16, ptrs=None, ws=None, wsb=0):
+    p = ptrs or [fake(k) for k in range(6)]
+    return lib.tp_shard_mlp(I, D, F, dt, *p, ws, wsb, None)
+
+
+def test_mlp_validation(lib):
+    assert mlp(lib, dt=7) == INVALID
+    assert mlp(lib, I=-1) == INVALID
+    assert mlp(lib, D=0) == INVALID
+    assert mlp(lib, F=0) == INVALID
+    assert mlp(lib, D=1 << 40) == INVALID
+    # I == 0 is a no-op even with null pointers
+    assert mlp(lib, I=0, ptrs=[None] * 6) == OK
+    for k in range(6):
+        p = [fake(j) for j in range(6)]
+        p[k] = None
+        assert mlp(lib, ptrs=p) == INVALID, k
+    assert mlp(lib, D=260) == MISALIGNED
+    assert mlp(lib, F=508) == MISALIGNED
+    for k in range(6):
+        p = [fake(j) for j in range(6)]
+        p[k] = ctypes.c_void_p(p[k].value + 8)
+        assert mlp(lib, ptrs=p) == MISALIGNED, k
+    # output overlapping an input, outputs overlapping each other
+    p = [fake(j) for j in range(6)]
+    p[4] = fake(0)
+    assert mlp(lib, ptrs=p) == INVALID
+    p = [fake(j) for j in range(6)]
+    p[5] = ctypes.c_void_p(p[4].value + 64)
+    assert mlp(lib, ptrs=p) == INVALID
+    # fp32 beyond the few-token kernel's K range
+    assert mlp(lib, D=32768, dt=tp.TP_F32) == UNSUPPORTED
+
+
+def test_attn_validation(lib):
+    f = lambda *a, **k: lib.tp_shard_attn_proj(*a, None, 0, None)
+    P = [fake(k) for k in range(3)]
+    assert f(5, 4, 256, 2, 1, 128, tp.TP_BF16, *P) == INVALID
+    assert f(tp.TP_ATTN_QKV, 4, 256, 0, 1, 128, tp.TP_BF16, *P) == INVALID
+    assert f(tp.TP_ATTN_QKV, 4, 256, 2, 0, 128, tp.TP_BF16, *P) == INVALID
+    assert f(tp.TP_ATTN_O, 0, 256, 2, 0, 128, tp.TP_BF16, None, None, None) == OK
+    assert f(tp.TP_ATTN_QKV, 4, 256, 2, 1, 12, tp.TP_BF16, *P) == MISALIGNED
+    assert f(tp.TP_ATTN_QKV, 4, 256, 2, 1, 128, tp.TP_BF16, P[0], None, P[2]) == INVALID
+    assert f(tp.TP_ATTN_O, 4, 256, 2, 1, 128, tp.TP_BF16, P[0], P[1],
+             ctypes.c_void_p(P[2].value + 4)) == MISALIGNED
+    assert f(tp.TP_ATTN_O, 4, 256, 2, 1, 128, tp.TP_BF16, P[0], P[1], P[0]) == INVALID
+
+
+def test_reduce_validation(lib):
+    r = lib.tp_partial_reduce
+    assert r(0, 64, fake(0), tp.TP_F32, fake(1), None) == INVALID
+    assert r(2, -1, fake(0), tp.TP_F32, fake(1), None) == INVALID
+    assert r(2, 64, fake(0), 3, fake(1), None) == INVALID
+    assert r(2, 0, None, tp.TP_F32, None, None) == OK
+    assert r(2, 60, fake(0), tp.TP_F32, fake(1), None) == MISALIGNED
+    assert r(2, 64, ctypes.c_void_p(FAKE + 4), tp.TP_F32, fake(1), None) == MISALIGNED
+    assert r(2, 64, fake(0), tp.TP_F32, ctypes.c_void_p(FAKE + 128), None) == INVALID
+
+
+def test_attn_core_validation(lib):
+    c = lib.tp_attn_core
+    assert c(8, 3, 4, 2, 64, fake(0), fake(1), None) == INVALID      # S does not divide I
+    assert c(8, 4, 2, 4, 64, fake(0), fake(1), None) == INVALID      # more KV groups than heads
+    assert c(8, 4, 4, 2, 512, fake(0), fake(1), None) == UNSUPPORTED
+    assert c(8, 4, 4, 2, 60, fake(0), fake(1), None) == MISALIGNED
+    assert c(0, 1, 4, 2, 64, None, None, None) == OK
+
+
+def test_workspace_queries_are_host_only(lib):
+    assert lib.tp_shard_mlp_workspace_size(64, 8192, 3584, tp.TP_BF16) >= 0
+    assert lib.tp_shard_attn_proj_workspace_size(tp.TP_ATTN_QKV, 32, 8192, 8, 1, 128,
+                                                 tp.TP_BF16) >= 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(tp, "_lib", None)
+    monkeypatch.setattr(tp, "LIB_PATH", tmp_path / "missing.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        tp.lib()

@@ -1,0 +1,96 @@
+"""The full Llama-3.1-70B-shaped layer with all 8 TP ranks emulated in turn on
+one GPU: QKV (column, by heads) -> attention core -> o_proj (row) -> reduce
+-> MLP (column gate/up, SwiGLU, row down) -> reduce, against the unsharded
+fp64 oracle layer (normwise 2e-2).  The GPU carries the attention block's
+output to the MLP in bf16; the oracle does not round it."""
+import numpy as np
+import pytest
+
+import megatron_tensor_layer_amd as tp
+from megatron_tensor_layer_amd import datagen
+from tests.common import normwise_err
+from tests.gpu_util import empty, to_dev, to_host, torch
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+D, F, NQ, NKV, HD, T_ = 8192, 28672, 64, 8, 128, 8
+
+
+@pytest.fixture(scope="module")
+def layer():
+    Wq, Wk, Wv, Wo = datagen.attn_weights(D, NQ, NKV, HD, "bf16", 11)
+    Wg, Wu, Wd = datagen.mlp_weights(D, F, "bf16", 11)
+    ranks = []
+    for r in range(T_):
+        ranks.append(dict(
+            qkv=to_dev(datagen.qkv_rank_shard(Wq, Wk, Wv, NQ, NKV, HD, T_, r), "bf16"),
+            o=to_dev(datagen.oproj_rank_shard(Wo, NQ, HD, T_, r), "bf16"),
+            mlp=tuple(to_dev(a, "bf16") for a in datagen.mlp_rank_shards(Wg, Wu, Wd, T_, r))))
+    yield dict(attn=(Wq, Wk, Wv, Wo), mlp=(Wg, Wu, Wd), ranks=ranks)
+    del ranks
+    torch().cuda.empty_cache()
+
+
+def gpu_layer(L, X, S):
+    """Returns (QKV of rank 0, A of rank 0, o-partial of rank 0, attention
+    block output y1 in bf16, layer output y)."""
+    T = torch()
+    I = X.shape[0]
+    nql, nkl = NQ // T_, NKV // T_
+    Xd = to_dev(X, "bf16")
+    po = T.empty((T_, I, D), dtype=T.float32, device="cuda")
+    keep = {}
+    for r, R in enumerate(L["ranks"]):
+        qkv = empty((I, (nql + 2 * nkl) * HD), "bf16")
+        tp.shard_attn_proj(tp.TP_ATTN_QKV, Xd, R["qkv"], qkv, nql, nkl, HD)
+        A = empty((I, nql * HD), "bf16")
+        tp.attn_core(qkv, A, S, nql, nkl, HD)
+        tp.shard_attn_proj(tp.TP_ATTN_O, A, R["o"], po[r], nql, nkl, HD)
+        if r == 0:
+            keep = dict(qkv=qkv, A=A)
+    y1 = empty((I, D), "bf16")
+    tp.partial_reduce(po, y1)
+    pm = T.empty((T_, I, D), dtype=T.float32, device="cuda")
+    for r, R in enumerate(L["ranks"]):
+        H = empty((I, F // T_), "bf16")
+        tp.shard_mlp(y1, *R["mlp"], H, pm[r])
+    y = empty((I, D), "f32")
+    tp.partial_reduce(pm, y)
+    T.cuda.synchronize()
+    return keep["qkv"], keep["A"], po[0], y1, y
+
+
+def test_layer_decode32(orc, layer):
+    """Decode batch 32: 32 independent sequences of one token each."""
+    I, S = 32, 1
+    X = datagen.gaussian("X", (I, D), 1.0, "bf16", 32)
+    qkv0, A0, po0, y1, y = gpu_layer(layer, X, S)
+    Wq, Wk, Wv, Wo = layer["attn"]
+    # rank 0 stages
+    q_ref, A_ref, po_ref = orc.attn_block_rank(X, Wq, Wk, Wv, Wo, NQ, NKV, HD, S, T_, 0)
+    assert normwise_err(to_host(qkv0), q_ref) <= TOL
+    assert normwise_err(to_host(A0), A_ref) <= TOL
+    assert normwise_err(to_host(po0), po_ref) <= TOL
+    # unsharded attention block, then the unsharded MLP on sampled rows
+    _, _, y1_ref = orc.attn_block_rank(X, Wq, Wk, Wv, Wo, NQ, NKV, HD, S)
+    assert normwise_err(to_host(y1), y1_ref) <= TOL
+    rows = [0, 13, 31]
+    _, y_ref = orc.mlp_full(y1_ref, *layer["mlp"], rows=rows)
+    assert normwise_err(to_host(y)[rows], y_ref) <= TOL
+
+
+def test_layer_prefill512_rank0(orc, layer):
+    """Prefill of one causal sequence of 512 tokens: rank 0's QKV, attention and
+    o_proj partial against the oracle (sampled rows), and the layer output is
+    finite everywhere."""
+    I, S = 512, 512
+    X = datagen.gaussian("X", (I, D), 1.0, "bf16", 512)
+    qkv0, A0, po0, y1, y = gpu_layer(layer, X, S)
+    Wq, Wk, Wv, Wo = layer["attn"]
+    q_ref, A_ref, po_ref = orc.attn_block_rank(X, Wq, Wk, Wv, Wo, NQ, NKV, HD, S, T_, 0)
+    rows = [0, 1, 100, 311, 511]
+    assert normwise_err(to_host(qkv0), q_ref) <= TOL
+    assert normwise_err(to_host(A0)[rows], A_ref[rows]) <= TOL
+    assert normwise_err(to_host(po0)[rows], po_ref[rows]) <= TOL
+    T = torch()
+    assert T.isfinite(y).all() and T.isfinite(y1.float()).all()
