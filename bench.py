@@ -1,0 +1,361 @@
+"""Benchmark of one tensor-parallel rank's layer share on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-detail] [--no-cpu]
+
+A step is one pass of the whole hot path over one batch: the Llama-3.1-70B-
+shaped layer (D=8192, F=28672, 64 query heads, 8 KV groups, head_dim 128) at
+TP=8 with all 8 rank shares computed in turn on the one GPU, decode batch 32
+(32 sequences of one token):
+
+    per rank: QKV (column, by heads) -> attention core -> o_proj (row partial)
+    reduce of the 8 o_proj partials (bf16 out)
+    per rank: gate/up (column) + SwiGLU -> down (row partial)
+    reduce of the 8 MLP partials (fp32 out)
+
+value = the step's compulsory HBM bytes (weights, inputs and outputs of every
+call, each once) / the step's time, in GB/s.  The 8 ranks' weights (1.71 GB)
+exceed the 256 MB Infinity Cache, so every step streams them from HBM.
+
+The printed JSON line also carries
+  roofline:     the dominant call (one rank's tp_shard_mlp at I=32) timed with
+                HIP events on its stream inside the timed region, against the
+                8 TB/s HBM peak;
+  cpu_baseline: the fp64 oracle on the host cores running one whole step
+                (about 55 GFLOP in fp64, a second or so on 16 cores);
+  detail:       per-config figures (MLP shard decode I=1/16/64/256 GB/s,
+                prefill 512 TFLOP/s at TP=8 and TP=1, Qwen2.5-1.5B TP=2 calls,
+                the layer at prefill 512, the partial reduce).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import pathlib
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+from megatron_tensor_layer_amd import datagen, workloads as wl  # noqa: E402
+
+D, F, NQ, NKV, HD, TP = 8192, 28672, 64, 8, 128, 8
+PEAK_HBM = wl.PEAK_HBM_GBS
+PEAK_BF16 = wl.PEAK_BF16_TFLOPS
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--batch", type=int, default=32, help="decode tokens of the timed step")
+    ap.add_argument("--no-detail", action="store_true", help="skip the per-config breakdown")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--calls", type=int, default=200, help="timed calls per detail config")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ helpers
+def to_dev(torch, a, dtype="bf16"):
+    if dtype == "bf16":
+        return torch.from_numpy(datagen.bf16_bits(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def time_calls(torch, fns, n, warm=10):
+    """Event-time n calls, cycling through fns (one per weight set); returns
+    per-call microseconds."""
+    for i in range(warm):
+        fns[i % len(fns)]()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    s = torch.cuda.current_stream()
+    for i in range(n):
+        ev[i][0].record(s)
+        fns[i % len(fns)]()
+        ev[i][1].record(s)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+
+def log(msg):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def stats(us):
+    us = sorted(us)
+    q = lambda p: us[min(len(us) - 1, int(p * len(us)))]
+    return dict(median_us=round(statistics.median(us), 2), p10_us=round(q(0.1), 2),
+                p90_us=round(q(0.9), 2))
+
+
+def src_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update((ROOT / f).read_bytes())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ the layer
+class Layer:
+    """All 8 TP rank shares of the Llama-3.1-70B-shaped layer, resident in HBM."""
+
+    def __init__(self, torch, tp, pool=11):
+        self.torch, self.tp = torch, tp
+        Wq, Wk, Wv, Wo = datagen.attn_weights(D, NQ, NKV, HD, "bf16", pool)
+        Wg, Wu, Wd = datagen.mlp_weights(D, F, "bf16", pool)
+        self.host = dict(attn=(Wq, Wk, Wv, Wo), mlp=(Wg, Wu, Wd))
+        self.ranks = []
+        for r in range(TP):
+            self.ranks.append(dict(
+                qkv=to_dev(torch, datagen.qkv_rank_shard(Wq, Wk, Wv, NQ, NKV, HD, TP, r)),
+                o=to_dev(torch, datagen.oproj_rank_shard(Wo, NQ, HD, TP, r)),
+                mlp=tuple(to_dev(torch, a) for a in datagen.mlp_rank_shards(Wg, Wu, Wd, TP, r))))
+        self.nql, self.nkl = NQ // TP, NKV // TP
+
+    def buffers(self, I):
+        T = self.torch
+        bf, f32 = T.bfloat16, T.float32
+        return dict(I=I, qkv=T.empty((I, (self.nql + 2 * self.nkl) * HD), dtype=bf, device="cuda"),
+                    A=T.empty((I, self.nql * HD), dtype=bf, device="cuda"),
+                    po=T.empty((TP, I, D), dtype=f32, device="cuda"),
+                    y1=T.empty((I, D), dtype=bf, device="cuda"),
+                    H=T.empty((I, F // TP), dtype=bf, device="cuda"),
+                    pm=T.empty((TP, I, D), dtype=f32, device="cuda"),
+                    y=T.empty((I, D), dtype=f32, device="cuda"))
+
+    def step(self, X, B, S, mlp_events=None):
+        tp = self.tp
+        for r, R in enumerate(self.ranks):
+            tp.shard_attn_proj(tp.TP_ATTN_QKV, X, R["qkv"], B["qkv"], self.nql, self.nkl, HD)
+            tp.attn_core(B["qkv"], B["A"], S, self.nql, self.nkl, HD)
+            tp.shard_attn_proj(tp.TP_ATTN_O, B["A"], R["o"], B["po"][r], self.nql, self.nkl, HD)
+        tp.partial_reduce(B["po"], B["y1"])
+        s = self.torch.cuda.current_stream()
+        for r, R in enumerate(self.ranks):
+            if mlp_events is not None:
+                e0, e1 = (self.torch.cuda.Event(enable_timing=True) for _ in range(2))
+                e0.record(s)
+            tp.shard_mlp(B["y1"], *R["mlp"], B["H"], B["pm"][r])
+            if mlp_events is not None:
+                e1.record(s)
+                mlp_events.append((e0, e1))
+        tp.partial_reduce(B["pm"], B["y"])
+
+
+def step_bytes(I, S):
+    """Compulsory HBM bytes of one step (all 8 ranks, both reduces)."""
+    q = wl.QkvShape(I, D, NQ // TP, NKV // TP, HD)
+    o = wl.OprojShape(I, D, NQ // TP, HD)
+    m = wl.MlpShape(I, D, F // TP)
+    attn_core = (I * q.N + I * o.K) * wl.BF16 if S == 1 else None
+    per_rank = q.bytes() + o.bytes() + m.bytes() + (attn_core or 0)
+    red = wl.ReduceShape(TP, I * D, wl.BF16).bytes() + wl.ReduceShape(TP, I * D, wl.F32).bytes()
+    return TP * per_rank + red
+
+
+def step_flops(I):
+    q = wl.QkvShape(I, D, NQ // TP, NKV // TP, HD)
+    o = wl.OprojShape(I, D, NQ // TP, HD)
+    m = wl.MlpShape(I, D, F // TP)
+    return TP * (q.flops() + o.flops() + m.flops())
+
+
+# ------------------------------------------------------------------ detail
+def detail(torch, tp, layer, calls):
+    out = {}
+    T = torch
+    # Llama-3.1-70B MLP rank share, TP=8: rotate through the 8 real rank shards
+    for I in (1, 16, 64, 256):
+        X = to_dev(T, datagen.gaussian("X", (I, D), 1.0, "bf16", 1000 + I))
+        H = T.empty((I, F // TP), dtype=T.bfloat16, device="cuda")
+        P = T.empty((I, D), dtype=T.float32, device="cuda")
+        fns = [(lambda R=R: tp.shard_mlp(X, *R["mlp"], H, P)) for R in layer.ranks]
+        st = stats(time_calls(T, fns, calls))
+        m = wl.MlpShape(I, D, F // TP)
+        gbs = m.bytes() / (st["median_us"] * 1e-6) / 1e9
+        log(f"MLP TP=8 decode I={I}: {st['median_us']} us")
+        out[f"llama70b_mlp_tp8_decode_I{I}"] = dict(
+            **st, GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM, 3),
+            TFLOPs=round(m.flops() / (st["median_us"] * 1e-6) / 1e12, 1),
+            tokens_per_s=round(I / (st["median_us"] * 1e-6)))
+    # prefill 512, TP=8 shards and the TP=1 unsharded MLP
+    I = 512
+    X = to_dev(T, datagen.gaussian("X", (I, D), 1.0, "bf16", 1512))
+    H = T.empty((I, F // TP), dtype=T.bfloat16, device="cuda")
+    P = T.empty((I, D), dtype=T.float32, device="cuda")
+    fns = [(lambda R=R: tp.shard_mlp(X, *R["mlp"], H, P)) for R in layer.ranks]
+    st = stats(time_calls(T, fns, calls // 2))
+    m = wl.MlpShape(I, D, F // TP)
+    tf = m.flops() / (st["median_us"] * 1e-6) / 1e12
+    out["llama70b_mlp_tp8_prefill_I512"] = dict(**st, TFLOPs=round(tf, 1),
+                                                frac_mfma=round(tf / PEAK_BF16, 3),
+                                                tokens_per_s=round(I / (st["median_us"] * 1e-6)))
+    full = tuple(to_dev(T, a) for a in layer.host["mlp"])
+    H1 = T.empty((I, F), dtype=T.bfloat16, device="cuda")
+    st = stats(time_calls(T, [lambda: tp.shard_mlp(X, *full, H1, P)], max(10, calls // 10), 3))
+    m = wl.MlpShape(I, D, F)
+    tf = m.flops() / (st["median_us"] * 1e-6) / 1e12
+    out["llama70b_mlp_tp1_prefill_I512"] = dict(**st, TFLOPs=round(tf, 1),
+                                                frac_mfma=round(tf / PEAK_BF16, 3))
+    del full, H1
+    # layer prefill 512 (one causal sequence), 8 ranks + reduces
+    B = layer.buffers(512)
+    X = to_dev(T, datagen.gaussian("X", (512, D), 1.0, "bf16", 2512))
+    st = stats(time_calls(T, [lambda: layer.step(X, B, 512)], 10, 2))
+    tf = step_flops(512) / (st["median_us"] * 1e-6) / 1e12
+    out["llama70b_layer_tp8x8_prefill_I512"] = dict(
+        **st, TFLOPs_projections=round(tf, 1), frac_mfma=round(tf / PEAK_BF16, 3),
+        tokens_per_s_excl_comm=round(512 / (st["median_us"] * 1e-6)))
+    del B
+    # partial reduce of 8 fp32 partials
+    for I in (32, 512):
+        Pp = T.randn((TP, I, D), device="cuda")
+        Y = T.empty((I, D), dtype=T.float32, device="cuda")
+        st = stats(time_calls(T, [lambda: tp.partial_reduce(Pp, Y)], calls))
+        gbs = wl.ReduceShape(TP, I * D).bytes() / (st["median_us"] * 1e-6) / 1e9
+        out[f"reduce_t8_I{I}"] = dict(**st, GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM, 3))
+    # Qwen2.5-1.5B-shaped rank share at TP=2: 24 independently seeded rank
+    # shares rotate so the calls stream from HBM, not the Infinity Cache
+    Dq, Fq, nq, nkv, t = 1536, 8960, 12, 2, 2
+    pools = []
+    for p in range(24):
+        Wg = datagen.gaussian("W_gate", (Fq // t, Dq), Dq ** -0.5, "bf16", 5000 + p)
+        Wu = datagen.gaussian("W_up", (Fq // t, Dq), Dq ** -0.5, "bf16", 5000 + p)
+        Wd = datagen.gaussian("W_down", (Dq, Fq // t), Dq ** -0.5, "bf16", 5000 + p)
+        Wqkv = datagen.gaussian("W_q", ((nq // t + 2 * nkv // t) * 128, Dq), Dq ** -0.5, "bf16",
+                                5000 + p)
+        Wo = datagen.gaussian("W_o", (Dq, nq // t * 128), Dq ** -0.5, "bf16", 5000 + p)
+        pools.append(tuple(to_dev(T, a) for a in (Wg, Wu, Wd, Wqkv, Wo)))
+    for I in (1, 8, 64):
+        X = to_dev(T, datagen.gaussian("X", (I, Dq), 1.0, "bf16", 3000 + I))
+        A = to_dev(T, datagen.gaussian("A", (I, nq // t * 128), 1.0, "bf16", 3000 + I))
+        H = T.empty((I, Fq // t), dtype=T.bfloat16, device="cuda")
+        P = T.empty((I, Dq), dtype=T.float32, device="cuda")
+        Q = T.empty((I, (nq // t + 2 * nkv // t) * 128), dtype=T.bfloat16, device="cuda")
+        row = {}
+        for name, fns, nbytes in (
+                ("mlp", [(lambda w=w: tp.shard_mlp(X, w[0], w[1], w[2], H, P)) for w in pools],
+                 wl.MlpShape(I, Dq, Fq // t).bytes()),
+                ("qkv", [(lambda w=w: tp.shard_attn_proj(tp.TP_ATTN_QKV, X, w[3], Q, nq // t,
+                                                         nkv // t, 128)) for w in pools],
+                 wl.QkvShape(I, Dq, nq // t, nkv // t, 128).bytes()),
+                ("o_proj", [(lambda w=w: tp.shard_attn_proj(tp.TP_ATTN_O, A, w[4], P, nq // t,
+                                                            nkv // t, 128)) for w in pools],
+                 wl.OprojShape(I, Dq, nq // t, 128).bytes())):
+            st = stats(time_calls(T, fns, calls))
+            row[name] = dict(**st, GBps=round(nbytes / (st["median_us"] * 1e-6) / 1e9, 1))
+        out[f"qwen2.5_1.5b_tp2_decode_I{I}"] = row
+    del pools
+    return out
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(layer, X, I, S, bytes_per_step):
+    """The fp64 oracle, untuned, on one whole step: all 8 ranks' QKV,
+    attention core, o_proj and MLP for all I tokens, plus both reduces."""
+    import oracle
+    orc = oracle.get()
+    # fp64 copies made before the clock starts: the oracle's own work is timed
+    Wq, Wk, Wv, Wo = (a.astype(np.float64) for a in layer.host["attn"])
+    Wg, Wu, Wd = (a.astype(np.float64) for a in layer.host["mlp"])
+    X = X.astype(np.float64)
+    t0 = time.perf_counter()
+    po = np.stack([orc.attn_block_rank(X, Wq, Wk, Wv, Wo, NQ, NKV, HD, S, TP, r)[2]
+                   for r in range(TP)])
+    y1 = orc.reduce(po)
+    pm = np.stack([orc.mlp_rank(y1, Wg, Wu, Wd, TP, r)[1] for r in range(TP)])
+    orc.reduce(pm)
+    step_s = time.perf_counter() - t0
+    return dict(value=round(bytes_per_step / step_s / 1e9, 3), unit="GB/s",
+                cores=oracle.num_threads(), kind="oracle",
+                sample=f"one whole step: 8 ranks x (QKV, attention core, o_proj, MLP) for all "
+                       f"{I} tokens plus both reduces, {step_s:.1f} s")
+
+
+# ------------------------------------------------------------------ main
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the TP "
+              "ranks are emulated in turn on a single device and no collective is used.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import megatron_tensor_layer_amd as tp
+
+    torch.cuda.set_device(0)
+    tp.lib()
+    I, S = args.batch, 1
+    layer = Layer(torch, tp)
+    log("8 rank shares of the layer resident in HBM")
+    Xh = datagen.gaussian("X", (I, D), 1.0, "bf16", 42)
+    X = to_dev(torch, Xh)
+    B = layer.buffers(I)
+
+    for _ in range(args.warmup):
+        layer.step(X, B, S)
+    torch.cuda.synchronize()
+    mlp_ev = []
+    t0 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        layer.step(X, B, S, mlp_events=mlp_ev)
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = step_bytes(I, S)
+    value = nbytes / (ms * 1e-3) / 1e9
+
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step")
+    mlp_us = statistics.mean(a.elapsed_time(b) * 1e3 for a, b in mlp_ev)
+    mlp_bytes = wl.MlpShape(I, D, F // TP).bytes()
+    achieved = mlp_bytes / (mlp_us * 1e-6) / 1e9
+    roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM, unit="GB/s",
+                frac=round(achieved / PEAK_HBM, 4), traffic=None,
+                kernel=f"tp_shard_mlp I={I} D={D} F_local={F // TP} "
+                       "(gate/up+SwiGLU kernel, then down kernel)",
+                avg_call_us=round(mlp_us, 2), algorithmic_bytes_per_call=mlp_bytes)
+    tf = ROOT / "profiles" / "traffic.json"
+    if tf.exists():
+        tr = json.loads(tf.read_text())
+        key = f"mlp_I{I}"
+        srcs = ["megatron_tensor_layer_amd/csrc/gemv.hip", "megatron_tensor_layer_amd/csrc/gemm.hip"]
+        if key in tr and tr[key].get("src_hash") == src_hash(srcs):
+            roof["traffic"] = tr[key]["bytes_per_call"]
+
+    line = dict(
+        metric="TP-rank MLP shard: decode HBM GB/s, prefill MFMA TFLOP/s, % roofline",
+        value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms, 4), wall_ms_per_step=round(wall_ms, 4), higher_is_better=True,
+        scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+        config=dict(workload=f"llama3.1-70b-shaped layer, TP=8 ranks emulated in turn on one "
+                             f"GPU, decode batch {I} (32 sequences x 1 token): QKV, attention "
+                             "core, o_proj, reduce, SwiGLU MLP, reduce",
+                    D=D, F=F, n_q=NQ, n_kv=NKV, head_dim=HD, tp=TP, tokens=I,
+                    bytes_per_step=nbytes, flops_per_step=step_flops(I),
+                    tokens_per_s_excl_comm=round(I / (ms * 1e-3), 1),
+                    frac_hbm=round(value / PEAK_HBM, 4)),
+        roofline=roof)
+
+    if not args.no_detail:
+        line["detail"] = detail(torch, tp, layer, args.calls)
+        log("per-config detail done")
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(layer, Xh, I, S, nbytes)
+        log("cpu baseline done")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
