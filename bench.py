@@ -172,7 +172,7 @@ def detail(torch, tp, layer, calls):
     out = {}
     T = torch
     # Llama-3.1-70B MLP rank share, TP=8: rotate through the 8 real rank shards
-    for I in (1, 16, 64, 256):
+    for I in (1, 16, 32, 64, 256):
         X = to_dev(T, datagen.gaussian("X", (I, D), 1.0, "bf16", 1000 + I))
         H = T.empty((I, F // TP), dtype=T.bfloat16, device="cuda")
         P = T.empty((I, D), dtype=T.float32, device="cuda")
@@ -185,6 +185,22 @@ def detail(torch, tp, layer, calls):
             **st, GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM, 3),
             TFLOPs=round(m.flops() / (st["median_us"] * 1e-6) / 1e12, 1),
             tokens_per_s=round(I / (st["median_us"] * 1e-6)))
+    # the attention projections of the layer's rank shares at decode 32
+    I = 32
+    nql, nkl = NQ // TP, NKV // TP
+    X = to_dev(T, datagen.gaussian("X", (I, D), 1.0, "bf16", 1032))
+    A = to_dev(T, datagen.gaussian("A", (I, nql * HD), 1.0, "bf16", 1032))
+    Q = T.empty((I, (nql + 2 * nkl) * HD), dtype=T.bfloat16, device="cuda")
+    P = T.empty((I, D), dtype=T.float32, device="cuda")
+    for name, fns, nbytes in (
+            ("qkv", [(lambda R=R: tp.shard_attn_proj(tp.TP_ATTN_QKV, X, R["qkv"], Q, nql, nkl, HD))
+                     for R in layer.ranks], wl.QkvShape(I, D, nql, nkl, HD).bytes()),
+            ("o_proj", [(lambda R=R: tp.shard_attn_proj(tp.TP_ATTN_O, A, R["o"], P, nql, nkl, HD))
+                        for R in layer.ranks], wl.OprojShape(I, D, nql, HD).bytes())):
+        st = stats(time_calls(T, fns, calls))
+        gbs = nbytes / (st["median_us"] * 1e-6) / 1e9
+        out[f"llama70b_{name}_tp8_decode_I32"] = dict(**st, GBps=round(gbs, 1),
+                                                      frac_hbm=round(gbs / PEAK_HBM, 3))
     # prefill 512, TP=8 shards and the TP=1 unsharded MLP
     I = 512
     X = to_dev(T, datagen.gaussian("X", (I, D), 1.0, "bf16", 1512))

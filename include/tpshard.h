@@ -63,8 +63,9 @@ const char* tp_status_string(tp_status_t s);
 
 /*
  * Device workspace, in bytes, that tp_shard_mlp needs for these sizes
- * (0 if none).  Host-only; never touches the GPU.  Returns 0 for invalid
- * sizes (the call itself then reports the error).
+ * (0 if none: few-token and many-token calls need none).  Host-only; never
+ * touches the GPU.  Returns 0 for invalid sizes (the call itself then reports
+ * the error).
  */
 size_t tp_shard_mlp_workspace_size(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt);
 
@@ -88,8 +89,11 @@ size_t tp_shard_mlp_workspace_size(int64_t I, int64_t D, int64_t F_local, tp_dty
  *                         to nearest-even on the bf16 path)
  *   P       [I, D]        fp32, overwritten (never accumulated into)
  *   workspace, workspace_bytes: device scratch of at least
- *           tp_shard_mlp_workspace_size(...) bytes (may be NULL when that is 0);
- *           contents on entry are ignored, on return undefined.
+ *           tp_shard_mlp_workspace_size(...) bytes, 16-byte aligned, not
+ *           overlapping any other argument (may be NULL when the size is 0).
+ *           9..64-token bf16 calls keep split-K fp32 partial sums there;
+ *           contents on entry are ignored, on return undefined.  Two calls
+ *           in flight at once (other streams) need separate workspaces.
  * Errors: TP_ERR_INVALID, TP_ERR_MISALIGNED (D or F_local not a multiple of 8,
  * a pointer not 16-byte aligned), TP_ERR_WORKSPACE, TP_ERR_LAUNCH.
  */

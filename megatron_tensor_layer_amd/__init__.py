@@ -112,6 +112,34 @@ def mlp_workspace_bytes(I: int, D: int, F_local: int, dtype: int = TP_BF16) -> i
     return lib().tp_shard_mlp_workspace_size(I, D, F_local, dtype)
 
 
+def attn_workspace_bytes(phase: int, I: int, D: int, n_q_local: int, n_kv_local: int,
+                         head_dim: int, dtype: int = TP_BF16) -> int:
+    return lib().tp_shard_attn_proj_workspace_size(phase, I, D, n_q_local, n_kv_local,
+                                                   head_dim, dtype)
+
+
+# One scratch buffer per device, grown on demand, used when a caller passes no
+# workspace.  Calls that may run concurrently on different streams of one
+# device must pass their own workspace instead.
+_ws_cache: dict = {}
+
+
+def _workspace(dev, nbytes: int):
+    if nbytes <= 0:
+        return None, 0
+    torch = _torch()
+    buf = _ws_cache.get(dev)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _ws_cache[dev] = buf
+    return _ptr(buf), buf.numel()
+
+
+def _user_workspace(workspace):
+    _dev(workspace)
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
 def shard_mlp(X, W_gate, W_up, W_down, H, P, workspace=None, stream=None) -> None:
     """P[I,D]{U_X} = (silu(X W_gate[D,F_X]) * (X W_up[D,F_X])) W_down[F_X,D]; H gets
     the SwiGLU activations.  Weights output-major: W_gate/W_up [F_local, D],
@@ -129,10 +157,10 @@ def shard_mlp(X, W_gate, W_up, W_down, H, P, workspace=None, stream=None) -> Non
     if (W_gate.shape != (F_local, D) or W_up.shape != (F_local, D)
             or W_down.shape != (D, F_local) or H.shape != (I, F_local) or P.shape != (I, D)):
         raise ValueError("shape mismatch")
-    ws_ptr, ws_bytes = None, 0
     if workspace is not None:
-        _dev(workspace)
-        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+        ws_ptr, ws_bytes = _user_workspace(workspace)
+    else:
+        ws_ptr, ws_bytes = _workspace(dev, mlp_workspace_bytes(I, D, F_local, dt))
     _check("tp_shard_mlp", lib().tp_shard_mlp(I, D, F_local, dt, _ptr(X), _ptr(W_gate),
                                               _ptr(W_up), _ptr(W_down), _ptr(H), _ptr(P),
                                               ws_ptr, ws_bytes, _stream(stream, dev)))
@@ -161,9 +189,11 @@ def shard_attn_proj(phase: int, inp, W, out, n_q_local: int, n_kv_local: int, he
             raise ValueError("shape/dtype mismatch (O)")
     else:
         raise ValueError("bad phase")
-    ws_ptr, ws_bytes = None, 0
     if workspace is not None:
-        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+        ws_ptr, ws_bytes = _user_workspace(workspace)
+    else:
+        ws_ptr, ws_bytes = _workspace(dev, attn_workspace_bytes(phase, I, D, n_q_local,
+                                                                n_kv_local, head_dim, dt))
     _check("tp_shard_attn_proj",
            lib().tp_shard_attn_proj(phase, I, D, n_q_local, n_kv_local, head_dim, dt, _ptr(inp),
                                     _ptr(W), _ptr(out), ws_ptr, ws_bytes, _stream(stream, dev)))

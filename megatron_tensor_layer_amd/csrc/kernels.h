@@ -2,7 +2,11 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
+
+#include <algorithm>
+#include <cmath>
 
 namespace tpk {
 
@@ -17,6 +21,17 @@ constexpr int kGemvMaxTokens = 8;
 template <typename T, int EPI>
 hipError_t gemv_launch(int I, int K, int N, const T* X, int64_t ldx, const T* W0,
                        const T* W1, void* out, int64_t ldo, hipStream_t stream);
+
+// Same product on bf16 MFMA for 9..64 tokens, weights streamed once from HBM,
+// K split over workgroups; `workspace` (splitk_workspace_bytes) holds the
+// arrival counters and the fp32 partial sums, contents on entry ignored.
+constexpr int kSplitKMaxTokens = 64;
+constexpr int64_t kSplitKMaxK = int64_t(1) << 23;
+size_t splitk_workspace_bytes(int I, int K, int N, bool swiglu);
+template <int EPI>
+hipError_t splitk_launch(int I, int K, int N, const uint16_t* X, const uint16_t* W0,
+                         const uint16_t* W1, void* out, int64_t ldo, void* workspace,
+                         hipStream_t stream);
 
 // Same product on bf16 MFMA for any M.
 template <int EPI>

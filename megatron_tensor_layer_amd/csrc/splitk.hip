@@ -1,0 +1,371 @@
+// Decode projections for 9..64 tokens: y[m, n] = sum_k X[m, k] W[n, k] on bf16
+// MFMA, streaming W from HBM once at close to the achievable read rate.
+//
+// Decode reads each weight of the rank's shard once per step (lecture
+// "Distributed Serving", §1.1 and §3.4); the design is about keeping every CU
+// streaming until the end:
+//   * the weight rows (for SwiGLU: gate rows, then up rows) are cut into
+//     16-row tiles and the K axis into NS ranges; a workgroup owns NW tiles
+//     times one K range, and the host picks NW and NS so the grid is close to
+//     one workgroup per CU (256 on MI355X) -- no second, half-empty wave of
+//     workgroups;
+//   * each wave streams its own tile: one load instruction reads 4 rows x 256
+//     contiguous bytes (whole cache lines) into registers, P groups of 128 K
+//     in flight; the group is transposed through a private 4 KB LDS tile
+//     (16-byte slots XOR-swizzled by row, conflict-free both ways) into the B
+//     operand of v_mfma_f32_16x16x32_bf16;
+//   * the activations of the workgroup's K range are staged once in LDS with
+//     direct global->LDS loads and shared by all waves (A operand);
+//   * no barrier after the start: waves run independently;
+//   * each workgroup writes fp32 partial sums part[split][m][row]; the last
+//     of a row block's NS workgroups to arrive (an arrival counter in the
+//     workspace) adds the NS partials in split order -- deterministic,
+//     whichever arrives last -- and applies the epilogue: fp32 store, bf16
+//     store, or silu(gate) * up (lecture §4.1: the SwiGLU elementwise op is
+//     local to the rank).  A SwiGLU row block holds the gate tiles and the up
+//     tiles of the same F block, so the epilogue has both;
+//   * one kernel launch per projection: no separate reduction pass.
+#include <atomic>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace tpk {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any record: reads zero
+constexpr int kAuxSys = 17;             // sc0 sc1: system coherent, bypasses L1 and L2
+constexpr int kGK = 128;                // K elements per streamed group
+constexpr int kLdsMax = 160 * 1024 - 1024;  // dynamic LDS budget (static LDS sits before it)
+constexpr int kCUs = 256;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Arrival at a row block's counter word (call_id << 32 | arrivals).  A word
+// from another call (or garbage) restarts the count at 1, so the workspace
+// needs no reset between calls.  Returns the arrivals including this one.
+// Each failed CAS means another arrival succeeded, so the loop is bounded.
+__device__ __forceinline__ unsigned arrive(unsigned long long* word, unsigned call_id) {
+  unsigned long long expect = 0;
+  for (;;) {
+    const unsigned long long want = ((expect >> 32) == call_id)
+                                        ? expect + 1
+                                        : (((unsigned long long)call_id << 32) | 1ull);
+    const unsigned long long seen = atomicCAS(word, expect, want);
+    if (seen == expect) return (unsigned)(want & 0xffffffffull);
+    expect = seen;
+  }
+}
+
+// Row space of the partial sums: row block rb holds NW 16-row tiles.  Single
+// matrix (N rows): block rb covers rows [16 NW rb, 16 NW (rb + 1)).  SwiGLU
+// (gate W0 and up W1, N rows each): block rb covers F rows f0 = 8 NW rb ..
+// f0 + 8 NW, its first NW/2 tiles from gate, the other NW/2 from up.
+template <int MT, int P, int EPI>
+__global__ void __launch_bounds__(1024)
+splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
+              const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int KR,
+              unsigned long long* __restrict__ counters, float* __restrict__ part, int NR,
+              void* __restrict__ out, int64_t ldo, unsigned call_id) {
+  constexpr int TOK = 16 * MT;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  __shared__ int is_last;
+  const int NW = blockDim.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int XRB = KR * 2;                                   // LDS bytes per token row
+  unsigned char* xs = lds;
+  unsigned char* tile = lds + TOK * XRB + wave * 4096;
+  const int ns = (K + KR - 1) / KR;
+  const int split = blockIdx.x % ns;
+  const int rb = blockIdx.x / ns;
+  const int k0 = split * KR;
+  const int kend = min(K, k0 + KR);
+
+  // ---- activations of this K range -> LDS; slot s of token t holds chunk s ^ (t & 15)
+  {
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)I * (uint32_t)K * 2u);
+    const int XSL = KR / 8;
+    const int XI = TOK * XSL / 64;
+    for (int q = wave; q < XI; q += NW) {
+      const int slot = q * 64 + lane;
+      const int t = slot / XSL, sl = slot % XSL;
+      const int k = k0 + (sl ^ (t & 15)) * 8;
+      const uint32_t off = (k < kend) ? ((uint32_t)t * (uint32_t)K + (uint32_t)k) * 2u : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t*)(xs + q * 1024), 16, off, 0, 0, 0);
+    }
+  }
+
+  // ---- this wave's 16 weight rows: uniform base, rows past the matrix read zero
+  int wrow0;
+  const uint16_t* wmat;
+  if constexpr (EPI == EPI_SWIGLU) {
+    const int half = NW / 2;
+    wrow0 = rb * 16 * half + 16 * (wave % half);
+    wmat = wave < half ? W0 : W1;
+  } else {
+    wrow0 = (rb * NW + wave) * 16;
+    wmat = W0;
+  }
+  const int rows = max(0, min(16, N - wrow0));
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(wmat + (int64_t)wrow0 * K, (uint32_t)rows * (uint32_t)K * 2u);
+  const int NG = (kend - k0 + kGK - 1) / kGK;
+
+  // group g, instruction p: rows 4p + lane/16, 16-byte chunk lane%16 of the group
+  auto issue = [&](int g, u32x4_t (&v)[4]) {
+    const int k = k0 + g * kGK + (lane & 15) * 8;
+    const bool ok = g < NG && k < kend;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t r = 4 * p + (lane >> 4);
+      v[p] = buf_load16<kAuxNT>(wr, ok ? (r * (uint32_t)K + (uint32_t)k) * 2u : kOob);
+    }
+  };
+
+  u32x4_t wv[P][4];
+#pragma unroll
+  for (int b = 0; b < P; ++b) issue(b, wv[b]);
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // the activation loads are older than every weight load: once group 0 has
+  // landed, so has this wave's share of X; the barrier publishes all shares
+  wait_vmcnt<(P - 1) * 4>();
+  __syncthreads();
+
+  for (int g0 = 0; g0 < NG; g0 += P) {
+#pragma unroll
+    for (int b = 0; b < P; ++b) {
+      const int g = g0 + b;
+      wait_vmcnt<(P - 1) * 4>();
+      // transpose through the tile: row r = 4p + lane/16 at slot (lane%16) ^ r
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int r = 4 * p + (lane >> 4);
+        *reinterpret_cast<u32x4_t*>(tile + r * 256 + (((lane & 15) ^ r) * 16)) = wv[b][p];
+      }
+      issue(g + P, wv[b]);  // past the end: out-of-range offsets, nothing fetched
+      if (g < NG) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = lane & 15, c = 4 * j + (lane >> 4);
+          const bf16x8_t bw = *reinterpret_cast<const bf16x8_t*>(tile + n * 256 + ((c ^ n) * 16));
+          const int xc = g * 16 + c;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const int t = mt * 16 + (lane & 15);
+            const bf16x8_t ax =
+                *reinterpret_cast<const bf16x8_t*>(xs + t * XRB + ((xc ^ (t & 15)) * 16));
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, acc[mt], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- partial tile C[m][n] (m = (lane/16)*4 + j token, n = lane%16 row) ->
+  // row-space column 16 (NW rb + wave) + n of split plane `split`.  The
+  // partials cross workgroups (and XCDs, whose L2s are not coherent with each
+  // other): they are stored system-coherent (sc0 sc1, written through to
+  // memory) and read back the same way, so no cache-wide writeback or
+  // invalidate is needed; the arrival counter is a device-scope atomic.
+  const int64_t plane = (int64_t)I * NR;
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(part, (uint32_t)(ns * plane * 4));
+  {
+    const int col = (rb * NW + wave) * 16 + (lane & 15);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = mt * 16 + (lane >> 4) * 4 + j;
+        const float v = acc[mt][j];  // bit_cast of a vector-element lvalue reads element 0
+        if (m < I)
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __builtin_bit_cast(uint32_t, v), pr, (uint32_t)((split * plane + (int64_t)m * NR + col) * 4), 0,
+              kAuxSys);
+      }
+  }
+
+  // ---- the last of the block's ns workgroups reduces and stores the block
+  wait_vmcnt<0>();  // this wave's partial stores have reached memory
+  __syncthreads();
+  if (tid == 0) is_last = arrive(counters + rb, call_id) == (unsigned)ns;
+  __syncthreads();
+  if (!is_last) return;
+
+  const int cols = (EPI == EPI_SWIGLU) ? 8 * NW : 16 * NW;  // output columns of the block
+  const int cbase = rb * cols;
+  const int ncols = min(cols, N - cbase);
+  const int cq = (ncols + 3) / 4;
+  const int rs0 = rb * NW * 16;                             // block's first row-space column
+  auto sum_splits = [&](int64_t q) {  // q: element offset of split 0
+    f32x4_t s4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    int r = 0;
+    for (; r + 4 <= ns; r += 4) {
+      f32x4_t v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[e] = __builtin_bit_cast(
+            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         pr, (uint32_t)((q + (r + e) * plane) * 4), 0, kAuxSys));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s4 += v[e];
+    }
+    for (; r < ns; ++r)
+      s4 += __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                            pr, (uint32_t)((q + r * plane) * 4), 0, kAuxSys));
+    return s4;
+  };
+  for (int idx = tid; idx < I * cq; idx += NW * 64) {
+    const int m = idx / cq, c = (idx % cq) * 4;
+    const int64_t q = (int64_t)m * NR + rs0 + c;
+    const f32x4_t s4 = sum_splits(q);
+    f32x4_t v;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const f32x4_t u = sum_splits(q + cols);
+      v = f32x4_t{silu(s4.x) * u.x, silu(s4.y) * u.y, silu(s4.z) * u.z, silu(s4.w) * u.w};
+    } else {
+      v = s4;
+    }
+    const int n = min(4, ncols - c);
+    if constexpr (EPI == EPI_F32) {
+      float* o = static_cast<float*>(out) + (int64_t)m * ldo + cbase + c;
+      if (n == 4 && ((reinterpret_cast<uintptr_t>(o) & 15) == 0)) {
+        *reinterpret_cast<f32x4_t*>(o) = v;
+      } else {
+        for (int e = 0; e < n; ++e) o[e] = v[e];
+      }
+    } else {
+      uint16_t* o = static_cast<uint16_t*>(out) + (int64_t)m * ldo + cbase + c;
+      for (int e = 0; e < n; ++e) o[e] = f32_to_bf16_bits(v[e]);
+    }
+  }
+}
+
+struct Plan {
+  int nw = 0;      // waves (16-row tiles) per workgroup
+  int kr = 0;      // K elements per split (multiple of kGK)
+  int ns = 0;      // number of K splits
+  int rbs = 0;     // row blocks
+  int nr = 0;      // row-space width = 16 * nw * rbs
+  int lds = 0;     // dynamic LDS bytes
+  int grid = 0;
+};
+
+constexpr size_t kCounterAlign = 256;
+
+size_t plan_bytes(const Plan& pl, int I) {
+  const size_t cnt = ((size_t)pl.rbs * 8 + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
+  return cnt + (size_t)pl.ns * (size_t)I * (size_t)pl.nr * sizeof(float);
+}
+
+Plan plan_for(int I, int K, int N, bool swiglu, int nw, int ns_req) {
+  Plan pl;
+  const int mt = (I + 15) / 16;
+  const int groups = (K + kGK - 1) / kGK;
+  const int gps = (groups + ns_req - 1) / ns_req;
+  pl.nw = nw;
+  pl.kr = gps * kGK;
+  pl.ns = (groups + gps - 1) / gps;
+  pl.rbs = swiglu ? (N + 8 * nw - 1) / (8 * nw) : (N + 16 * nw - 1) / (16 * nw);
+  pl.nr = 16 * nw * pl.rbs;
+  pl.lds = 16 * mt * pl.kr * 2 + nw * 4096;
+  pl.grid = pl.rbs * pl.ns;
+  return pl;
+}
+
+// Choose waves per workgroup (nw) and the K split (ns).  Measured on MI355X
+// (one rank's decode projections of the Llama-3.1-70B and Qwen2.5-1.5B shapes):
+// the best grids hold about 200-256 workgroups -- one per CU, none waiting --
+// with 4..16 waves each; every extra split adds an fp32 partial round trip.
+Plan make_plan(int I, int K, int N, bool swiglu) {
+  const int groups = (K + kGK - 1) / kGK;
+  const double wbytes = 2.0 * (swiglu ? 2.0 : 1.0) * N * K;
+  Plan best;
+  double best_score = 1e30;
+  for (int nw = 16; nw >= 2; --nw) {
+    if (swiglu && (nw % 2)) continue;
+    for (int s = 1; s <= groups; ++s) {
+      const Plan pl = plan_for(I, K, N, swiglu, nw, s);
+      if (pl.ns != s || pl.lds > kLdsMax) continue;
+      if ((double)pl.ns * I * pl.nr * 4.0 >= 2147483648.0) continue;
+      const int wgs = pl.grid;
+      const double per_cu_max = std::ceil((double)wgs / kCUs);
+      const double imbalance = per_cu_max * kCUs / (double)wgs;
+      const double underfill = wgs < kCUs ? std::pow((double)kCUs / wgs, 0.6) : 1.0;
+      const double partial = 2.0 * pl.ns * I * pl.nr * 4.0 / wbytes;
+      const double waves = std::min(per_cu_max, 1.0) * nw;
+      const double few = waves < 4 ? (4.0 - waves) / 4.0 : 0.0;
+      const double score = std::max(imbalance, underfill) * (1.0 + partial) * (1.0 + few);
+      if (score < best_score - 1e-9) {
+        best_score = score;
+        best = pl;
+      }
+    }
+  }
+  return best;
+}
+
+// Call ids name one launch in the arrival counters; one sequence for every
+// kernel variant of the process (0 is never used: a zeroed workspace is fresh).
+unsigned next_call_id() {
+  static std::atomic<unsigned> next{0};
+  unsigned id = ++next;
+  if (id == 0) id = ++next;
+  return id;
+}
+
+template <int MT, int EPI>
+hipError_t launch_plan(const Plan& pl, int I, int K, int N, const uint16_t* X,
+                       const uint16_t* W0, const uint16_t* W1, void* out, int64_t ldo,
+                       void* workspace, hipStream_t stream) {
+  auto kern = splitk_kernel<MT, 2, EPI>;
+  static bool attr_set = false;  // raising the dynamic-LDS limit once per process is enough
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const unsigned id = next_call_id();
+  auto* counters = static_cast<unsigned long long*>(workspace);
+  const size_t cnt = ((size_t)pl.rbs * 8 + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + cnt);
+  hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(pl.nw * 64), pl.lds, stream, I, K, N, X, W0, W1,
+                     pl.kr, counters, part, pl.nr, out, ldo, id);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t splitk_workspace_bytes(int I, int K, int N, bool swiglu) {
+  return plan_bytes(make_plan(I, K, N, swiglu), I);
+}
+
+template <int EPI>
+hipError_t splitk_launch(int I, int K, int N, const uint16_t* X, const uint16_t* W0,
+                         const uint16_t* W1, void* out, int64_t ldo, void* workspace,
+                         hipStream_t stream) {
+  const Plan pl = make_plan(I, K, N, EPI == EPI_SWIGLU);
+  if (pl.grid == 0) return hipErrorInvalidValue;
+  if (I <= 16) return launch_plan<1, EPI>(pl, I, K, N, X, W0, W1, out, ldo, workspace, stream);
+  if (I <= 32) return launch_plan<2, EPI>(pl, I, K, N, X, W0, W1, out, ldo, workspace, stream);
+  if (I <= 48) return launch_plan<3, EPI>(pl, I, K, N, X, W0, W1, out, ldo, workspace, stream);
+  return launch_plan<4, EPI>(pl, I, K, N, X, W0, W1, out, ldo, workspace, stream);
+}
+
+template hipError_t splitk_launch<EPI_F32>(int, int, int, const uint16_t*, const uint16_t*,
+                                           const uint16_t*, void*, int64_t, void*, hipStream_t);
+template hipError_t splitk_launch<EPI_DT>(int, int, int, const uint16_t*, const uint16_t*,
+                                          const uint16_t*, void*, int64_t, void*, hipStream_t);
+template hipError_t splitk_launch<EPI_SWIGLU>(int, int, int, const uint16_t*, const uint16_t*,
+                                              const uint16_t*, void*, int64_t, void*,
+                                              hipStream_t);
+
+}  // namespace tpk

@@ -3,10 +3,12 @@
 // Host side only: validates arguments without touching the GPU, picks a
 // kernel family by the token count and enqueues it on the caller's stream.
 //   bf16, I <= 8   few-token streaming kernel (VALU dot2), weights read once
-//   bf16, I > 8    MFMA tiled kernel
+//   bf16, I <= 64  split-K weight streaming on MFMA, workspace for partials
+//   bf16, I > 64   MFMA tiled kernel (LDS double-buffered)
 //   fp32           few-token streaming kernel, 8 tokens per launch
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 
@@ -34,10 +36,27 @@ bool dims_ok(int64_t v) { return v >= 1 && v <= kMaxDim; }
 
 tp_status_t launched(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_LAUNCH; }
 
+// Kernel family for a bf16 projection of I tokens with contraction length K.
+enum class Path { Gemv, SplitK, Gemm };
+Path bf16_path(int64_t I, int64_t K) {
+  // few tokens: weight streaming on VALU; past K = kGemvMaxK16 / 2 the
+  // 8-token variant runs out of registers, so 5..8 tokens go to MFMA there
+  const int64_t kmax = (I <= 4) ? tpk::kGemvMaxK16 : tpk::kGemvMaxK16 / 2;
+  if (I <= tpk::kGemvMaxTokens && K <= kmax) return Path::Gemv;
+  if (I <= tpk::kSplitKMaxTokens && K <= tpk::kSplitKMaxK) return Path::SplitK;
+  return Path::Gemm;
+}
+
+// Workspace of one projection (0 unless it takes the split-K path).
+size_t proj_workspace(int64_t I, int64_t K, int64_t N, bool swiglu, tp_dtype_t dt) {
+  if (dt != TP_BF16 || I < 1 || bf16_path(I, K) != Path::SplitK) return 0;
+  return tpk::splitk_workspace_bytes((int)I, (int)K, (int)N, swiglu);
+}
+
 // One projection out[I, N] = in[I, K] . W[N, K]^T with epilogue EPI.
 template <int EPI>
 hipError_t project(int64_t I, int64_t K, int64_t N, tp_dtype_t dt, const void* in,
-                   const void* W0, const void* W1, void* out, hipStream_t s) {
+                   const void* W0, const void* W1, void* out, void* ws, hipStream_t s) {
   using tpk::gemm_launch;
   using tpk::gemv_launch;
   // element size of the stored output (fp32 partial or dtype)
@@ -46,12 +65,14 @@ hipError_t project(int64_t I, int64_t K, int64_t N, tp_dtype_t dt, const void* i
     auto X = static_cast<const uint16_t*>(in);
     auto A0 = static_cast<const uint16_t*>(W0);
     auto A1 = static_cast<const uint16_t*>(W1);
-    // few tokens: weight streaming on VALU; past K = kGemvMaxK16 / 2 the
-    // 8-token variant runs out of registers, so 5..8 tokens go to MFMA there
-    const int64_t kmax = (I <= 4) ? tpk::kGemvMaxK16 : tpk::kGemvMaxK16 / 2;
-    if (I <= tpk::kGemvMaxTokens && K <= kmax)
-      return gemv_launch<uint16_t, EPI>((int)I, (int)K, (int)N, X, K, A0, A1, out, N, s);
-    return gemm_launch<EPI>((int)I, (int)N, (int)K, X, K, A0, A1, out, N, s);
+    switch (bf16_path(I, K)) {
+      case Path::Gemv:
+        return gemv_launch<uint16_t, EPI>((int)I, (int)K, (int)N, X, K, A0, A1, out, N, s);
+      case Path::SplitK:
+        return tpk::splitk_launch<EPI>((int)I, (int)K, (int)N, X, A0, A1, out, N, ws, s);
+      case Path::Gemm:
+        return gemm_launch<EPI>((int)I, (int)N, (int)K, X, K, A0, A1, out, N, s);
+    }
   }
   auto X = static_cast<const float*>(in);
   auto A0 = static_cast<const float*>(W0);
@@ -89,8 +110,10 @@ const char* tp_status_string(tp_status_t s) {
 }
 
 size_t tp_shard_mlp_workspace_size(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt) {
-  (void)I; (void)D; (void)F_local; (void)dt;
-  return 0;
+  if (!dtype_ok(dt) || I < 1 || I > kMaxDim || !dims_ok(D) || !dims_ok(F_local)) return 0;
+  // gate/up+SwiGLU then down run one after the other and share the workspace
+  return std::max(proj_workspace(I, D, F_local, true, dt),
+                  proj_workspace(I, F_local, D, false, dt));
 }
 
 tp_status_t tp_shard_mlp(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt, const void* X,
@@ -112,22 +135,35 @@ tp_status_t tp_shard_mlp(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt, c
     if (overlap(rH, in) || overlap(rP, in)) return TP_ERR_INVALID;
   if (overlap(rH, rP)) return TP_ERR_INVALID;
   const size_t need = tp_shard_mlp_workspace_size(I, D, F_local, dt);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return TP_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return TP_ERR_MISALIGNED;
+    const Range rW = rng(workspace, (int64_t)need);
+    for (Range o : {rX, rG, rU, rD, rH, rP})
+      if (overlap(rW, o)) return TP_ERR_INVALID;
+  }
   if (dt == TP_F32 && (D > tpk::kGemvMaxK32 || F_local > tpk::kGemvMaxK32))
     return TP_ERR_UNSUPPORTED;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so the checks below are ours
-  hipError_t e = project<tpk::EPI_SWIGLU>(I, D, F_local, dt, X, W_gate, W_up, H, s);
+  hipError_t e = project<tpk::EPI_SWIGLU>(I, D, F_local, dt, X, W_gate, W_up, H, workspace, s);
   if (e != hipSuccess) return TP_ERR_LAUNCH;
-  e = project<tpk::EPI_F32>(I, F_local, D, dt, H, W_down, nullptr, P, s);
+  e = project<tpk::EPI_F32>(I, F_local, D, dt, H, W_down, nullptr, P, workspace, s);
   return launched(e);
 }
 
 size_t tp_shard_attn_proj_workspace_size(tp_attn_phase_t phase, int64_t I, int64_t D,
                                          int64_t n_q_local, int64_t n_kv_local,
                                          int64_t head_dim, tp_dtype_t dt) {
-  (void)phase; (void)I; (void)D; (void)n_q_local; (void)n_kv_local; (void)head_dim; (void)dt;
+  if (!dtype_ok(dt) || I < 1 || I > kMaxDim || !dims_ok(D) || !dims_ok(n_q_local) ||
+      !dims_ok(head_dim))
+    return 0;
+  if (phase == TP_ATTN_QKV) {
+    if (!dims_ok(n_kv_local)) return 0;
+    return proj_workspace(I, D, (n_q_local + 2 * n_kv_local) * head_dim, false, dt);
+  }
+  if (phase == TP_ATTN_O) return proj_workspace(I, n_q_local * head_dim, D, false, dt);
   return 0;
 }
 
@@ -152,14 +188,19 @@ tp_status_t tp_shard_attn_proj(tp_attn_phase_t phase, int64_t I, int64_t D, int6
   if (overlap(rO, rIn) || overlap(rO, rW)) return TP_ERR_INVALID;
   const size_t need =
       tp_shard_attn_proj_workspace_size(phase, I, D, n_q_local, n_kv_local, head_dim, dt);
-  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return TP_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return TP_ERR_MISALIGNED;
+    const Range rWs = rng(workspace, (int64_t)need);
+    if (overlap(rWs, rIn) || overlap(rWs, rW) || overlap(rWs, rO)) return TP_ERR_INVALID;
+  }
   if (dt == TP_F32 && K > tpk::kGemvMaxK32) return TP_ERR_UNSUPPORTED;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (phase == TP_ATTN_QKV)
-    return launched(project<tpk::EPI_DT>(I, K, N, dt, in, W, nullptr, out, s));
-  return launched(project<tpk::EPI_F32>(I, K, N, dt, in, W, nullptr, out, s));
+    return launched(project<tpk::EPI_DT>(I, K, N, dt, in, W, nullptr, out, workspace, s));
+  return launched(project<tpk::EPI_F32>(I, K, N, dt, in, W, nullptr, out, workspace, s));
 }
 
 tp_status_t tp_partial_reduce(int32_t t, int64_t n, const float* partials, tp_dtype_t out_dt,

@@ -119,9 +119,33 @@ def test_attn_core_validation(lib):
 
 
 def test_workspace_queries_are_host_only(lib):
-    assert lib.tp_shard_mlp_workspace_size(64, 8192, 3584, tp.TP_BF16) >= 0
-    assert lib.tp_shard_attn_proj_workspace_size(tp.TP_ATTN_QKV, 32, 8192, 8, 1, 128,
-                                                 tp.TP_BF16) >= 0
+    # split-K decode (9..64 tokens) needs scratch for fp32 partials; few-token
+    # and prefill paths need none; invalid sizes report 0
+    ws = lib.tp_shard_mlp_workspace_size
+    assert ws(32, 8192, 3584, tp.TP_BF16) > 0
+    assert ws(64, 8192, 3584, tp.TP_BF16) >= ws(32, 8192, 3584, tp.TP_BF16) // 4
+    assert ws(1, 8192, 3584, tp.TP_BF16) == 0
+    assert ws(512, 8192, 3584, tp.TP_BF16) == 0
+    assert ws(32, 8192, 3584, tp.TP_F32) == 0
+    assert ws(0, 8192, 3584, tp.TP_BF16) == 0 and ws(32, 0, 3584, tp.TP_BF16) == 0
+    wa = lib.tp_shard_attn_proj_workspace_size
+    assert wa(tp.TP_ATTN_QKV, 32, 8192, 8, 1, 128, tp.TP_BF16) > 0
+    assert wa(tp.TP_ATTN_O, 32, 8192, 8, 1, 128, tp.TP_BF16) > 0
+    assert wa(tp.TP_ATTN_QKV, 1, 8192, 8, 1, 128, tp.TP_BF16) == 0
+    assert wa(7, 32, 8192, 8, 1, 128, tp.TP_BF16) == 0
+
+
+def test_workspace_required_and_checked(lib):
+    need = lib.tp_shard_mlp_workspace_size(32, 256, 512, tp.TP_BF16)
+    assert need > 0
+    assert mlp(lib, I=32, D=256, F=512) == WORKSPACE                       # none given
+    assert mlp(lib, I=32, D=256, F=512, ws=fake(6), wsb=need - 1) == WORKSPACE
+    assert mlp(lib, I=32, D=256, F=512, ws=ctypes.c_void_p(fake(6).value + 8),
+               wsb=need) == MISALIGNED
+    assert mlp(lib, I=32, D=256, F=512, ws=fake(1), wsb=need) == INVALID   # overlaps W_gate
+    f = lambda *a: lib.tp_shard_attn_proj(*a, None)
+    P = [fake(k) for k in range(3)]
+    assert f(tp.TP_ATTN_QKV, 32, 256, 2, 1, 64, tp.TP_BF16, *P, None, 0) == WORKSPACE
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

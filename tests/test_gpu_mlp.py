@@ -28,7 +28,8 @@ def gpu_mlp(X, Wg_r, Wu_r, Wd_r, dtype):
 
 
 # (I, D, F_local, t, r, dtype): few-token kernel (I <= 8), MFMA kernel (I > 8),
-# ragged K tiles (D = 264, 520), ragged F tiles (F_local = 200, 328, 136),
+# weight-streaming MFMA kernel (9..64 tokens), ragged K tiles and steps
+# (D = 264, 520, 1000), ragged F tiles (F_local = 200, 328, 136, 24, 1000),
 # long K (lanes holding 4 and 8 chunks), the fp32 path in 8- and 4-token launches
 SMALL = [
     (1, 264, 200, 2, 1, "bf16"), (2, 264, 200, 2, 0, "bf16"), (3, 136, 72, 1, 0, "bf16"),
@@ -36,7 +37,8 @@ SMALL = [
     (1, 24576, 32, 1, 0, "bf16"), (6, 24576, 32, 1, 0, "bf16"),
     (9, 264, 200, 2, 1, "bf16"), (17, 520, 328, 1, 0, "bf16"), (40, 264, 200, 2, 0, "bf16"),
     (64, 136, 72, 2, 1, "bf16"), (65, 264, 200, 1, 0, "bf16"), (130, 520, 136, 2, 1, "bf16"),
-    (257, 264, 200, 2, 1, "bf16"),
+    (257, 264, 200, 2, 1, "bf16"), (33, 72, 24, 2, 1, "bf16"), (48, 1000, 1000, 1, 0, "bf16"),
+    (16, 2048, 4096, 1, 0, "bf16"),
     (4, 256, 512, 2, 0, "f32"), (11, 264, 200, 2, 1, "f32"), (3, 9216, 64, 1, 0, "f32"),
 ]
 
@@ -220,3 +222,25 @@ def test_mlp_empty_and_errors_touch_nothing():
         tp.partial_reduce(parts, Y)
     T.cuda.synchronize()
     assert T.isnan(H).all() and T.isnan(P).all() and T.isnan(Y).all()
+
+
+def test_explicit_workspace_contents_do_not_matter(llama_mlp):
+    """Split-K decode (9..64 tokens) keeps fp32 partials in the workspace: a
+    caller buffer full of NaN gives the same bits as the binding's own."""
+    L = llama_mlp
+    T = torch()
+    for I in (9, 32, 64):
+        X = to_dev(datagen.gaussian("X", (I, L["D"]), 1.0, "bf16", 77), "bf16")
+        need = tp.mlp_workspace_bytes(I, L["D"], L["F"] // L["t"])
+        assert need > 0
+        ws = T.full((need // 4 + 4,), float("nan"), dtype=T.float32, device="cuda")
+        outs = []
+        for w in (None, ws):
+            H = empty((I, L["F"] // L["t"]), "bf16")
+            P = empty((I, L["D"]), "f32")
+            tp.shard_mlp(X, *L["shards"][5], H, P, workspace=w)
+            outs.append((H, P))
+        T.cuda.synchronize()
+        assert T.equal(outs[0][0], outs[1][0]) and T.equal(outs[0][1], outs[1][1]), I
+        with pytest.raises(tp.TPError, match="WORKSPACE"):
+            tp.shard_mlp(X, *L["shards"][5], outs[0][0], outs[0][1], workspace=ws[:8])
