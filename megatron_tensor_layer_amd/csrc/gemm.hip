@@ -1,21 +1,35 @@
-// Projections for many tokens: C[M, N] = A[M, K] . W[N, K]^T on bf16 MFMA.
+// Projections for many tokens: C[M, N] = A[M, K] . W[N, K]^T on bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
 //
-// Both operands are K-contiguous (activations row-major, weights
-// output-major), so each lane's MFMA operand -- 8 consecutive K elements of
-// one row -- is a single 16-byte load from either matrix.
-//   * workgroup tile BM x BN, K step BK, 4 waves in a WM x WN grid, each wave
-//     computing (BM/WM) x (BN/WN) with v_mfma_f32_32x32x16_bf16;
-//   * A and W tiles staged in LDS, double-buffered: the next K step's global
-//     loads are in flight while MFMA consumes the current buffer; rows are
-//     padded by 16 bytes so the 32 rows a 128-bit LDS read touches fall in
-//     distinct banks;
-//   * the SwiGLU variant stages gate rows f0.. and up rows f0.. of the same
-//     F block in one W tile, so a wave holds g and u of the same (m, f) in
-//     identical accumulator lanes and writes silu(g) * u once (lecture
-//     "Distributed Serving", §4.1: the elementwise op is local to the rank);
-//   * workgroups are dispatched round-robin over the 8 XCDs; the linear
-//     block id is remapped so that tiles sharing a W block run on the same
-//     XCD and its L2 serves the re-reads.
+// Prefill and large decode batches are the compute-heavy side of the layer
+// (lecture "Distributed Serving", §3.4: 2·B·D·F/n FLOPs per rank); the kernel
+// is shaped for gfx950's measured balance -- a 64x64 wave tile keeps MFMA
+// busy only with 8 waves per CU to cover LDS latency, and 128x128 workgroup
+// tiles keep about one workgroup per CU at the per-rank shapes:
+//   * workgroup tile 128 x 128, eight waves: a 2 x 2 grid of 64 x 64 wave
+//     tiles, twice -- the two wave groups take alternate 16-wide K steps of
+//     every stage and are summed through LDS at the end;
+//   * both operands are K-contiguous (activations row-major, weights
+//     output-major) and are copied global -> LDS by the buffer unit directly
+//     (no register staging), 64 K per stage, 4 stages in flight; in LDS a
+//     tile row is 128 bytes and its 16-byte chunk c sits in slot
+//     c ^ ((row / 2) % 8), so the 32 rows one MFMA operand read touches
+//     cover all 64 banks once;
+//   * the SwiGLU variant stages gate rows f0.. and up rows f0.. of the same F
+//     block in one W tile and gives each wave 32 gate and the matching 32 up
+//     rows, so silu(g) * u is formed in registers (lecture §4.1: the
+//     elementwise op is local to the rank);
+//   * when the tiles alone cannot fill the chip (decode batches of 65..256
+//     tokens) the K axis is split over workgroups: each writes an fp32
+//     partial tile, and the last of a tile's workgroups to arrive sums the
+//     partials in split order (deterministic) and applies the epilogue.
+//     Partials cross XCDs, whose L2s are not coherent, so they are written
+//     and read system-coherent; the arrival counter is a device atomic;
+//   * workgroups go round-robin to the 8 XCDs; the block id is remapped so
+//     that each XCD runs a contiguous range of tiles, and tiles sharing a W
+//     block (same N block, other M blocks) are neighbours in that range.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -23,196 +37,419 @@ namespace tpk {
 
 namespace {
 
-constexpr int kPad = 8;  // bf16 elements of padding per LDS row
+constexpr int BM = 128, BN = 128, BK = 64, S = 4;
+constexpr int kThreads = 512;
+constexpr int kRowB = BK * 2;                  // bytes per LDS tile row
+constexpr int kStageA = BM * kRowB;            // 16 KB
+constexpr int kStage = (BM + BN) * kRowB;      // 32 KB
+constexpr int kLds = S * kStage;               // 128 KB
+constexpr uint32_t kOob = 0x80000000u;         // buffer offset past any record: reads zero
+constexpr int kAuxSys = 17;                    // sc0 sc1: system coherent
+constexpr int kCUs = 256;
+static_assert(4 * 16 * 64 * 4 <= kStageA, "a wave pair's K-group reduction fits one stage buffer");
 
-// Row m of the 32x32 accumulator element r (0..15) held by lane `lane` of
-// v_mfma_f32_32x32x16_bf16; the column is lane % 32.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Buffer descriptor words (raw addressing over [base, base + bytes)); kept
+// in SGPRs for the asm load below.
+__device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// 16 bytes per lane from buffer offset `voff` straight into LDS at
+// lds_base + 16 * lane (buffer_load_dwordx4 ... lds; M0 holds lds_base).
+// Written as asm so that the compiler does not add its own wait for it before
+// every LDS read: the kernel orders these loads itself, with an explicit
+// vmcnt wait and a barrier before the stage they fill is read.  No register
+// is written, so nothing in flight can be overwritten.
+__device__ __forceinline__ void lds_dma16(u32x4_t rsrc, uint32_t voff, uint32_t lds_base) {
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// LDS byte offset of (row, logical 16-byte chunk) inside one operand tile.
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * kRowB + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+// Row m (within the 32x32 tile) of accumulator element r held by `lane`; the
+// column is lane % 32.
 __device__ __forceinline__ int acc_row32(int r, int lane) {
   return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int EPI>
-__global__ void __launch_bounds__(256)
-gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
-            const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-            void* __restrict__ out, int64_t ldo) {
-  static_assert(WM * WN == 4, "4 waves");
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int MS = TM / 32, NS = TN / 32;
-  static_assert(MS >= 1 && NS >= 1 && TM % 32 == 0 && TN % 32 == 0, "wave tile");
-  static_assert(EPI != EPI_SWIGLU || NS % 2 == 0, "SwiGLU pairs gate/up subtiles");
-  constexpr int LDK = BK + kPad;
-  constexpr int KCH = BK / 8;                 // 16-byte chunks per tile row
-  constexpr int A_CH = BM * KCH / 256;        // chunks per thread
-  constexpr int B_CH = BN * KCH / 256;
-  static_assert(A_CH * 256 == BM * KCH && B_CH * 256 == BN * KCH, "tile / thread split");
-
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDK];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-
-  // ---- tile of this workgroup, XCD-aware
-  const int mt_n = (M + BM - 1) / BM;
-  const int cols_per_tile = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  const int nt_n = (N + cols_per_tile - 1) / cols_per_tile;
-  const int ntiles = mt_n * nt_n;
-  int b = blockIdx.x;
-  if ((ntiles & 7) == 0) b = (b & 7) * (ntiles >> 3) + (b >> 3);
-  const int tm = b % mt_n, tn = b / mt_n;
-  const int m0 = tm * BM;
-  const int c0 = tn * cols_per_tile;  // first output column
-
-  // ---- global -> register staging
-  const int KT = (K + BK - 1) / BK;
-  const int KC = K / 8;
-  u32x4_t ra[A_CH], rb[B_CH];
-
-  auto load_tiles = [&](int kt) {
-#pragma unroll
-    for (int s = 0; s < A_CH; ++s) {
-      const int q = tid + s * 256;
-      const int row = q / KCH, kc = kt * KCH + q % KCH;
-      const int m = m0 + row;
-      ra[s] = (m < M && kc < KC)
-                  ? *reinterpret_cast<const u32x4_t*>(A + (int64_t)m * lda + (int64_t)kc * 8)
-                  : u32x4_t{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int s = 0; s < B_CH; ++s) {
-      const int q = tid + s * 256;
-      const int row = q / KCH, kc = kt * KCH + q % KCH;
-      const uint16_t* Wm;
-      int n;
-      if (EPI == EPI_SWIGLU) {
-        Wm = row < BN / 2 ? W0 : W1;
-        n = c0 + (row < BN / 2 ? row : row - BN / 2);
-      } else {
-        Wm = W0;
-        n = c0 + row;
-      }
-      rb[s] = (n < N && kc < KC)
-                  ? __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4_t*>(Wm + (int64_t)n * K + (int64_t)kc * 8))
-                  : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tiles = [&](int buf) {
-#pragma unroll
-    for (int s = 0; s < A_CH; ++s) {
-      const int q = tid + s * 256;
-      *reinterpret_cast<u32x4_t*>(&As[buf][q / KCH][(q % KCH) * 8]) = ra[s];
-    }
-#pragma unroll
-    for (int s = 0; s < B_CH; ++s) {
-      const int q = tid + s * 256;
-      *reinterpret_cast<u32x4_t*>(&Bs[buf][q / KCH][(q % KCH) * 8]) = rb[s];
-    }
-  };
-
-  // tile row of W feeding subtile ns of this wave
-  auto b_row0 = [&](int ns) {
-    if (EPI == EPI_SWIGLU) {
-      const int half = NS / 2;
-      return (ns < half) ? wn * (TN / 2) + ns * 32 : BN / 2 + wn * (TN / 2) + (ns - half) * 32;
-    }
-    return wn * TN + ns * 32;
-  };
-
-  f32x16_t acc[MS][NS];
-#pragma unroll
-  for (int i = 0; i < MS; ++i)
-#pragma unroll
-    for (int j = 0; j < NS; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  load_tiles(0);
-  store_tiles(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) load_tiles(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int kof = kk * 16 + (lane >> 5) * 8;
-      bf16x8_t af[MS], bfr[NS];
-#pragma unroll
-      for (int i = 0; i < MS; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&As[buf][wm * TM + i * 32 + (lane & 31)][kof]);
-#pragma unroll
-      for (int j = 0; j < NS; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(&Bs[buf][b_row0(j) + (lane & 31)][kof]);
-#pragma unroll
-      for (int i = 0; i < MS; ++i)
-#pragma unroll
-        for (int j = 0; j < NS; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) store_tiles(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue
-#pragma unroll
-  for (int i = 0; i < MS; ++i) {
-#pragma unroll
-    for (int j = 0; j < ((EPI == EPI_SWIGLU) ? NS / 2 : NS); ++j) {
-      int col;
-      if (EPI == EPI_SWIGLU)
-        col = c0 + wn * (TN / 2) + j * 32 + (lane & 31);
-      else
-        col = c0 + wn * TN + j * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * TM + i * 32 + acc_row32(r, lane);
-        if (m < M && col < N) {
-          if constexpr (EPI == EPI_SWIGLU) {
-            const float g = acc[i][j][r], u = acc[i][j + NS / 2][r];
-            static_cast<uint16_t*>(out)[(int64_t)m * ldo + col] = f32_to_bf16_bits(silu(g) * u);
-          } else if constexpr (EPI == EPI_F32) {
-            static_cast<float*>(out)[(int64_t)m * ldo + col] = acc[i][j][r];
-          } else {
-            static_cast<uint16_t*>(out)[(int64_t)m * ldo + col] = f32_to_bf16_bits(acc[i][j][r]);
-          }
-        }
-      }
-    }
+// Arrival at a tile's counter word (call_id << 32 | arrivals); a word from
+// another call restarts the count, so the workspace needs no reset.
+__device__ __forceinline__ unsigned arrive(unsigned long long* word, unsigned call_id) {
+  unsigned long long expect = 0;
+  for (;;) {
+    const unsigned long long want = ((expect >> 32) == call_id)
+                                        ? expect + 1
+                                        : (((unsigned long long)call_id << 32) | 1ull);
+    const unsigned long long seen = atomicCAS(word, expect, want);
+    if (seen == expect) return (unsigned)(want & 0xffffffffull);
+    expect = seen;
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int EPI>
-hipError_t launch_cfg(int M, int N, int K, const uint16_t* A, int64_t lda, const uint16_t* W0,
-                      const uint16_t* W1, void* out, int64_t ldo, hipStream_t stream) {
-  const int cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
-  const int ntiles = ((M + BM - 1) / BM) * ((N + cols - 1) / cols);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, BK, WM, WN, EPI>), dim3(ntiles), dim3(256), 0, stream,
-                     M, N, K, A, lda, W0, W1, out, ldo);
+template <int EPI>
+__device__ __forceinline__ void store_out(void* out, int64_t ldo, int m, int col, float v) {
+  if constexpr (EPI == EPI_F32)
+    static_cast<float*>(out)[(int64_t)m * ldo + col] = v;
+  else
+    static_cast<uint16_t*>(out)[(int64_t)m * ldo + col] = f32_to_bf16_bits(v);
+}
+
+// One launch: grid = tiles * ns workgroups of 512 threads, 128 KB static LDS.
+//   KR: K elements per split (multiple of BK); ns = ceil(K / KR).
+//   counters/part: split-K workspace (unused when ns == 1).
+template <int EPI>
+__global__ void __launch_bounds__(kThreads)
+gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
+            const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
+            void* __restrict__ out, int64_t ldo, int KR, unsigned long long* __restrict__ counters,
+            float* __restrict__ part, unsigned call_id) {
+  // one array per stage and operand: the loads into a stage and the reads
+  // of another are then visibly disjoint, so the compiler's own wait before
+  // an LDS read covers only the stage being read
+  __shared__ __attribute__((aligned(16))) unsigned char sa0[kStageA], sa1[kStageA], sa2[kStageA],
+      sa3[kStageA], sb0[kStageA], sb1[kStageA], sb2[kStageA], sb3[kStageA];
+  __shared__ int is_last;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
+  const int g = wave >> 2;              // K group
+  const int wm = (wave >> 1) & 1, wn = wave & 1;
+
+  // ---- tile and split of this workgroup, XCD-aware
+  const int mt_n = (M + BM - 1) / BM;
+  constexpr int kCols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns per tile
+  const int nt_n = (N + kCols - 1) / kCols;
+  const int tiles = mt_n * nt_n;
+  const int ns = (K + KR - 1) / KR;
+  const int G = tiles * ns;
+  int b = blockIdx.x;
+  const int G8 = G & ~7;
+  if (b < G8) b = (b & 7) * (G8 >> 3) + (b >> 3);
+  const int split = b / tiles;
+  const int tile = b % tiles;
+  const int tm = tile % mt_n, tn = tile / mt_n;
+  const int m0 = tm * BM, c0 = tn * kCols;
+  const int kb = split * KR, ke = min(K, kb + KR);
+
+  // ---- operand sources: X rows m0.., W rows c0.. (SwiGLU: 64 gate + 64 up)
+  const u32x4_t ra = rsrc_words(A + (int64_t)m0 * lda, (uint32_t)min(BM, M - m0) * (uint32_t)lda * 2u);
+  const int wrows = min(kCols, N - c0);
+  const u32x4_t rw0 = rsrc_words(W0 + (int64_t)c0 * K, (uint32_t)wrows * (uint32_t)K * 2u);
+  const u32x4_t rw1 = rsrc_words((EPI == EPI_SWIGLU ? W1 : W0) + (int64_t)c0 * K,
+                                 (uint32_t)wrows * (uint32_t)K * 2u);
+
+  // Stage st (K from kb + 64 st) into buffer buf.  One instruction writes
+  // 1 KB = 8 tile rows; lane l fills slot l % 8 of row 8q + l / 8 with the
+  // logical chunk that lds_off places there.  Wave w issues A and W
+  // instructions w and w + 8.  Past the K range (or past M / N) the offset
+  // is out of range and the slot is zero-filled.
+  const int rr = lane >> 3, sl = lane & 7;
+  auto issue = [&](int st, const unsigned char* sa, const unsigned char* sb) {
+    const uint32_t la = lds_addr(sa), lb = lds_addr(sb);  // constants: static arrays
+    const int k0 = kb + st * BK;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q = wave + h * 8;
+      const int r = q * 8 + rr;
+      const int c = sl ^ ((r >> 1) & 7);
+      const int k = k0 + c * 8;
+      const bool kin = k < ke;
+      const uint32_t oa = (kin && m0 + r < M) ? (uint32_t)r * (uint32_t)lda * 2u + (uint32_t)k * 2u
+                                              : kOob;
+      lds_dma16(ra, oa, la + q * 1024);
+      int wr;  // row within its weight matrix block
+      if constexpr (EPI == EPI_SWIGLU)
+        wr = r & 63;  // h == 0: gate rows (r < 64), h == 1: up rows
+      else
+        wr = r;
+      const uint32_t ow = (kin && wr < wrows) ? (uint32_t)wr * (uint32_t)K * 2u + (uint32_t)k * 2u
+                                              : kOob;
+      lds_dma16((EPI == EPI_SWIGLU && h == 1) ? rw1 : rw0, ow, lb + q * 1024);
+    }
+  };
+
+  // W tile rows feeding this wave's two 32-column fragments
+  int brow[2];
+  if constexpr (EPI == EPI_SWIGLU) {
+    brow[0] = wn * 32;       // gate f = c0 + wn*32 + lane%32
+    brow[1] = 64 + wn * 32;  // up, same f
+  } else {
+    brow[0] = wn * 64;
+    brow[1] = wn * 64 + 32;
+  }
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int NT = (ke - kb + BK - 1) / BK;
+  issue(0, sa0, sb0);
+  issue(1, sa1, sb1);
+  issue(2, sa2, sb2);
+
+  // K step kt reads buffers (sa, sb) and refills (na, nb) -- the buffers of
+  // step kt - 1 -- with stage kt + 3
+  auto step = [&](int kt, const unsigned char* sa, const unsigned char* sb, unsigned char* na,
+                  unsigned char* nb) {
+    wait_vmcnt<(S - 2) * 4>();  // this wave's part of stage kt has landed
+    __syncthreads();            // everyone's has; stage kt - 1 is consumed
+    issue(kt + S - 1, na, nb);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = (2 * g + h) * 2 + (lane >> 5);  // 16-wide K step 2g + h
+      bf16x8_t af[2], bw[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + lds_off(wm * 64 + i * 32 + (lane & 31), c));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bw[j] = *reinterpret_cast<const bf16x8_t*>(sb + lds_off(brow[j] + (lane & 31), c));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bw[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  for (int kt = 0; kt < NT; kt += S) {
+    step(kt, sa0, sb0, sa3, sb3);
+    if (kt + 1 < NT) step(kt + 1, sa1, sb1, sa0, sb0);
+    if (kt + 2 < NT) step(kt + 2, sa2, sb2, sa1, sb1);
+    if (kt + 3 < NT) step(kt + 3, sa3, sb3, sa2, sb2);
+  }
+
+  // ---- sum the two K groups through LDS (lane-linear, conflict-free)
+  wait_vmcnt<0>();  // zero-fill loads of stages past the end have landed
+  __syncthreads();
+  const int pair = wave & 3;  // waves pair and pair + 4 hold the same tile
+  float* red = reinterpret_cast<float*>(pair == 0 ? sa0 : pair == 1 ? sa1 : pair == 2 ? sa2 : sa3);
+  if (g == 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((i * 2 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+  }
+  __syncthreads();
+  if (g == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * 2 + j) * 16 + r) * 64 + lane];
+  }
+
+  if (ns == 1) {
+    if (g != 0) return;
+    // ---- direct epilogue
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int col = c0 + wn * 32 + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * 64 + i * 32 + acc_row32(r, lane);
+          if (m < M && col < N)
+            store_out<EPI_DT>(out, ldo, m, col, silu(acc[i][0][r]) * acc[i][1][r]);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = c0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + wm * 64 + i * 32 + acc_row32(r, lane);
+            if (m < M && col < N) store_out<EPI>(out, ldo, m, col, acc[i][j][r]);
+          }
+        }
+    }
+    return;
+  }
+
+  // ---- split K: partial tile [BM][BN] in W-tile row order, then arrival
+  const int64_t tile_elems = (int64_t)BM * BN;
+  const __amdgpu_buffer_rsrc_t pr =
+      make_rsrc(part, (uint32_t)((int64_t)ns * tiles * tile_elems * 4));
+  const int64_t tbase = (int64_t)tile * tile_elems;  // split 0 of this tile
+  const int64_t plane = (int64_t)tiles * tile_elems;
+  if (g == 0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int tc = brow[j] + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tr = wm * 64 + i * 32 + acc_row32(r, lane);
+          const float v = acc[i][j][r];
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __builtin_bit_cast(uint32_t, v), pr,
+              (uint32_t)((split * plane + tbase + tr * BN + tc) * 4), 0, kAuxSys);
+        }
+      }
+  }
+  wait_vmcnt<0>();  // partial stores have reached memory
+  __syncthreads();
+  if (tid == 0) is_last = arrive(counters + tile, call_id) == (unsigned)ns;
+  __syncthreads();
+  if (!is_last) return;
+
+  // Sum of the ns split tiles at element offset q (split 0), in split order;
+  // eight loads in flight, offsets past the last split read zero.
+  auto sum_splits = [&](int64_t q) {
+    f32x4_t s4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < ns; s += 8) {
+      f32x4_t v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[e] = __builtin_bit_cast(
+            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         pr, s + e < ns ? (uint32_t)((q + (s + e) * plane) * 4) : kOob, 0,
+                         kAuxSys));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s4 += v[e];
+    }
+    return s4;
+  };
+  constexpr int kQ = kCols / 4;  // float4 items per output row of the tile
+  for (int idx = tid; idx < BM * kQ; idx += kThreads) {
+    const int tr = idx / kQ, tc = (idx % kQ) * 4;
+    const int m = m0 + tr;
+    if (m >= M) continue;
+    const f32x4_t s4 = sum_splits(tbase + tr * BN + tc);
+    f32x4_t v;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const f32x4_t u = sum_splits(tbase + tr * BN + 64 + tc);
+      v = f32x4_t{silu(s4.x) * u.x, silu(s4.y) * u.y, silu(s4.z) * u.z, silu(s4.w) * u.w};
+    } else {
+      v = s4;
+    }
+    const int n = min(4, N - (c0 + tc));
+    for (int e = 0; e < n; ++e)
+      store_out<EPI == EPI_F32 ? EPI_F32 : EPI_DT>(out, ldo, m, c0 + tc + e, v[e]);
+  }
+}
+
+struct Plan {
+  int tiles = 0;
+  int ns = 0;  // K splits
+  int kr = 0;  // K per split
+  int grid = 0;
+};
+
+constexpr size_t kCounterAlign = 256;
+
+// Split K when the tiles alone leave CUs idle: pick the split count that
+// minimises the busiest CU's share of work (in whole tiles), charging each
+// extra split a little for its partial round trip; at least 8 stages of K
+// per split, and the partials stay addressable with 32-bit offsets.
+Plan make_plan(int M, int N, int K, bool swiglu) {
+  Plan pl;
+  const int cols = swiglu ? BN / 2 : BN;
+  pl.tiles = ((M + BM - 1) / BM) * ((N + cols - 1) / cols);
+  const int kst = (K + BK - 1) / BK;  // K stages in all
+  const int max_ns = std::max(1, std::min(16, kst / 8));
+  int best_ns = 1;
+  double best = 1e30;
+  for (int ns = 1; ns <= max_ns; ++ns) {
+    if (ns > 1 && (double)ns * pl.tiles * BM * BN * 4.0 >= 2147483648.0) break;
+    const double busiest = std::ceil((double)pl.tiles * ns / kCUs) / ns;
+    const double cost = busiest * (1.0 + 0.04 * (ns - 1));
+    if (cost < best - 1e-9) {
+      best = cost;
+      best_ns = ns;
+    }
+  }
+  const int sps = (kst + best_ns - 1) / best_ns;  // stages per split
+  pl.kr = sps * BK;
+  pl.ns = (K + pl.kr - 1) / pl.kr;
+  pl.grid = pl.tiles * pl.ns;
+  return pl;
+}
+
+size_t plan_bytes(const Plan& pl) {
+  if (pl.ns <= 1) return 0;
+  const size_t cnt = ((size_t)pl.tiles * 8 + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
+  return cnt + (size_t)pl.ns * pl.tiles * BM * BN * sizeof(float);
+}
+
+unsigned next_call_id() {
+  static std::atomic<unsigned> next{0};
+  unsigned id = ++next;
+  if (id == 0) id = ++next;
+  return id;
+}
+
+template <int EPI>
+hipError_t launch_plan(const Plan& pl, int M, int N, int K, const uint16_t* A, int64_t lda,
+                       const uint16_t* W0, const uint16_t* W1, void* out, int64_t ldo,
+                       void* workspace, hipStream_t stream) {
+  auto kern = gemm_kernel<EPI>;
+  unsigned long long* counters = nullptr;
+  float* part = nullptr;
+  unsigned id = 0;
+  if (pl.ns > 1) {
+    if (workspace == nullptr) return hipErrorInvalidValue;
+    id = next_call_id();
+    counters = static_cast<unsigned long long*>(workspace);
+    const size_t cnt =
+        ((size_t)pl.tiles * 8 + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
+    part = reinterpret_cast<float*>(static_cast<char*>(workspace) + cnt);
+  }
+  hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(kThreads), 0, stream, M, N, K, A, lda, W0,
+                     W1, out, ldo, pl.kr, counters, part, id);
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t gemm_workspace_bytes(int M, int N, int K, bool swiglu) {
+  return plan_bytes(make_plan(M, N, K, swiglu));
+}
+
 template <int EPI>
 hipError_t gemm_launch(int M, int N, int K, const uint16_t* A, int64_t lda, const uint16_t* W0,
-                       const uint16_t* W1, void* out, int64_t ldo, hipStream_t stream) {
-  if (M <= 64)
-    return launch_cfg<64, 128, 64, 2, 2, EPI>(M, N, K, A, lda, W0, W1, out, ldo, stream);
-  return launch_cfg<128, 128, 64, 2, 2, EPI>(M, N, K, A, lda, W0, W1, out, ldo, stream);
+                       const uint16_t* W1, void* out, int64_t ldo, void* workspace,
+                       hipStream_t stream) {
+  const Plan pl = make_plan(M, N, K, EPI == EPI_SWIGLU);
+  if (pl.grid == 0) return hipErrorInvalidValue;
+  return launch_plan<EPI>(pl, M, N, K, A, lda, W0, W1, out, ldo, workspace, stream);
 }
 
 template hipError_t gemm_launch<EPI_F32>(int, int, int, const uint16_t*, int64_t,
-                                         const uint16_t*, const uint16_t*, void*, int64_t,
+                                         const uint16_t*, const uint16_t*, void*, int64_t, void*,
                                          hipStream_t);
 template hipError_t gemm_launch<EPI_DT>(int, int, int, const uint16_t*, int64_t,
-                                        const uint16_t*, const uint16_t*, void*, int64_t,
+                                        const uint16_t*, const uint16_t*, void*, int64_t, void*,
                                         hipStream_t);
 template hipError_t gemm_launch<EPI_SWIGLU>(int, int, int, const uint16_t*, int64_t,
                                             const uint16_t*, const uint16_t*, void*, int64_t,
-                                            hipStream_t);
+                                            void*, hipStream_t);
 
 }  // namespace tpk

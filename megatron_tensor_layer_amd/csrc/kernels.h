@@ -33,10 +33,15 @@ hipError_t splitk_launch(int I, int K, int N, const uint16_t* X, const uint16_t*
                          const uint16_t* W1, void* out, int64_t ldo, void* workspace,
                          hipStream_t stream);
 
-// Same product on bf16 MFMA for any M.
+// Same product on bf16 MFMA for any M (128 x 128 tiles).  When the tiles
+// cannot fill the chip, K is split over workgroups and `workspace`
+// (gemm_workspace_bytes, 0 when not split) holds the arrival counters and
+// the fp32 partial tiles, contents on entry ignored.
+size_t gemm_workspace_bytes(int M, int N, int K, bool swiglu);
 template <int EPI>
 hipError_t gemm_launch(int M, int N, int K, const uint16_t* A, int64_t lda, const uint16_t* W0,
-                       const uint16_t* W1, void* out, int64_t ldo, hipStream_t stream);
+                       const uint16_t* W1, void* out, int64_t ldo, void* workspace,
+                       hipStream_t stream);
 
 hipError_t reduce_launch(int t, int64_t n, const float* P, bool out_bf16, void* Y,
                          hipStream_t stream);

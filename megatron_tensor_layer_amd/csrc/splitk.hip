@@ -204,22 +204,22 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   const int ncols = min(cols, N - cbase);
   const int cq = (ncols + 3) / 4;
   const int rs0 = rb * NW * 16;                             // block's first row-space column
-  auto sum_splits = [&](int64_t q) {  // q: element offset of split 0
+  // Sum of the ns split planes at element offset q (split 0), in split order.
+  // Eight loads are in flight per batch; offsets of splits past ns are out of
+  // range and read zero (x + 0 == x), so the batch needs no branch.
+  auto sum_splits = [&](int64_t q) {
     f32x4_t s4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    int r = 0;
-    for (; r + 4 <= ns; r += 4) {
-      f32x4_t v[4];
+    for (int r = 0; r < ns; r += 8) {
+      f32x4_t v[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < 8; ++e)
         v[e] = __builtin_bit_cast(
             f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                         pr, (uint32_t)((q + (r + e) * plane) * 4), 0, kAuxSys));
+                         pr, r + e < ns ? (uint32_t)((q + (r + e) * plane) * 4) : kOob, 0,
+                         kAuxSys));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s4 += v[e];
+      for (int e = 0; e < 8; ++e) s4 += v[e];
     }
-    for (; r < ns; ++r)
-      s4 += __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                            pr, (uint32_t)((q + r * plane) * 4), 0, kAuxSys));
     return s4;
   };
   for (int idx = tid; idx < I * cq; idx += NW * 64) {

@@ -4,7 +4,8 @@
 // kernel family by the token count and enqueues it on the caller's stream.
 //   bf16, I <= 8   few-token streaming kernel (VALU dot2), weights read once
 //   bf16, I <= 64  split-K weight streaming on MFMA, workspace for partials
-//   bf16, I > 64   MFMA tiled kernel (LDS double-buffered)
+//   bf16, I > 64   MFMA tiled kernel (4-stage LDS pipeline, K split when
+//                  the tiles cannot fill the chip)
 //   fp32           few-token streaming kernel, 8 tokens per launch
 #include <hip/hip_runtime.h>
 
@@ -47,10 +48,15 @@ Path bf16_path(int64_t I, int64_t K) {
   return Path::Gemm;
 }
 
-// Workspace of one projection (0 unless it takes the split-K path).
+// Workspace of one projection (split-K partial sums; 0 when not split).
 size_t proj_workspace(int64_t I, int64_t K, int64_t N, bool swiglu, tp_dtype_t dt) {
-  if (dt != TP_BF16 || I < 1 || bf16_path(I, K) != Path::SplitK) return 0;
-  return tpk::splitk_workspace_bytes((int)I, (int)K, (int)N, swiglu);
+  if (dt != TP_BF16 || I < 1) return 0;
+  switch (bf16_path(I, K)) {
+    case Path::Gemv: return 0;
+    case Path::SplitK: return tpk::splitk_workspace_bytes((int)I, (int)K, (int)N, swiglu);
+    case Path::Gemm: return tpk::gemm_workspace_bytes((int)I, (int)N, (int)K, swiglu);
+  }
+  return 0;
 }
 
 // One projection out[I, N] = in[I, K] . W[N, K]^T with epilogue EPI.
@@ -71,7 +77,7 @@ hipError_t project(int64_t I, int64_t K, int64_t N, tp_dtype_t dt, const void* i
       case Path::SplitK:
         return tpk::splitk_launch<EPI>((int)I, (int)K, (int)N, X, A0, A1, out, N, ws, s);
       case Path::Gemm:
-        return gemm_launch<EPI>((int)I, (int)N, (int)K, X, K, A0, A1, out, N, s);
+        return gemm_launch<EPI>((int)I, (int)N, (int)K, X, K, A0, A1, out, N, ws, s);
     }
   }
   auto X = static_cast<const float*>(in);
