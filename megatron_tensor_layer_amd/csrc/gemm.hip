@@ -11,7 +11,9 @@
 //     every stage and are summed through LDS at the end;
 //   * both operands are K-contiguous (activations row-major, weights
 //     output-major) and are copied global -> LDS by the buffer unit directly
-//     (no register staging), 64 K per stage, 4 stages in flight; in LDS a
+//     (no register staging), 64 K per stage, 5 stages (all 160 KB of LDS),
+//     4 in flight -- at these shapes the copies wait on HBM misses, so the
+//     bytes in flight set the speed; in LDS a
 //     tile row is 128 bytes and its 16-byte chunk c sits in slot
 //     c ^ ((row / 2) % 8), so the 32 rows one MFMA operand read touches
 //     cover all 64 banks once;
@@ -37,16 +39,17 @@ namespace tpk {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64, S = 4;
+constexpr int BM = 128, BN = 128, BK = 64, S = 5;
 constexpr int kThreads = 512;
 constexpr int kRowB = BK * 2;                  // bytes per LDS tile row
 constexpr int kStageA = BM * kRowB;            // 16 KB
 constexpr int kStage = (BM + BN) * kRowB;      // 32 KB
-constexpr int kLds = S * kStage;               // 128 KB
+constexpr int kLds = S * kStage;               // 160 KB: all of a CU's LDS
 constexpr uint32_t kOob = 0x80000000u;         // buffer offset past any record: reads zero
 constexpr int kAuxSys = 17;                    // sc0 sc1: system coherent
 constexpr int kCUs = 256;
 static_assert(4 * 16 * 64 * 4 <= kStageA, "a wave pair's K-group reduction fits one stage buffer");
+static_assert(4 * kStageA + 4 <= kLds, "the arrival flag follows the reduction area");
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -122,12 +125,9 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
             const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
             void* __restrict__ out, int64_t ldo, int KR, unsigned long long* __restrict__ counters,
             float* __restrict__ part, unsigned call_id) {
-  // one array per stage and operand: the loads into a stage and the reads
-  // of another are then visibly disjoint, so the compiler's own wait before
-  // an LDS read covers only the stage being read
-  __shared__ __attribute__((aligned(16))) unsigned char sa0[kStageA], sa1[kStageA], sa2[kStageA],
-      sa3[kStageA], sb0[kStageA], sb1[kStageA], sb2[kStageA], sb3[kStageA];
-  __shared__ int is_last;
+  // S stages of (A tile, W tile); after the K loop the same memory holds
+  // the K-group reduction and the split-K arrival flag
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar registers
   const int g = wave >> 2;              // K group
@@ -162,8 +162,9 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
   // instructions w and w + 8.  Past the K range (or past M / N) the offset
   // is out of range and the slot is zero-filled.
   const int rr = lane >> 3, sl = lane & 7;
-  auto issue = [&](int st, const unsigned char* sa, const unsigned char* sb) {
-    const uint32_t la = lds_addr(sa), lb = lds_addr(sb);  // constants: static arrays
+  const uint32_t lsm = lds_addr(smem);
+  auto issue = [&](int st, int buf) {
+    const uint32_t la = lsm + buf * kStage, lb = la + kStageA;
     const int k0 = kb + st * BK;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -205,17 +206,15 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int NT = (ke - kb + BK - 1) / BK;
-  issue(0, sa0, sb0);
-  issue(1, sa1, sb1);
-  issue(2, sa2, sb2);
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) issue(st, st);
 
-  // K step kt reads buffers (sa, sb) and refills (na, nb) -- the buffers of
-  // step kt - 1 -- with stage kt + 3
-  auto step = [&](int kt, const unsigned char* sa, const unsigned char* sb, unsigned char* na,
-                  unsigned char* nb) {
+  for (int kt = 0; kt < NT; ++kt) {
     wait_vmcnt<(S - 2) * 4>();  // this wave's part of stage kt has landed
     __syncthreads();            // everyone's has; stage kt - 1 is consumed
-    issue(kt + S - 1, na, nb);
+    issue(kt + S - 1, (kt + S - 1) % S);
+    const unsigned char* sa = smem + (kt % S) * kStage;
+    const unsigned char* sb = sa + kStageA;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int c = (2 * g + h) * 2 + (lane >> 5);  // 16-wide K step 2g + h
@@ -232,19 +231,13 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bw[j], acc[i][j], 0, 0, 0);
     }
-  };
-  for (int kt = 0; kt < NT; kt += S) {
-    step(kt, sa0, sb0, sa3, sb3);
-    if (kt + 1 < NT) step(kt + 1, sa1, sb1, sa0, sb0);
-    if (kt + 2 < NT) step(kt + 2, sa2, sb2, sa1, sb1);
-    if (kt + 3 < NT) step(kt + 3, sa3, sb3, sa2, sb2);
   }
 
   // ---- sum the two K groups through LDS (lane-linear, conflict-free)
   wait_vmcnt<0>();  // zero-fill loads of stages past the end have landed
   __syncthreads();
   const int pair = wave & 3;  // waves pair and pair + 4 hold the same tile
-  float* red = reinterpret_cast<float*>(pair == 0 ? sa0 : pair == 1 ? sa1 : pair == 2 ? sa2 : sa3);
+  float* red = reinterpret_cast<float*>(smem + pair * kStageA);
   if (g == 1) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -314,11 +307,12 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
         }
       }
   }
+  int* is_last = reinterpret_cast<int*>(smem + 4 * kStageA);  // past the reduction area
   wait_vmcnt<0>();  // partial stores have reached memory
   __syncthreads();
-  if (tid == 0) is_last = arrive(counters + tile, call_id) == (unsigned)ns;
+  if (tid == 0) *is_last = arrive(counters + tile, call_id) == (unsigned)ns;
   __syncthreads();
-  if (!is_last) return;
+  if (!*is_last) return;
 
   // Sum of the ns split tiles at element offset q (split 0), in split order;
   // eight loads in flight, offsets past the last split read zero.

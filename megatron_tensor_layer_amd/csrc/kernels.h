@@ -28,6 +28,9 @@ hipError_t gemv_launch(int I, int K, int N, const T* X, int64_t ldx, const T* W0
 constexpr int kSplitKMaxTokens = 64;
 constexpr int64_t kSplitKMaxK = int64_t(1) << 23;
 size_t splitk_workspace_bytes(int I, int K, int N, bool swiglu);
+// Whether the split-K kernel is the better choice for this projection: it is
+// unless the activations of a full K range do not fit LDS (many tokens, long K).
+bool splitk_suits(int I, int K, int N, bool swiglu);
 template <int EPI>
 hipError_t splitk_launch(int I, int K, int N, const uint16_t* X, const uint16_t* W0,
                          const uint16_t* W1, void* out, int64_t ldo, void* workspace,

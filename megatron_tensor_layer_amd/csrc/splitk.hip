@@ -280,36 +280,34 @@ Plan plan_for(int I, int K, int N, bool swiglu, int nw, int ns_req) {
   return pl;
 }
 
-// Choose waves per workgroup (nw) and the K split (ns).  Measured on MI355X
-// (one rank's decode projections of the Llama-3.1-70B and Qwen2.5-1.5B shapes):
-// the best grids hold about 200-256 workgroups -- one per CU, none waiting --
-// with 4..16 waves each; every extra split adds an fp32 partial round trip.
+// Choose the K split (ns) and waves per workgroup (nw).  Measured on MI355X
+// over the decode projections of the Llama-3.1-70B and Qwen2.5-1.5B rank
+// shares (9..64 tokens): the best plans give each workgroup about a third of
+// K, clamped to 256..1408 elements (long ranges make few, slow-to-start
+// workgroups; short ones multiply the partial sums), then use the fewest
+// waves per workgroup -- at least 4 -- that keep the grid within one
+// workgroup per CU.  When the activations of the K range do not fit LDS the
+// range shrinks.
+int target_groups(int K) {  // K groups per split the rule aims for
+  const int groups = (K + kGK - 1) / kGK;
+  return std::min(std::min(std::max((K / 3 + kGK / 2) / kGK, 2), 11), groups);
+}
+
 Plan make_plan(int I, int K, int N, bool swiglu) {
   const int groups = (K + kGK - 1) / kGK;
-  const double wbytes = 2.0 * (swiglu ? 2.0 : 1.0) * N * K;
-  Plan best;
-  double best_score = 1e30;
-  for (int nw = 16; nw >= 2; --nw) {
-    if (swiglu && (nw % 2)) continue;
-    for (int s = 1; s <= groups; ++s) {
-      const Plan pl = plan_for(I, K, N, swiglu, nw, s);
-      if (pl.ns != s || pl.lds > kLdsMax) continue;
-      if ((double)pl.ns * I * pl.nr * 4.0 >= 2147483648.0) continue;
-      const int wgs = pl.grid;
-      const double per_cu_max = std::ceil((double)wgs / kCUs);
-      const double imbalance = per_cu_max * kCUs / (double)wgs;
-      const double underfill = wgs < kCUs ? std::pow((double)kCUs / wgs, 0.6) : 1.0;
-      const double partial = 2.0 * pl.ns * I * pl.nr * 4.0 / wbytes;
-      const double waves = std::min(per_cu_max, 1.0) * nw;
-      const double few = waves < 4 ? (4.0 - waves) / 4.0 : 0.0;
-      const double score = std::max(imbalance, underfill) * (1.0 + partial) * (1.0 + few);
-      if (score < best_score - 1e-9) {
-        best_score = score;
-        best = pl;
-      }
-    }
+  const int tiles = swiglu ? (N + 7) / 8 : (N + 15) / 16;  // 16-row weight tiles
+  int gps = target_groups(K);
+  for (;;) {
+    const int ns = (groups + gps - 1) / gps;
+    const int per_split = std::max(1, kCUs / ns);  // row blocks that fit beside the splits
+    int nw = std::max(4, (tiles + per_split - 1) / per_split);
+    if (swiglu) nw += nw & 1;
+    nw = std::min(nw, 16);
+    Plan pl = plan_for(I, K, N, swiglu, nw, ns);
+    const bool fits = pl.lds <= kLdsMax && (double)pl.ns * I * pl.nr * 4.0 < 2147483648.0;
+    if (fits || gps == 1) return fits ? pl : Plan{};
+    --gps;
   }
-  return best;
 }
 
 // Call ids name one launch in the arrival counters; one sequence for every
@@ -343,6 +341,14 @@ hipError_t launch_plan(const Plan& pl, int I, int K, int N, const uint16_t* X,
 }
 
 }  // namespace
+
+bool splitk_suits(int I, int K, int N, bool swiglu) {
+  if (I < 1 || I > kSplitKMaxTokens || K > kSplitKMaxK) return false;
+  const Plan pl = make_plan(I, K, N, swiglu);
+  if (pl.grid == 0) return false;
+  // K range cut below half the target by LDS: the tiled kernel does better
+  return 2 * (pl.kr / kGK) >= target_groups(K);
+}
 
 size_t splitk_workspace_bytes(int I, int K, int N, bool swiglu) {
   return plan_bytes(make_plan(I, K, N, swiglu), I);
