@@ -58,6 +58,12 @@ def parse():
     ap.add_argument("--no-detail", action="store_true", help="skip the per-config breakdown")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--calls", type=int, default=200, help="timed calls per detail config")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="for rocprofv3 --pmc: one calibration copy of COPY_MIB MiB, then one "
+                         "tp_shard_mlp call per rank at the bench batch; no timing")
+    ap.add_argument("--ingest-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn the counter_collection.csv files of the FETCH_SIZE and "
+                         "WRITE_SIZE passes over --traffic-probe into profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -95,11 +101,81 @@ def stats(us):
                 p90_us=round(q(0.9), 2))
 
 
-def src_hash(files):
+def src_hash(files=None):
+    """Hash of the kernel sources (all of csrc by default): stored counter
+    figures are used only while the kernels they were taken on are unchanged."""
+    if files is None:
+        files = sorted(str(p.relative_to(ROOT)) for p in
+                       (ROOT / "megatron_tensor_layer_amd" / "csrc").iterdir() if p.is_file())
     h = hashlib.sha256()
     for f in files:
         h.update((ROOT / f).read_bytes())
     return h.hexdigest()[:16]
+
+
+COPY_MIB = 512  # calibration copy: reads and writes COPY_MIB MiB of fp32
+
+
+def traffic_probe(torch, tp, layer, I):
+    """Launch sequence read back by --ingest-traffic: a plain copy of known
+    size (torch's elementwise multiply by 1), then tp_shard_mlp once per rank."""
+    n = COPY_MIB * 2**20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    X = to_dev(torch, datagen.gaussian("X", (I, D), 1.0, "bf16", 42))
+    B = layer.buffers(I)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    for R in layer.ranks:
+        tp.shard_mlp(X, *R["mlp"], B["H"], B["pm"][0])
+    torch.cuda.synchronize()
+    log(f"traffic probe: copy of {COPY_MIB} MiB, then {len(layer.ranks)} tp_shard_mlp calls at I={I}")
+
+
+def ingest_traffic(fetch_csv, write_csv, I):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one tp_shard_mlp call,
+    each scaled by what the counter reads for the calibration copy."""
+    import csv
+
+    def read(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        copy = [r for r in rows if "MulFunctor" in r["Kernel_Name"]]
+        if len(copy) != 1:
+            raise SystemExit(f"{path}: expected one calibration copy dispatch, found {len(copy)}")
+        after = [r for r in rows if int(r["Dispatch_Id"]) > int(copy[0]["Dispatch_Id"])
+                 and "tpk::" in r["Kernel_Name"]]
+        per_kernel = {}
+        for r in after:
+            per_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return float(copy[0]["Counter_Value"]), per_kernel
+
+    true_bytes = COPY_MIB * 2**20
+    cf, kf = read(fetch_csv, "FETCH_SIZE")
+    cw, kw = read(write_csv, "WRITE_SIZE")
+    f_fetch, f_write = true_bytes / (cf * 1024), true_bytes / (cw * 1024)
+    calls = len(next(iter(kf.values())))
+    fetch = sum(sum(v) for v in kf.values()) * 1024 * f_fetch / calls
+    write = sum(sum(v) for v in kw.values()) * 1024 * f_write / calls
+    key = f"mlp_I{I}"
+    tf = ROOT / "profiles" / "traffic.json"
+    tr = json.loads(tf.read_text()) if tf.exists() else {}
+    tr[key] = dict(
+        bytes_per_call=round(fetch + write), fetch_bytes_per_call=round(fetch),
+        write_bytes_per_call=round(write), calls=calls,
+        copy_calibration=dict(bytes_read=true_bytes, bytes_written=true_bytes,
+                              fetch_size_kib=cf, write_size_kib=cw,
+                              fetch_factor=round(f_fetch, 4), write_factor=round(f_write, 4)),
+        kernels_kib_per_dispatch={k: dict(fetch=round(sum(kf[k]) / len(kf[k]), 1),
+                                          write=round(sum(kw.get(k, [0])) / max(1, len(kw.get(k, [0]))), 1))
+                                  for k in kf},
+        src_hash=src_hash(),
+        command="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
+                f"python3 bench.py --traffic-probe --batch {I}")
+    tf.write_text(json.dumps(tr, indent=1) + "\n")
+    log(f"{key}: {fetch / 1e6:.1f} MB fetched + {write / 1e6:.1f} MB written per call "
+        f"(copy factors {f_fetch:.3f} / {f_write:.3f})")
 
 
 # ------------------------------------------------------------------ the layer
@@ -305,14 +381,21 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    I, S = args.batch, 1
+    if args.ingest_traffic:
+        ingest_traffic(*args.ingest_traffic, I)
+        return
+
     import torch
     import megatron_tensor_layer_amd as tp
 
     torch.cuda.set_device(0)
     tp.lib()
-    I, S = args.batch, 1
     layer = Layer(torch, tp)
     log("8 rank shares of the layer resident in HBM")
+    if args.traffic_probe:
+        traffic_probe(torch, tp, layer, I)
+        return
     Xh = datagen.gaussian("X", (I, D), 1.0, "bf16", 42)
     X = to_dev(torch, Xh)
     B = layer.buffers(I)
@@ -346,8 +429,7 @@ def main():
     if tf.exists():
         tr = json.loads(tf.read_text())
         key = f"mlp_I{I}"
-        srcs = ["megatron_tensor_layer_amd/csrc/gemv.hip", "megatron_tensor_layer_amd/csrc/gemm.hip"]
-        if key in tr and tr[key].get("src_hash") == src_hash(srcs):
+        if key in tr and tr[key].get("src_hash") == src_hash():
             roof["traffic"] = tr[key]["bytes_per_call"]
 
     line = dict(

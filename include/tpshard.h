@@ -63,7 +63,7 @@ const char* tp_status_string(tp_status_t s);
 
 /*
  * Device workspace, in bytes, that tp_shard_mlp needs for these sizes
- * (0 if none: few-token and many-token calls need none).  Host-only; never
+ * (0 if none: calls that do not split K over workgroups need none).  Host-only; never
  * touches the GPU.  Returns 0 for invalid sizes (the call itself then reports
  * the error).
  */
@@ -91,9 +91,14 @@ size_t tp_shard_mlp_workspace_size(int64_t I, int64_t D, int64_t F_local, tp_dty
  *   workspace, workspace_bytes: device scratch of at least
  *           tp_shard_mlp_workspace_size(...) bytes, 16-byte aligned, not
  *           overlapping any other argument (may be NULL when the size is 0).
- *           9..64-token bf16 calls keep split-K fp32 partial sums there;
- *           contents on entry are ignored, on return undefined.  Two calls
- *           in flight at once (other streams) need separate workspaces.
+ *           bf16 calls that split K over workgroups (9..256 tokens, by
+ *           shape) keep arrival counters and fp32 partial sums there.  The
+ *           first 8 KiB (the counters) must be zero before the workspace's
+ *           first use (one hipMemset after allocating it); every completed
+ *           call leaves them zero again, so one workspace serves any sequence
+ *           of calls on one stream.  The rest is scratch: contents on entry
+ *           ignored, on return undefined.  Two calls in flight at once
+ *           (other streams) need separate workspaces.
  * Errors: TP_ERR_INVALID, TP_ERR_MISALIGNED (D or F_local not a multiple of 8,
  * a pointer not 16-byte aligned), TP_ERR_WORKSPACE, TP_ERR_LAUNCH.
  */

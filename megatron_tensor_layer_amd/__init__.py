@@ -119,8 +119,10 @@ def attn_workspace_bytes(phase: int, I: int, D: int, n_q_local: int, n_kv_local:
 
 
 # One scratch buffer per device, grown on demand, used when a caller passes no
-# workspace.  Calls that may run concurrently on different streams of one
-# device must pass their own workspace instead.
+# workspace.  It is allocated zero-filled: its leading counter area must be
+# zero before first use, and every completed call leaves it zero.  Calls that
+# may run concurrently on different streams of one device must pass their own
+# workspace instead (zero-filled the same way).
 _ws_cache: dict = {}
 
 

@@ -50,6 +50,14 @@ __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
 }
 
+// Split-K arrival at a tile's counter: true for the last of `ns` arrivals.
+// atomicInc wraps the counter to zero on that arrival, so a finished call
+// leaves every counter zero and the next call needs no reset (one atomic
+// round trip per workgroup, no compare-and-swap retries under contention).
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned ns) {
+  return atomicInc(counter, ns - 1) == ns - 1;
+}
+
 // silu(z) = z / (1 + exp(-z)), fp32.
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 

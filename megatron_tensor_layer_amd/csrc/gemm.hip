@@ -26,12 +26,10 @@
 //     partial tile, and the last of a tile's workgroups to arrive sums the
 //     partials in split order (deterministic) and applies the epilogue.
 //     Partials cross XCDs, whose L2s are not coherent, so they are written
-//     and read system-coherent; the arrival counter is a device atomic;
+//     and read system-coherent; the arrival counter is one device atomic;
 //   * workgroups go round-robin to the 8 XCDs; the block id is remapped so
 //     that each XCD runs a contiguous range of tiles, and tiles sharing a W
 //     block (same N block, other M blocks) are neighbours in that range.
-#include <atomic>
-
 #include "common.h"
 #include "kernels.h"
 
@@ -94,20 +92,6 @@ __device__ __forceinline__ int acc_row32(int r, int lane) {
   return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
 }
 
-// Arrival at a tile's counter word (call_id << 32 | arrivals); a word from
-// another call restarts the count, so the workspace needs no reset.
-__device__ __forceinline__ unsigned arrive(unsigned long long* word, unsigned call_id) {
-  unsigned long long expect = 0;
-  for (;;) {
-    const unsigned long long want = ((expect >> 32) == call_id)
-                                        ? expect + 1
-                                        : (((unsigned long long)call_id << 32) | 1ull);
-    const unsigned long long seen = atomicCAS(word, expect, want);
-    if (seen == expect) return (unsigned)(want & 0xffffffffull);
-    expect = seen;
-  }
-}
-
 template <int EPI>
 __device__ __forceinline__ void store_out(void* out, int64_t ldo, int m, int col, float v) {
   if constexpr (EPI == EPI_F32)
@@ -123,8 +107,8 @@ template <int EPI>
 __global__ void __launch_bounds__(kThreads)
 gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
             const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-            void* __restrict__ out, int64_t ldo, int KR, unsigned long long* __restrict__ counters,
-            float* __restrict__ part, unsigned call_id) {
+            void* __restrict__ out, int64_t ldo, int KR, unsigned* __restrict__ counters,
+            float* __restrict__ part) {
   // S stages of (A tile, W tile); after the K loop the same memory holds
   // the K-group reduction and the split-K arrival flag
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
@@ -310,7 +294,7 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
   int* is_last = reinterpret_cast<int*>(smem + 4 * kStageA);  // past the reduction area
   wait_vmcnt<0>();  // partial stores have reached memory
   __syncthreads();
-  if (tid == 0) *is_last = arrive(counters + tile, call_id) == (unsigned)ns;
+  if (tid == 0) *is_last = arrive_last(counters + tile, (unsigned)ns);
   __syncthreads();
   if (!*is_last) return;
 
@@ -357,8 +341,6 @@ struct Plan {
   int grid = 0;
 };
 
-constexpr size_t kCounterAlign = 256;
-
 // Split K when the tiles alone leave CUs idle: pick the split count that
 // minimises the busiest CU's share of work (in whole tiles), charging each
 // extra split a little for its partial round trip; at least 8 stages of K
@@ -372,7 +354,9 @@ Plan make_plan(int M, int N, int K, bool swiglu) {
   int best_ns = 1;
   double best = 1e30;
   for (int ns = 1; ns <= max_ns; ++ns) {
-    if (ns > 1 && (double)ns * pl.tiles * BM * BN * 4.0 >= 2147483648.0) break;
+    if (ns > 1 && ((double)ns * pl.tiles * BM * BN * 4.0 >= 2147483648.0 ||
+                   pl.tiles > kWsMaxCounters))
+      break;
     const double busiest = std::ceil((double)pl.tiles * ns / kCUs) / ns;
     const double cost = busiest * (1.0 + 0.04 * (ns - 1));
     if (cost < best - 1e-9) {
@@ -389,15 +373,7 @@ Plan make_plan(int M, int N, int K, bool swiglu) {
 
 size_t plan_bytes(const Plan& pl) {
   if (pl.ns <= 1) return 0;
-  const size_t cnt = ((size_t)pl.tiles * 8 + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
-  return cnt + (size_t)pl.ns * pl.tiles * BM * BN * sizeof(float);
-}
-
-unsigned next_call_id() {
-  static std::atomic<unsigned> next{0};
-  unsigned id = ++next;
-  if (id == 0) id = ++next;
-  return id;
+  return kWsCounterBytes + (size_t)pl.ns * pl.tiles * BM * BN * sizeof(float);
 }
 
 template <int EPI>
@@ -405,19 +381,15 @@ hipError_t launch_plan(const Plan& pl, int M, int N, int K, const uint16_t* A, i
                        const uint16_t* W0, const uint16_t* W1, void* out, int64_t ldo,
                        void* workspace, hipStream_t stream) {
   auto kern = gemm_kernel<EPI>;
-  unsigned long long* counters = nullptr;
+  unsigned* counters = nullptr;
   float* part = nullptr;
-  unsigned id = 0;
   if (pl.ns > 1) {
-    if (workspace == nullptr) return hipErrorInvalidValue;
-    id = next_call_id();
-    counters = static_cast<unsigned long long*>(workspace);
-    const size_t cnt =
-        ((size_t)pl.tiles * 8 + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
-    part = reinterpret_cast<float*>(static_cast<char*>(workspace) + cnt);
+    if (workspace == nullptr || pl.tiles > kWsMaxCounters) return hipErrorInvalidValue;
+    counters = static_cast<unsigned*>(workspace);
+    part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsCounterBytes);
   }
   hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(kThreads), 0, stream, M, N, K, A, lda, W0,
-                     W1, out, ldo, pl.kr, counters, part, id);
+                     W1, out, ldo, pl.kr, counters, part);
   return hipGetLastError();
 }
 

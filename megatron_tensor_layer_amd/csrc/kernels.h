@@ -10,6 +10,13 @@
 
 namespace tpk {
 
+// Split-K workspace layout shared by every kernel that splits K: a fixed
+// area of 32-bit arrival counters (zero before the first use; each completed
+// call leaves it zero), then the fp32 partial sums.  The fixed size lets
+// calls of any shape share one workspace.
+constexpr size_t kWsCounterBytes = 8192;
+constexpr int kWsMaxCounters = int(kWsCounterBytes / 4);
+
 // Largest contraction length (elements) the few-token kernel handles:
 // 8 chunks of 16 bytes per lane, 512 lanes.
 constexpr int64_t kGemvMaxK16 = 8 * 512 * 8;   // bf16
@@ -24,7 +31,7 @@ hipError_t gemv_launch(int I, int K, int N, const T* X, int64_t ldx, const T* W0
 
 // Same product on bf16 MFMA for 9..64 tokens, weights streamed once from HBM,
 // K split over workgroups; `workspace` (splitk_workspace_bytes) holds the
-// arrival counters and the fp32 partial sums, contents on entry ignored.
+// arrival counters and the fp32 partial sums (layout above).
 constexpr int kSplitKMaxTokens = 64;
 constexpr int64_t kSplitKMaxK = int64_t(1) << 23;
 size_t splitk_workspace_bytes(int I, int K, int N, bool swiglu);
@@ -39,7 +46,7 @@ hipError_t splitk_launch(int I, int K, int N, const uint16_t* X, const uint16_t*
 // Same product on bf16 MFMA for any M (128 x 128 tiles).  When the tiles
 // cannot fill the chip, K is split over workgroups and `workspace`
 // (gemm_workspace_bytes, 0 when not split) holds the arrival counters and
-// the fp32 partial tiles, contents on entry ignored.
+// the fp32 partial tiles (layout above).
 size_t gemm_workspace_bytes(int M, int N, int K, bool swiglu);
 template <int EPI>
 hipError_t gemm_launch(int M, int N, int K, const uint16_t* A, int64_t lda, const uint16_t* W0,

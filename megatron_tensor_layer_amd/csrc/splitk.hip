@@ -19,14 +19,12 @@
 //   * no barrier after the start: waves run independently;
 //   * each workgroup writes fp32 partial sums part[split][m][row]; the last
 //     of a row block's NS workgroups to arrive (an arrival counter in the
-//     workspace) adds the NS partials in split order -- deterministic,
+//     workspace, one atomic each) adds the NS partials in split order -- deterministic,
 //     whichever arrives last -- and applies the epilogue: fp32 store, bf16
 //     store, or silu(gate) * up (lecture §4.1: the SwiGLU elementwise op is
 //     local to the rank).  A SwiGLU row block holds the gate tiles and the up
 //     tiles of the same F block, so the epilogue has both;
 //   * one kernel launch per projection: no separate reduction pass.
-#include <atomic>
-
 #include "common.h"
 #include "kernels.h"
 
@@ -47,22 +45,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-// Arrival at a row block's counter word (call_id << 32 | arrivals).  A word
-// from another call (or garbage) restarts the count at 1, so the workspace
-// needs no reset between calls.  Returns the arrivals including this one.
-// Each failed CAS means another arrival succeeded, so the loop is bounded.
-__device__ __forceinline__ unsigned arrive(unsigned long long* word, unsigned call_id) {
-  unsigned long long expect = 0;
-  for (;;) {
-    const unsigned long long want = ((expect >> 32) == call_id)
-                                        ? expect + 1
-                                        : (((unsigned long long)call_id << 32) | 1ull);
-    const unsigned long long seen = atomicCAS(word, expect, want);
-    if (seen == expect) return (unsigned)(want & 0xffffffffull);
-    expect = seen;
-  }
-}
-
 // Row space of the partial sums: row block rb holds NW 16-row tiles.  Single
 // matrix (N rows): block rb covers rows [16 NW rb, 16 NW (rb + 1)).  SwiGLU
 // (gate W0 and up W1, N rows each): block rb covers F rows f0 = 8 NW rb ..
@@ -71,8 +53,8 @@ template <int MT, int P, int EPI>
 __global__ void __launch_bounds__(1024)
 splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
               const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int KR,
-              unsigned long long* __restrict__ counters, float* __restrict__ part, int NR,
-              void* __restrict__ out, int64_t ldo, unsigned call_id) {
+              unsigned* __restrict__ counters, float* __restrict__ part, int NR,
+              void* __restrict__ out, int64_t ldo) {
   constexpr int TOK = 16 * MT;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   __shared__ int is_last;
@@ -195,7 +177,7 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   // ---- the last of the block's ns workgroups reduces and stores the block
   wait_vmcnt<0>();  // this wave's partial stores have reached memory
   __syncthreads();
-  if (tid == 0) is_last = arrive(counters + rb, call_id) == (unsigned)ns;
+  if (tid == 0) is_last = arrive_last(counters + rb, (unsigned)ns);
   __syncthreads();
   if (!is_last) return;
 
@@ -258,11 +240,8 @@ struct Plan {
   int grid = 0;
 };
 
-constexpr size_t kCounterAlign = 256;
-
 size_t plan_bytes(const Plan& pl, int I) {
-  const size_t cnt = ((size_t)pl.rbs * 8 + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
-  return cnt + (size_t)pl.ns * (size_t)I * (size_t)pl.nr * sizeof(float);
+  return kWsCounterBytes + (size_t)pl.ns * (size_t)I * (size_t)pl.nr * sizeof(float);
 }
 
 Plan plan_for(int I, int K, int N, bool swiglu, int nw, int ns_req) {
@@ -282,21 +261,28 @@ Plan plan_for(int I, int K, int N, bool swiglu, int nw, int ns_req) {
 
 // Choose the K split (ns) and waves per workgroup (nw).  Measured on MI355X
 // over the decode projections of the Llama-3.1-70B and Qwen2.5-1.5B rank
-// shares (9..64 tokens): the best plans give each workgroup about a third of
-// K, clamped to 256..1408 elements (long ranges make few, slow-to-start
-// workgroups; short ones multiply the partial sums), then use the fewest
-// waves per workgroup -- at least 4 -- that keep the grid within one
-// workgroup per CU.  When the activations of the K range do not fit LDS the
-// range shrinks.
-int target_groups(int K) {  // K groups per split the rule aims for
+// shares (9..64 tokens): with 4 waves per workgroup, split K until the grid
+// nears one workgroup per CU, keeping 256..1408 K elements per split (short
+// ranges multiply the partial sums, long ones make slow-starting
+// workgroups); then use the fewest waves (at least 4) that keep the grid
+// within one workgroup per CU.  When the activations of the K range do not
+// fit LDS the range shrinks.
+int target_groups(int K, int tiles) {  // K groups per split the rule aims for
   const int groups = (K + kGK - 1) / kGK;
-  return std::min(std::min(std::max((K / 3 + kGK / 2) / kGK, 2), 11), groups);
+  const int rbs4 = (tiles + 3) / 4;  // row blocks at 4 waves
+  const int ns = std::max(1, kCUs / rbs4);
+  const int gps = (groups + ns - 1) / ns;
+  return std::min(std::min(std::max(gps, 2), 11), groups);
+}
+
+int weight_tiles(int N, bool swiglu) {  // 16-row weight tiles
+  return swiglu ? (N + 7) / 8 : (N + 15) / 16;
 }
 
 Plan make_plan(int I, int K, int N, bool swiglu) {
   const int groups = (K + kGK - 1) / kGK;
-  const int tiles = swiglu ? (N + 7) / 8 : (N + 15) / 16;  // 16-row weight tiles
-  int gps = target_groups(K);
+  const int tiles = weight_tiles(N, swiglu);
+  int gps = target_groups(K, tiles);
   for (;;) {
     const int ns = (groups + gps - 1) / gps;
     const int per_split = std::max(1, kCUs / ns);  // row blocks that fit beside the splits
@@ -308,15 +294,6 @@ Plan make_plan(int I, int K, int N, bool swiglu) {
     if (fits || gps == 1) return fits ? pl : Plan{};
     --gps;
   }
-}
-
-// Call ids name one launch in the arrival counters; one sequence for every
-// kernel variant of the process (0 is never used: a zeroed workspace is fresh).
-unsigned next_call_id() {
-  static std::atomic<unsigned> next{0};
-  unsigned id = ++next;
-  if (id == 0) id = ++next;
-  return id;
 }
 
 template <int MT, int EPI>
@@ -331,12 +308,11 @@ hipError_t launch_plan(const Plan& pl, int I, int K, int N, const uint16_t* X,
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const unsigned id = next_call_id();
-  auto* counters = static_cast<unsigned long long*>(workspace);
-  const size_t cnt = ((size_t)pl.rbs * 8 + kCounterAlign - 1) / kCounterAlign * kCounterAlign;
-  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + cnt);
+  if (pl.rbs > kWsMaxCounters) return hipErrorInvalidValue;
+  auto* counters = static_cast<unsigned*>(workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsCounterBytes);
   hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(pl.nw * 64), pl.lds, stream, I, K, N, X, W0, W1,
-                     pl.kr, counters, part, pl.nr, out, ldo, id);
+                     pl.kr, counters, part, pl.nr, out, ldo);
   return hipGetLastError();
 }
 
@@ -347,7 +323,7 @@ bool splitk_suits(int I, int K, int N, bool swiglu) {
   const Plan pl = make_plan(I, K, N, swiglu);
   if (pl.grid == 0) return false;
   // K range cut below half the target by LDS: the tiled kernel does better
-  return 2 * (pl.kr / kGK) >= target_groups(K);
+  return 2 * (pl.kr / kGK) >= target_groups(K, weight_tiles(N, swiglu));
 }
 
 size_t splitk_workspace_bytes(int I, int K, int N, bool swiglu) {

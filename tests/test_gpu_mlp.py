@@ -224,23 +224,32 @@ def test_mlp_empty_and_errors_touch_nothing():
     assert T.isnan(H).all() and T.isnan(P).all() and T.isnan(Y).all()
 
 
-def test_explicit_workspace_contents_do_not_matter(llama_mlp):
-    """Split-K decode (9..64 tokens) keeps fp32 partials in the workspace: a
-    caller buffer full of NaN gives the same bits as the binding's own."""
+COUNTER_BYTES = 8192  # leading arrival-counter area of a split-K workspace
+
+
+def test_explicit_workspace_scratch_contents_do_not_matter(llama_mlp):
+    """Split-K calls (9..64 tokens on the streaming kernel, 65..256 on the
+    tiled one) keep arrival counters and fp32 partials in the workspace: a
+    caller buffer whose counter area is zero and whose partial area is NaN
+    gives the same bits as the binding's own, twice in a row, and leaves the
+    counter area zero."""
     L = llama_mlp
     T = torch()
-    for I in (9, 32, 64):
+    for I in (9, 32, 64, 128, 256):
         X = to_dev(datagen.gaussian("X", (I, L["D"]), 1.0, "bf16", 77), "bf16")
         need = tp.mlp_workspace_bytes(I, L["D"], L["F"] // L["t"])
-        assert need > 0
+        assert need > COUNTER_BYTES, I
         ws = T.full((need // 4 + 4,), float("nan"), dtype=T.float32, device="cuda")
+        ws[:COUNTER_BYTES // 4].view(T.int32).zero_()
         outs = []
-        for w in (None, ws):
+        for w in (None, ws, ws):
             H = empty((I, L["F"] // L["t"]), "bf16")
             P = empty((I, L["D"]), "f32")
             tp.shard_mlp(X, *L["shards"][5], H, P, workspace=w)
             outs.append((H, P))
         T.cuda.synchronize()
-        assert T.equal(outs[0][0], outs[1][0]) and T.equal(outs[0][1], outs[1][1]), I
+        for o in outs[1:]:
+            assert T.equal(outs[0][0], o[0]) and T.equal(outs[0][1], o[1]), I
+        assert int(ws[:COUNTER_BYTES // 4].view(T.int32).abs().sum()) == 0, I
         with pytest.raises(tp.TPError, match="WORKSPACE"):
             tp.shard_mlp(X, *L["shards"][5], outs[0][0], outs[0][1], workspace=ws[:8])
