@@ -155,7 +155,8 @@ tp_status_t tp_partial_reduce(int32_t t, int64_t n, const float* partials,
  * Tokens form I/S sequences of S consecutive rows.
  *   qkv [I, (n_q_local + 2 n_kv_local) head_dim] bf16, as TP_ATTN_QKV writes it
  *   A   [I, n_q_local head_dim] bf16 out
- * bf16 only; head_dim a multiple of 8 and at most 256; S must divide I.
+ * bf16 only; head_dim a multiple of 8 and at most 256; S must divide I;
+ * qkv at most 2 GiB (TP_ERR_UNSUPPORTED beyond).
  */
 tp_status_t tp_attn_core(int64_t I, int64_t S, int64_t n_q_local, int64_t n_kv_local,
                          int64_t head_dim, const void* qkv, void* A, void* stream);

@@ -1,70 +1,298 @@
 // Attention core of one rank (test support: it joins the QKV projection to
 // o_proj; it is not a projection).  Each rank computes its own heads
-// completely (lecture "Distributed Serving", §4.2).  One wavefront per
-// (token, local head): scores q.k/sqrt(hd) over the causal window of the
-// token's sequence, online softmax in fp32, probability-weighted sum of the
-// values of the head's KV group.  Plain and unoptimised on purpose.
+// completely (lecture "Distributed Serving", §4.2).
+//
+// One workgroup per (block of 32 query rows, local head), its waves taking
+// every NWV-th block of keys and merging their softmax states at the end; on bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16), online softmax in fp32, computed transposed so
+// that every lane owns one query:
+//   * S^T = K Q^T per block of 32 keys: K rows (A operand) and the block's Q
+//     (B operand, kept in registers) are both read as 16-byte chunks along
+//     head_dim, as the QKV projection writes them;
+//   * scale 1/sqrt(hd), causal mask inside each sequence (query i sees keys
+//     s0(i)..i, s0 = the first row of its sequence); the lane holds 16 of its
+//     query's 32 scores and lane ^ 32 the other 16, so the running max and
+//     sum need one exchange each per key block;
+//   * O^T += V^T P^T: P^T comes straight from the score registers (rounded
+//     to bf16) as the B operand; V is staged transposed in LDS, keys in the
+//     accumulator's order, so the A operand is one 16-byte read; the per-query
+//     rescale is lane-local;
+//   * head_dim up to 256 in 32-row tiles of O^T (HDT of them); columns past
+//     head_dim read zero and are not stored;
+//   * the next key block's K and V are loaded while the current one is
+//     processed.
+// Sequences of one token (decode without a cache) take a copy kernel: one
+// key, weight exactly 1, A = V.
 #include "common.h"
 #include "kernels.h"
 
 namespace tpk {
 
-__global__ void __launch_bounds__(64)
+namespace {
+
+constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any record: reads zero
+constexpr int kVStride = 40;            // bf16 per LDS row of V^T (32 keys + pad)
+
+// Row (query within the block) of accumulator element r held by `lane`; the
+// column (key, or output column) is lane % 32.
+__device__ __forceinline__ int acc_row32(int r, int lane) {
+  return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+}
+
+__device__ __forceinline__ float half_wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+__device__ __forceinline__ float half_wave_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+template <int HDT, int NWV>
+__global__ void __launch_bounds__(64 * NWV)
 attn_core_kernel(int I, int S, int nq, int nkv, int hd, const uint16_t* __restrict__ qkv,
                  uint16_t* __restrict__ A) {
-  const int i = blockIdx.x;
-  const int j = blockIdx.y;
-  const int lane = threadIdx.x;
-  const int N = (nq + 2 * nkv) * hd;
-  const int g = (j * nkv) / nq;
-  const int s0 = (i / S) * S;
-  const float scale = 1.0f / sqrtf((float)hd);
-  constexpr int EPL = 4;  // elements per lane, hd <= 256
+  constexpr int KS = 2 * HDT;  // 16-wide steps along head_dim
+  constexpr int kVt = 32 * HDT * kVStride;  // bf16 per wave's V^T tile
+  __shared__ __attribute__((aligned(16))) uint16_t Vts[NWV * kVt];
+  // partial results of waves 1.. for the merge: max and sum, then O^T tiles
+  __shared__ float mls[NWV][2][64];
+  __shared__ float ots[NWV > 1 ? NWV - 1 : 1][HDT][16][64];
 
-  float q[EPL], o[EPL];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // key blocks w, w + NWV, ...
+  uint16_t* Vt = Vts + w * kVt;
+  const int i0 = blockIdx.x * 32;
+  const int j = blockIdx.y;
+  const int g = (j * nkv) / nq;  // KV group of local head j
+  const int N = (nq + 2 * nkv) * hd;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qkv, (uint32_t)I * (uint32_t)N * 2u);
+  const int qcol = j * hd, kcol = (nq + g) * hd, vcol = (nq + nkv + g) * hd;
+  const float scale = 1.0f / sqrtf((float)hd);
+
+  // 16-byte chunk c of row `row` of the head starting at `col0` (zero past
+  // head_dim or past the last row)
+  auto chunk_off = [&](int row, int col0, int c) -> uint32_t {
+    return (c * 8 < hd && row < I) ? ((uint32_t)row * (uint32_t)N + (uint32_t)(col0 + c * 8)) * 2u
+                                   : kOob;
+  };
+
+  // This lane's query (column of every accumulator below) and its sequence start
+  const int qi = i0 + (lane & 31);
+  const int qlo = (qi / S) * S;
+  // Q of the block as the B operand: query lane%32, chunk 2 ks + lane/32
+  bf16x8_t qf[KS];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const int c = lane + 64 * e;
-    q[e] = (c < hd) ? bf16_bits_to_f32(qkv[(int64_t)i * N + j * hd + c]) : 0.0f;
-    o[e] = 0.0f;
-  }
-  float m = -INFINITY, l = 0.0f;
-  for (int p = s0; p <= i; ++p) {
-    const uint16_t* kp = qkv + (int64_t)p * N + (nq + g) * hd;
-    const uint16_t* vp = qkv + (int64_t)p * N + (nq + nkv + g) * hd;
-    float d = 0.0f;
+  for (int ks = 0; ks < KS; ++ks)
+    qf[ks] = __builtin_bit_cast(bf16x8_t,
+                                buf_load16(rq, chunk_off(qi, qcol, 2 * ks + (lane >> 5))));
+
+  f32x16_t ot[HDT];  // O^T tiles: rows = head_dim columns, column = this lane's query
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const int c = lane + 64 * e;
-      if (c < hd) d += q[e] * bf16_bits_to_f32(kp[c]);
+  for (int t = 0; t < HDT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ot[t][r] = 0.0f;
+  float m = -INFINITY, l = 0.0f;  // running max and sum of this lane's query
+
+  const int last = min(i0 + 31, I - 1);
+  const int first = (i0 / S) * S;
+  // K fragments (A operand: key lane%32, chunk 2 ks + lane/32) and V chunks of
+  // a key block; the next block's are loaded while the current one is processed
+  auto load_k = [&](int kb, bf16x8_t (&kf)[KS]) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[ks] = __builtin_bit_cast(
+          bf16x8_t, buf_load16(rq, chunk_off(kb + (lane & 31), kcol, 2 * ks + (lane >> 5))));
+  };
+  auto load_v = [&](int kb, u32x4_t (&vr)[2 * HDT]) {
+#pragma unroll
+    for (int u = 0; u < 2 * HDT; ++u) {
+      const int q = lane + 64 * u;  // chunk (key, 8-column group) of the 32 x 32 HDT tile
+      vr[u] = buf_load16(rq, chunk_off(kb + q / (4 * HDT), vcol, q % (4 * HDT)));
     }
+  };
+  int kb = (first / 32) * 32 + 32 * w;
+  bf16x8_t kf[KS];
+  u32x4_t vr[2 * HDT];
+  load_k(kb, kf);
+  load_v(kb, vr);
+  for (; kb <= last; kb += 32 * NWV) {
+    // ---- S^T = K Q^T: element r holds key kb + acc_row32(r, lane)
+    f32x16_t st;
 #pragma unroll
-    for (int msk = 32; msk >= 1; msk /= 2) d += __shfl_xor(d, msk, 64);
-    const float s = d * scale;
-    const float mn = fmaxf(m, s);
-    const float corr = expf(m - mn);
-    const float pe = expf(s - mn);
-    l = l * corr + pe;
+    for (int r = 0; r < 16; ++r) st[r] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const int c = lane + 64 * e;
-      const float vv = (c < hd) ? bf16_bits_to_f32(vp[c]) : 0.0f;
-      o[e] = o[e] * corr + pe * vv;
+    for (int ks = 0; ks < KS; ++ks)
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st, 0, 0, 0);
+    // ---- V^T of the key block into LDS.  Key k of the block sits at
+    //      position k with bits 2 and 3 swapped: the order in which the S^T
+    //      accumulator holds keys, so that one 16-byte read gives the A
+    //      operand matching the P^T fragment taken from the accumulator.
+#pragma unroll
+    for (int u = 0; u < 2 * HDT; ++u) {
+      const int q = lane + 64 * u;
+      const int key = q / (4 * HDT), c = q % (4 * HDT);
+      const int pos = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Vt[(c * 8 + 2 * e) * kVStride + pos] = (uint16_t)(vr[u][e] & 0xffffu);
+        Vt[(c * 8 + 2 * e + 1) * kVStride + pos] = (uint16_t)(vr[u][e] >> 16);
+      }
     }
-    m = mn;
-  }
+    // this wave's next block's loads (past the last block they read zero)
+    const int nb = kb + 32 * NWV <= last ? kb + 32 * NWV : I;
+    load_k(nb, kf);
+    load_v(nb, vr);
+    // ---- masked, scaled scores and the online softmax of this lane's query:
+    //      16 of its keys here, the other 16 in lane ^ 32
+    float x[16];
+    float mx = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const int c = lane + 64 * e;
-    if (c < hd) A[(int64_t)i * (nq * hd) + j * hd + c] = f32_to_bf16_bits(o[e] / l);
+    for (int r = 0; r < 16; ++r) {
+      const int key = kb + acc_row32(r, lane);
+      const bool ok = key <= qi && key >= qlo && qi < I;
+      x[r] = ok ? st[r] * scale : -INFINITY;
+      mx = fmaxf(mx, x[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(m, mx);
+    const float base = (mnew == -INFINITY) ? 0.0f : mnew;  // no key seen yet
+    const float corr = expf(m - base);
+    float ps = 0.0f;
+    bf16x8_t pb[2];  // P^T as the B operand: 8 keys per 16-key step
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = expf(x[r] - base);
+      ps += p;
+      pb[r >> 3][r & 7] = (__bf16)p;
+    }
+    ps += __shfl_xor(ps, 32, 64);
+    l = l * corr + ps;
+    m = mnew;
+#pragma unroll
+    for (int t = 0; t < HDT; ++t) ot[t] *= corr;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- O^T += V^T P^T: A = V^T[32 columns][16 keys], B = P^T[16 keys][query]
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int t = 0; t < HDT; ++t) {
+        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(
+            &Vt[(t * 32 + (lane & 31)) * kVStride + ks * 16 + (lane >> 5) * 8]);
+        ot[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ks], ot[t], 0, 0, 0);
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // the next block rewrites Vt
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
+  // ---- merge the waves' partial softmax states into wave 0:
+  //      O = sum_w O_w e^(m_w - M), l = sum_w l_w e^(m_w - M), M = max_w m_w
+  if constexpr (NWV > 1) {
+    if (w > 0) {
+      mls[w][0][lane] = m;
+      mls[w][1][lane] = l;
+#pragma unroll
+      for (int t = 0; t < HDT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ots[w - 1][t][r][lane] = ot[t][r];
+    }
+    __syncthreads();
+    if (w > 0) return;
+    float mm = m;
+#pragma unroll
+    for (int v = 1; v < NWV; ++v) mm = fmaxf(mm, mls[v][0][lane]);
+    const float base = (mm == -INFINITY) ? 0.0f : mm;
+    const float f0 = expf(m - base);
+    l *= f0;
+#pragma unroll
+    for (int t = 0; t < HDT; ++t) ot[t] *= f0;
+#pragma unroll
+    for (int v = 1; v < NWV; ++v) {
+      const float f = expf(mls[v][0][lane] - base);
+      l += mls[v][1][lane] * f;
+#pragma unroll
+      for (int t = 0; t < HDT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ot[t][r] += ots[v - 1][t][r][lane] * f;
+    }
+  }
+
+  // ---- A[query][column] = O / l, bf16
+  if (qi < I) {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int t = 0; t < HDT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int col = t * 32 + acc_row32(r, lane);
+        if (col < hd) A[(int64_t)qi * (nq * hd) + j * hd + col] = f32_to_bf16_bits(ot[t][r] * inv);
+      }
   }
 }
 
+// Sequences of one token: the softmax runs over a single key, whose weight is
+// exactly 1, so A is the value row of the head's KV group (16 bytes per lane).
+__global__ void __launch_bounds__(256)
+attn_single_key_kernel(int I, int nq, int nkv, int hd, const uint16_t* __restrict__ qkv,
+                       uint16_t* __restrict__ A) {
+  const int cpr = hd / 8;  // 16-byte chunks per head row
+  const int64_t n = (int64_t)I * nq * cpr;
+  const int N = (nq + 2 * nkv) * hd;
+  for (int64_t q = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; q < n;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(q % cpr);
+    const int j = (int)((q / cpr) % nq);
+    const int64_t i = q / ((int64_t)cpr * nq);
+    const int g = (j * nkv) / nq;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qkv + i * N + (nq + nkv + g) * hd + c * 8);
+    *reinterpret_cast<u32x4_t*>(A + i * (int64_t)nq * hd + j * hd + c * 8) = v;
+  }
+}
+
+// Waves per workgroup: 4 (2 above head_dim 128, for LDS), or 1 when every
+// sequence fits one key block.
+template <int HDT>
+hipError_t launch_hdt(int I, int S, int nq, int nkv, int hd, const uint16_t* qkv, uint16_t* A,
+                      hipStream_t stream) {
+  const dim3 grid((I + 31) / 32, nq);
+  if (S <= 32) {
+    hipLaunchKernelGGL((attn_core_kernel<HDT, 1>), grid, dim3(64), 0, stream, I, S, nq, nkv, hd,
+                       qkv, A);
+  } else {
+    constexpr int NWV = HDT <= 4 ? 4 : 2;
+    hipLaunchKernelGGL((attn_core_kernel<HDT, NWV>), grid, dim3(64 * NWV), 0, stream, I, S, nq,
+                       nkv, hd, qkv, A);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t attn_core_launch(int I, int S, int nq, int nkv, int hd, const uint16_t* qkv,
                             uint16_t* A, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_core_kernel, dim3(I, nq), dim3(64), 0, stream, I, S, nq, nkv, hd, qkv,
-                     A);
-  return hipGetLastError();
+  if (S == 1) {
+    const int64_t n = (int64_t)I * nq * (hd / 8);
+    const int grid = (int)std::min<int64_t>((n + 255) / 256, 1024);
+    hipLaunchKernelGGL(attn_single_key_kernel, dim3(grid), dim3(256), 0, stream, I, nq, nkv, hd,
+                       qkv, A);
+    return hipGetLastError();
+  }
+  switch ((hd + 31) / 32) {
+    case 1: return launch_hdt<1>(I, S, nq, nkv, hd, qkv, A, stream);
+    case 2: return launch_hdt<2>(I, S, nq, nkv, hd, qkv, A, stream);
+    case 3: return launch_hdt<3>(I, S, nq, nkv, hd, qkv, A, stream);
+    case 4: return launch_hdt<4>(I, S, nq, nkv, hd, qkv, A, stream);
+    case 5: return launch_hdt<5>(I, S, nq, nkv, hd, qkv, A, stream);
+    case 6: return launch_hdt<6>(I, S, nq, nkv, hd, qkv, A, stream);
+    case 7: return launch_hdt<7>(I, S, nq, nkv, hd, qkv, A, stream);
+    case 8: return launch_hdt<8>(I, S, nq, nkv, hd, qkv, A, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace tpk

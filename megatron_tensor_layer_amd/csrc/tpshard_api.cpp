@@ -239,6 +239,7 @@ tp_status_t tp_attn_core(int64_t I, int64_t S, int64_t n_q_local, int64_t n_kv_l
   if (head_dim % 8) return TP_ERR_MISALIGNED;
   if (!aligned16(qkv) || !aligned16(A)) return TP_ERR_MISALIGNED;
   const int64_t N = (n_q_local + 2 * n_kv_local) * head_dim;
+  if (I * N * 2 >= (int64_t(1) << 31)) return TP_ERR_UNSUPPORTED;  // 32-bit buffer offsets
   if (overlap(rng(A, I * n_q_local * head_dim * 2), rng(qkv, I * N * 2))) return TP_ERR_INVALID;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();

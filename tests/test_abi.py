@@ -116,13 +116,16 @@ def test_attn_core_validation(lib):
     assert c(8, 4, 4, 2, 512, fake(0), fake(1), None) == UNSUPPORTED
     assert c(8, 4, 4, 2, 60, fake(0), fake(1), None) == MISALIGNED
     assert c(0, 1, 4, 2, 64, None, None, None) == OK
+    assert c(1 << 20, 1, 8, 1, 128, fake(0), fake(1), None) == UNSUPPORTED  # qkv over 2 GiB
 
 
 def test_workspace_queries_are_host_only(lib):
-    # split-K decode (9..64 tokens) needs scratch for fp32 partials; few-token
-    # and prefill paths need none; invalid sizes report 0
+    # calls that split K (9..64 tokens on the streaming kernel, up to 256 on
+    # the tiled one) need counters + fp32 partials; few-token calls and
+    # prefill need none; invalid sizes report 0
     ws = lib.tp_shard_mlp_workspace_size
     assert ws(32, 8192, 3584, tp.TP_BF16) > 0
+    assert ws(256, 8192, 3584, tp.TP_BF16) > 0
     assert ws(64, 8192, 3584, tp.TP_BF16) >= ws(32, 8192, 3584, tp.TP_BF16) // 4
     assert ws(1, 8192, 3584, tp.TP_BF16) == 0
     assert ws(512, 8192, 3584, tp.TP_BF16) == 0

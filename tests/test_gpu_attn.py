@@ -45,7 +45,11 @@ def test_qwen_attn_projections_tp2(orc, I):
 # (I, S, n_q_local, n_kv_local, head_dim): several sequences, GQA groups,
 # head_dim below one wavefront, and above two (lanes holding 3 elements)
 CORE = [(12, 4, 4, 2, 64), (7, 7, 2, 1, 136), (16, 16, 8, 1, 128), (5, 1, 4, 4, 32),
-        (40, 20, 6, 2, 256)]
+        (40, 20, 6, 2, 256),
+        # sequences straddling the 32-row query blocks, head_dim of 3 column tiles
+        (96, 48, 4, 2, 64), (70, 35, 3, 1, 72),
+        # one causal sequence of 512 tokens at the Llama-70B TP=8 head layout
+        (512, 512, 8, 1, 128)]
 
 
 @pytest.mark.parametrize("I,S,nq,nkv,hd", CORE)
