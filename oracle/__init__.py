@@ -60,6 +60,8 @@ class Oracle:
         lib.orc_attn_core.argtypes = [_i64] * 5 + [_pd] * 2
         lib.orc_oproj_rank.restype = None
         lib.orc_oproj_rank.argtypes = [_i64] * 6 + [_pd] * 3
+        lib.orc_residual_rmsnorm.restype = None
+        lib.orc_residual_rmsnorm.argtypes = [_i64] * 3 + [_pd] * 3 + [ctypes.c_double, _pd, _pd]
 
     # ------------------------------------------------------------ helpers
     @staticmethod
@@ -147,6 +149,29 @@ class Oracle:
         qkv = self.qkv_rank(X, Wq, Wk, Wv, n_q, n_kv, hd, t, r)
         A = self.attn_core(qkv, S, n_q // t, n_kv // t, hd)
         return qkv, A, self.oproj_rank(A, Wo, n_q, hd, t, r)
+
+    # ------------------------------------------------------------ around the block
+    def residual_rmsnorm(self, partials, residual, gamma=None, eps: float = 1e-5):
+        """h = residual + sum_r partials[r] and x = RMSNorm(h) * gamma.
+        partials [t, I, D] or None (t = 0); residual [I, D] or None (zero);
+        gamma None: returns (h, None)."""
+        if partials is None and residual is None:
+            raise ValueError("need partials or a residual")
+        if partials is not None:
+            P = self._f64(partials)
+            t, I, D = P.shape
+        else:
+            P, t = None, 0
+            I, D = np.asarray(residual).shape
+        R = self._f64(residual) if residual is not None else None
+        G = self._f64(gamma) if gamma is not None else None
+        h = np.zeros((I, D))
+        x = np.zeros((I, D)) if G is not None else None
+        self.lib.orc_residual_rmsnorm(t, I, D, self._p(P) if P is not None else None,
+                                      self._p(R) if R is not None else None,
+                                      self._p(G) if G is not None else None, float(eps),
+                                      self._p(h), self._p(x) if x is not None else None)
+        return h, x
 
 
 _default: Oracle | None = None

@@ -201,3 +201,33 @@ void orc_oproj_rank(int64_t I, int64_t D, int64_t nq, int64_t hd, int64_t t,
       P[i * D + n] = s;
     }
 }
+
+/*
+ * Residual add and RMSNorm around a row-parallel block.  The lecture (§4.2)
+ * has the RMSNorm scale replicated on every rank, each rank normalising the
+ * full hidden row itself; after the block's all-reduce the residual stream
+ * is updated.  The pages name RMSNorm without defining it; the standard
+ * definition (root mean square over the hidden dimension, plus eps, scaled
+ * elementwise by gamma) is used:
+ *   h[i, j] = residual[i, j] + sum_{r<t} partials[r, i, j]   (r in order)
+ *   x[i, j] = h[i, j] / sqrt(mean_k h[i, k]^2 + eps) * gamma[j]
+ *   partials [t, I, D] (t may be 0), residual [I, D] or NULL (zero),
+ *   gamma [D] and x [I, D] both NULL: h only.
+ */
+void orc_residual_rmsnorm(int64_t t, int64_t I, int64_t D, const double *partials,
+                          const double *residual, const double *gamma, double eps,
+                          double *h, double *x) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < I; ++i) {
+    double ss = 0.0;
+    for (int64_t j = 0; j < D; ++j) {
+      double v = residual ? residual[i * D + j] : 0.0;
+      for (int64_t r = 0; r < t; ++r) v += partials[(r * I + i) * D + j];
+      h[i * D + j] = v;
+      ss += v * v;
+    }
+    if (!gamma || !x) continue;
+    const double inv = 1.0 / sqrt(ss / (double)D + eps);
+    for (int64_t j = 0; j < D; ++j) x[i * D + j] = h[i * D + j] * inv * gamma[j];
+  }
+}

@@ -25,6 +25,11 @@ MUTANTS = {
     "gqa_map": ("const int64_t g = (j * nkl) / nql;", "const int64_t g = j % nkl;"),
     "qkv_k_from_v": ("w = Wk + (g0 * hd + (c - Nq)) * D;", "w = Wv + (g0 * hd + (c - Nq)) * D;"),
     "oproj_offset": ("Wo[n * K + c0 + c]", "Wo[n * K + c]"),
+    "rms_no_eps": ("sqrt(ss / (double)D + eps)", "sqrt(ss / (double)D)"),
+    "rms_sum_not_mean": ("ss / (double)D + eps", "ss + eps"),
+    "rms_no_gamma": ("* inv * gamma[j]", "* inv"),
+    "rms_no_sqrt": ("1.0 / sqrt(ss / (double)D + eps)", "1.0 / (ss / (double)D + eps)"),
+    "residual_dropped": ("double v = residual ? residual[i * D + j] : 0.0;", "double v = 0.0;"),
 }
 
 

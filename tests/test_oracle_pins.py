@@ -260,6 +260,66 @@ def pin_attention_block_sharded_equals_full(orc):
         assert normwise_err(orc.reduce(parts), full) <= 1e-12, t
 
 
+def _residual_rmsnorm_decimal(P, R, g, eps):
+    """Independent brute force in 40-digit decimal arithmetic."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 40
+    t, I, D = P.shape
+    h = [[Decimal(float(R[i, j])) + sum(Decimal(float(P[r, i, j])) for r in range(t))
+          for j in range(D)] for i in range(I)]
+    x = []
+    for i in range(I):
+        ms = sum(v * v for v in h[i]) / D
+        inv = 1 / (ms + Decimal(eps)).sqrt()
+        x.append([h[i][j] * inv * Decimal(float(g[j])) for j in range(D)])
+    return (np.array([[float(v) for v in row] for row in h]),
+            np.array([[float(v) for v in row] for row in x]))
+
+
+def pin_residual_rmsnorm_bruteforce(orc):
+    """Residual add + RMSNorm (standard definition: the pages name RMSNorm,
+    replicated on every rank, without spelling it out) against a 40-digit
+    decimal evaluation of the same definition."""
+    rng = np.random.default_rng(11)
+    for t, I, D, eps in ((3, 2, 7, 1e-5), (1, 3, 16, 0.5), (2, 1, 5, 1e-6)):
+        P = rng.standard_normal((t, I, D))
+        R = rng.standard_normal((I, D))
+        g = rng.uniform(0.5, 1.5, D)
+        h, x = orc.residual_rmsnorm(P, R, g, eps)
+        hb, xb = _residual_rmsnorm_decimal(P, R, g, eps)
+        assert np.allclose(h, hb, rtol=1e-14, atol=1e-14)
+        assert np.allclose(x, xb, rtol=1e-13, atol=1e-14)
+
+
+def pin_rmsnorm_closed_forms(orc):
+    """A constant row c gives x_j = c g_j / sqrt(c^2 + eps); with eps = 0 the
+    result is invariant to scaling the row; mean_j (x_j / g_j)^2 equals
+    ms / (ms + eps); no partials leave the residual, no residual leaves the
+    rank-order sum (exact small values)."""
+    D = 16
+    g = np.linspace(0.5, 2.0, D)
+    for c, eps in ((3.0, 0.25), (-2.0, 1e-5), (0.5, 0.0)):
+        _, x = orc.residual_rmsnorm(None, np.full((1, D), c), g, eps)
+        assert np.allclose(x[0], c * g / math.sqrt(c * c + eps), rtol=1e-15)
+    rng = np.random.default_rng(3)
+    R = rng.standard_normal((4, D))
+    _, x1 = orc.residual_rmsnorm(None, R, g, 0.0)
+    _, x3 = orc.residual_rmsnorm(None, 3.0 * R, g, 0.0)
+    assert np.allclose(x1, x3, rtol=1e-14)
+    eps = 0.3
+    _, x = orc.residual_rmsnorm(None, R, g, eps)
+    ms = (R ** 2).mean(axis=1)
+    assert np.allclose(((x / g) ** 2).mean(axis=1), ms / (ms + eps), rtol=1e-14)
+    h, xn = orc.residual_rmsnorm(None, R, None)
+    assert np.array_equal(h, R) and xn is None
+    P = np.arange(2 * 3 * 4, dtype=np.float64).reshape(2, 3, 4) - 7.0
+    Rs = np.full((3, 4), 0.5)
+    h, _ = orc.residual_rmsnorm(P, None)
+    assert np.array_equal(h, P.sum(axis=0))
+    h, _ = orc.residual_rmsnorm(P, Rs)
+    assert np.array_equal(h, P.sum(axis=0) + 0.5)
+
+
 ALL_PINS = [
     pin_silu_closed_forms,
     pin_mlp_bruteforce_exact,
@@ -273,6 +333,8 @@ ALL_PINS = [
     pin_qkv_column_shards,
     pin_oproj_row_partials,
     pin_attention_block_sharded_equals_full,
+    pin_residual_rmsnorm_bruteforce,
+    pin_rmsnorm_closed_forms,
 ]
 
 
