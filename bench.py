@@ -18,13 +18,16 @@ exceed the 256 MB Infinity Cache, so every step streams them from HBM.
 
 The printed JSON line also carries
   roofline:     the dominant call (one rank's tp_shard_mlp at I=32) timed with
-                HIP events on its stream inside the timed region, against the
-                8 TB/s HBM peak;
+                HIP events on its stream inside the timed region (one rank's
+                call per step, rotating over the ranks), against the 8 TB/s
+                HBM peak;
   cpu_baseline: the fp64 oracle on the host cores running one whole step
                 (about 55 GFLOP in fp64, a second or so on 16 cores);
   detail:       per-config figures (MLP shard decode I=1/16/64/256 GB/s,
                 prefill 512 TFLOP/s at TP=8 and TP=1, Qwen2.5-1.5B TP=2 calls,
-                the layer at prefill 512, the partial reduce).
+                the layer at prefill 512, the partial reduce, the residual
+                update + RMSNorm after a block, and the layer as a pre-norm
+                block with those at decode 32).
 """
 from __future__ import annotations
 
@@ -194,6 +197,9 @@ class Layer:
                 o=to_dev(torch, datagen.oproj_rank_shard(Wo, NQ, HD, TP, r)),
                 mlp=tuple(to_dev(torch, a) for a in datagen.mlp_rank_shards(Wg, Wu, Wd, TP, r))))
         self.nql, self.nkl = NQ // TP, NKV // TP
+        # replicated RMSNorm scales in front of attention and MLP (and of the next layer)
+        self.gammas = [to_dev(torch, datagen.rmsnorm_gamma(D, pool + k, "bf16"))
+                       for k in range(3)]
 
     def buffers(self, I):
         T = self.torch
@@ -204,9 +210,10 @@ class Layer:
                     y1=T.empty((I, D), dtype=bf, device="cuda"),
                     H=T.empty((I, F // TP), dtype=bf, device="cuda"),
                     pm=T.empty((TP, I, D), dtype=f32, device="cuda"),
-                    y=T.empty((I, D), dtype=f32, device="cuda"))
+                    y=T.empty((I, D), dtype=f32, device="cuda"),
+                    x=T.empty((I, D), dtype=bf, device="cuda"))
 
-    def step(self, X, B, S, mlp_events=None):
+    def step(self, X, B, S, mlp_events=None, timed_rank=0):
         tp = self.tp
         for r, R in enumerate(self.ranks):
             tp.shard_attn_proj(tp.TP_ATTN_QKV, X, R["qkv"], B["qkv"], self.nql, self.nkl, HD)
@@ -215,14 +222,33 @@ class Layer:
         tp.partial_reduce(B["po"], B["y1"])
         s = self.torch.cuda.current_stream()
         for r, R in enumerate(self.ranks):
-            if mlp_events is not None:
+            timed = mlp_events is not None and r == timed_rank
+            if timed:  # one rank's call per step: few event records in the stream
                 e0, e1 = (self.torch.cuda.Event(enable_timing=True) for _ in range(2))
                 e0.record(s)
             tp.shard_mlp(B["y1"], *R["mlp"], B["H"], B["pm"][r])
-            if mlp_events is not None:
+            if timed:
                 e1.record(s)
                 mlp_events.append((e0, e1))
         tp.partial_reduce(B["pm"], B["y"])
+
+
+    def prenorm_step(self, h, B, S):
+        """The layer as a pre-norm block on the residual stream h [I, D] bf16
+        (updated in place): x = RMSNorm(h); per rank QKV -> attention core ->
+        o_proj; h += sum of the partials, x = RMSNorm(h); per rank MLP;
+        h += sum of the partials, x = RMSNorm(h) (the next layer's input).
+        The RMSNorm every rank repeats is computed once here: same result."""
+        tp, g = self.tp, self.gammas
+        tp.residual_rmsnorm(None, h, h, g[0], B["x"])
+        for r, R in enumerate(self.ranks):
+            tp.shard_attn_proj(tp.TP_ATTN_QKV, B["x"], R["qkv"], B["qkv"], self.nql, self.nkl, HD)
+            tp.attn_core(B["qkv"], B["A"], S, self.nql, self.nkl, HD)
+            tp.shard_attn_proj(tp.TP_ATTN_O, B["A"], R["o"], B["po"][r], self.nql, self.nkl, HD)
+        tp.residual_rmsnorm(B["po"], h, h, g[1], B["x"])
+        for r, R in enumerate(self.ranks):
+            tp.shard_mlp(B["x"], *R["mlp"], B["H"], B["pm"][r])
+        tp.residual_rmsnorm(B["pm"], h, h, g[2], B["x"])
 
 
 def step_bytes(I, S):
@@ -234,6 +260,16 @@ def step_bytes(I, S):
     per_rank = q.bytes() + o.bytes() + m.bytes() + (attn_core or 0)
     red = wl.ReduceShape(TP, I * D, wl.BF16).bytes() + wl.ReduceShape(TP, I * D, wl.F32).bytes()
     return TP * per_rank + red
+
+
+def prenorm_step_bytes(I, S):
+    """Compulsory bytes of the pre-norm block: the projections and attention
+    as in step_bytes, plus the first RMSNorm and the two residual updates
+    with RMSNorm in place of the two reduces."""
+    red = wl.ReduceShape(TP, I * D, wl.BF16).bytes() + wl.ReduceShape(TP, I * D, wl.F32).bytes()
+    norms = (wl.ResidualNormShape(0, I, D).bytes() +
+             2 * wl.ResidualNormShape(TP, I, D).bytes())
+    return step_bytes(I, S) - red + norms
 
 
 def step_flops(I):
@@ -313,6 +349,29 @@ def detail(torch, tp, layer, calls):
         st = stats(time_calls(T, [lambda: tp.partial_reduce(Pp, Y)], calls))
         gbs = wl.ReduceShape(TP, I * D).bytes() / (st["median_us"] * 1e-6) / 1e9
         out[f"reduce_t8_I{I}"] = dict(**st, GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM, 3))
+    # residual update + RMSNorm after a block's reduce of 8 partials (bf16 h, x)
+    for I in (32, 512):
+        Pp = T.randn((TP, I, D), device="cuda")
+        h = to_dev(T, datagen.gaussian("h", (I, D), 1.0, "bf16", 4000 + I))
+        x = T.empty((I, D), dtype=T.bfloat16, device="cuda")
+        g = layer.gammas[1]
+        st = stats(time_calls(T, [lambda: tp.residual_rmsnorm(Pp, h, h, g, x)], calls))
+        gbs = wl.ResidualNormShape(TP, I, D).bytes() / (st["median_us"] * 1e-6) / 1e9
+        out[f"residual_rmsnorm_t8_I{I}"] = dict(**st, GBps=round(gbs, 1),
+                                                frac_hbm=round(gbs / PEAK_HBM, 3))
+    # the layer as a pre-norm block (RMSNorm, attention block, residual + RMSNorm,
+    # MLP, residual + RMSNorm), decode 32
+    I = 32
+    B = layer.buffers(I)
+    h = to_dev(T, datagen.gaussian("h", (I, D), 1.0, "bf16", 4032))
+    st = stats(time_calls(T, [lambda: layer.prenorm_step(h, B, 1)], 20, 3))
+    nb = prenorm_step_bytes(I, 1)
+    gbs = nb / (st["median_us"] * 1e-6) / 1e9
+    out["llama70b_prenorm_layer_tp8x8_decode_I32"] = dict(
+        **st, bytes_per_step=nb, GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM, 3),
+        tokens_per_s_excl_comm=round(I / (st["median_us"] * 1e-6)))
+    log(f"pre-norm layer decode 32: {st['median_us']} us")
+    del B
     # Qwen2.5-1.5B-shaped rank share at TP=2: 24 independently seeded rank
     # shares rotate so the calls stream from HBM, not the Infinity Cache
     Dq, Fq, nq, nkv, t = 1536, 8960, 12, 2, 2
@@ -407,8 +466,8 @@ def main():
     t0 = time.perf_counter()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(args.steps):
-        layer.step(X, B, S, mlp_events=mlp_ev)
+    for k in range(args.steps):
+        layer.step(X, B, S, mlp_events=mlp_ev, timed_rank=k % TP)
     e1.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps

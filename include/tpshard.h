@@ -148,6 +148,29 @@ tp_status_t tp_partial_reduce(int32_t t, int64_t n, const float* partials,
                               tp_dtype_t out_dt, void* Y, void* stream);
 
 /*
+ * The step after a row-parallel block's all-reduce, fused into one pass over
+ * each hidden row: the residual update and the replicated RMSNorm in front of
+ * the next column-parallel projection ([L4] §4.2: the RMSNorm scale is
+ * replicated and every rank normalises the full row itself).  The pages name
+ * RMSNorm without defining it; the standard definition is used:
+ *   h[i, :] = residual[i, :] + sum_{r<t} partials[r, i, :]    fp32, r in order
+ *   x[i, :] = h[i, :] / sqrt(mean_j h[i, j]^2 + eps) * gamma  from h as stored
+ *   partials [t, I, D] fp32, t >= 0 (may be NULL when t == 0)
+ *   residual [I, D] h_dt, or NULL (zero; then t >= 1)
+ *   h        [I, D] h_dt out (fp32, or bf16 rounded to nearest-even); may be
+ *            the residual pointer itself (in-place update), no other overlap
+ *   gamma    [D] x_dt and x [I, D] x_dt out: both NULL to compute h only
+ *   eps      >= 0, finite
+ * D a multiple of 8 and at most 32768.  With t partials of the o_proj (or
+ * MLP) block this is what every rank does right after the block's all-reduce.
+ * Errors: TP_ERR_INVALID, TP_ERR_MISALIGNED, TP_ERR_UNSUPPORTED, TP_ERR_LAUNCH.
+ */
+tp_status_t tp_residual_rmsnorm(int32_t t, int64_t I, int64_t D, const float* partials,
+                                const void* residual, tp_dtype_t h_dt, void* h,
+                                const void* gamma, tp_dtype_t x_dt, void* x, float eps,
+                                void* stream);
+
+/*
  * Attention core of one rank (test support, not a projection): each rank
  * computes its own heads' attention completely ([L4] §4.2).  Scaled dot
  * product (scale 1/sqrt(head_dim)), causal inside each sequence, no rotary

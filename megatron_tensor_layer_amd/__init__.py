@@ -39,6 +39,8 @@ SIGNATURES = {
                                           ctypes.c_int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "tp_partial_reduce": (ctypes.c_int, [_i32, _i64, _vp, ctypes.c_int, _vp, _vp]),
     "tp_attn_core": (ctypes.c_int, [_i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "tp_residual_rmsnorm": (ctypes.c_int, [_i32, _i64, _i64, _vp, _vp, ctypes.c_int, _vp, _vp,
+                                           ctypes.c_int, _vp, ctypes.c_float, _vp]),
 }
 
 
@@ -213,6 +215,38 @@ def partial_reduce(partials, Y, stream=None) -> None:
         raise ValueError("Y must hold one partial's elements")
     _check("tp_partial_reduce", lib().tp_partial_reduce(t, n, _ptr(partials), _dt(Y), _ptr(Y),
                                                         _stream(stream, dev)))
+
+
+def residual_rmsnorm(partials, residual, h, gamma=None, x=None, eps: float = 1e-5,
+                     stream=None) -> None:
+    """h = residual + sum over r of partials[r] (rank order, fp32), then
+    x = h / sqrt(mean(h^2) + eps) * gamma from h as stored.  partials [t, I, D]
+    float32 or None; residual [I, D] (h's dtype) or None; h may be residual
+    itself; gamma [D] and x [I, D] (same dtype) both None for h only."""
+    torch = _torch()
+    tensors = [a for a in (partials, residual, h, gamma, x) if a is not None]
+    dev = _dev(*tensors)
+    I, D = h.shape
+    t = 0
+    if partials is not None:
+        if partials.dtype != torch.float32 or partials.dim() != 3 or \
+                tuple(partials.shape[1:]) != (I, D):
+            raise ValueError("partials must be float32 [t, I, D]")
+        t = partials.shape[0]
+    if residual is not None and (residual.dtype != h.dtype or tuple(residual.shape) != (I, D)):
+        raise ValueError("residual must match h's dtype and shape")
+    if (gamma is None) != (x is None):
+        raise ValueError("gamma and x go together")
+    x_dt = TP_F32
+    if x is not None:
+        if x.dtype != gamma.dtype or tuple(x.shape) != (I, D) or gamma.numel() != D:
+            raise ValueError("x [I, D] and gamma [D] must share a dtype")
+        x_dt = _dt(x)
+    _check("tp_residual_rmsnorm", lib().tp_residual_rmsnorm(
+        t, I, D, _ptr(partials) if partials is not None else None,
+        _ptr(residual) if residual is not None else None, _dt(h), _ptr(h),
+        _ptr(gamma) if gamma is not None else None, x_dt,
+        _ptr(x) if x is not None else None, float(eps), _stream(stream, dev)))
 
 
 def attn_core(qkv, A, S: int, n_q_local: int, n_kv_local: int, head_dim: int,

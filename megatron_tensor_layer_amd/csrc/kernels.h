@@ -56,6 +56,13 @@ hipError_t gemm_launch(int M, int N, int K, const uint16_t* A, int64_t lda, cons
 hipError_t reduce_launch(int t, int64_t n, const float* P, bool out_bf16, void* Y,
                          hipStream_t stream);
 
+// h = residual + sum_r P_r (rank order), then x = RMSNorm(h as stored) * gamma
+// (x == nullptr: h only); one workgroup per row, D <= kNormMaxD.
+constexpr int kNormMaxD = 32768;
+hipError_t residual_rmsnorm_launch(int t, int I, int D, const float* P, const void* residual,
+                                   bool h_bf16, void* h, const void* gamma, bool x_bf16, void* x,
+                                   float eps, hipStream_t stream);
+
 hipError_t attn_core_launch(int I, int S, int nq, int nkv, int hd, const uint16_t* qkv,
                             uint16_t* A, hipStream_t stream);
 

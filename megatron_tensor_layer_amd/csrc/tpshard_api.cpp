@@ -227,6 +227,39 @@ tp_status_t tp_partial_reduce(int32_t t, int64_t n, const float* partials, tp_dt
   return launched(tpk::reduce_launch(t, n, partials, out_dt == TP_BF16, Y, s));
 }
 
+tp_status_t tp_residual_rmsnorm(int32_t t, int64_t I, int64_t D, const float* partials,
+                                const void* residual, tp_dtype_t h_dt, void* h,
+                                const void* gamma, tp_dtype_t x_dt, void* x, float eps,
+                                void* stream) {
+  if (t < 0 || I < 0 || I > INT32_MAX || !dims_ok(D) || !dtype_ok(h_dt) || !dtype_ok(x_dt))
+    return TP_ERR_INVALID;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return TP_ERR_INVALID;  // rejects NaN and inf too
+  if (I == 0) return TP_OK;
+  if (!h || (t > 0 && !partials) || (t == 0 && !residual) || (!gamma) != (!x))
+    return TP_ERR_INVALID;
+  if (D % 8) return TP_ERR_MISALIGNED;
+  if (D > tpk::kNormMaxD) return TP_ERR_UNSUPPORTED;
+  for (const void* p : {static_cast<const void*>(partials), residual, static_cast<const void*>(h),
+                        gamma, static_cast<const void*>(x)})
+    if (p && !aligned16(p)) return TP_ERR_MISALIGNED;
+  const int64_t n = I * D;
+  const Range rP = rng(partials, (int64_t)t * n * 4), rR = rng(residual, residual ? n * esize(h_dt) : 0),
+              rH = rng(h, n * esize(h_dt)), rG = rng(gamma, gamma ? D * esize(x_dt) : 0),
+              rX = rng(x, x ? n * esize(x_dt) : 0);
+  if (t > 0 && overlap(rH, rP)) return TP_ERR_INVALID;
+  if (residual && residual != h && overlap(rH, rR)) return TP_ERR_INVALID;  // exact alias is in place
+  if (x) {
+    for (Range o : {rP, rR, rH, rG})
+      if (overlap(rX, o)) return TP_ERR_INVALID;
+    if (overlap(rH, rG)) return TP_ERR_INVALID;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  return launched(tpk::residual_rmsnorm_launch(t, (int)I, (int)D, partials, residual,
+                                               h_dt == TP_BF16, h, gamma, x_dt == TP_BF16, x,
+                                               eps, s));
+}
+
 tp_status_t tp_attn_core(int64_t I, int64_t S, int64_t n_q_local, int64_t n_kv_local,
                          int64_t head_dim, const void* qkv, void* A, void* stream) {
   if (I < 0 || I > INT32_MAX || !dims_ok(S) || !dims_ok(n_kv_local) || n_q_local < 1 ||

@@ -41,6 +41,9 @@ TENSOR_IDS = {
     "W_v": 6,      # [n_kv*hd, D]
     "W_o": 7,      # [D, n_q*hd]
     "A": 8,        # stand-alone attention output [I, n_q*hd] (o_proj-only cases)
+    "P": 9,        # stand-alone row-parallel partials [t, I, D] (reduce / norm cases)
+    "h": 10,       # residual stream [I, D]
+    "gamma": 11,   # RMSNorm scale [D]: 1 + N(0, sigma^2), near 1 like trained scales
 }
 
 _CHUNK = 1 << 24  # elements per draw, bounds the temporaries of the rounding
@@ -144,3 +147,12 @@ def oproj_rank_shard(Wo, n_q: int, hd: int, t: int, r: int):
     """Rank r's W_o block: columns of its own heads, [D, (n_q/t)*hd]."""
     bq = rank_block(n_q, t, r)
     return np.ascontiguousarray(Wo[:, bq.start * hd:bq.stop * hd])
+
+
+def rmsnorm_gamma(D: int, pool: int, dtype: str = "f32", sigma: float = 0.1) -> np.ndarray:
+    """RMSNorm scale: 1 + N(0, sigma^2) per hidden unit, float32, rounded to
+    bf16 (nearest-even) when dtype == 'bf16'."""
+    g = (1.0 + gaussian("gamma", (D,), sigma, "f32", pool)).astype(np.float32)
+    if dtype == "bf16":
+        _round_to_bf16_inplace(g)
+    return g

@@ -88,6 +88,28 @@ class ReduceShape:
         return self.t * self.n * F32 + self.n * self.out_esize
 
 
+@dataclass(frozen=True)
+class ResidualNormShape:
+    """Residual update + RMSNorm after a block's reduce: reads t fp32
+    partials, the residual and gamma, writes h and x (each once)."""
+    t: int
+    I: int
+    D: int
+    h_esize: int = BF16
+    x_esize: int = BF16
+    residual: bool = True
+    norm: bool = True
+
+    def bytes(self) -> int:
+        n = self.I * self.D
+        b = self.t * n * F32 + n * self.h_esize
+        if self.residual:
+            b += n * self.h_esize
+        if self.norm:
+            b += n * self.x_esize + self.D * self.x_esize
+        return b
+
+
 def allreduce_message_bytes(B: int, D: int, esize: int = BF16) -> int:
     """Size of one layer all-reduce message [B, D] (lecture §4.5, exercise 3)."""
     return B * D * esize

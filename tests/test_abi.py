@@ -119,6 +119,30 @@ def test_attn_core_validation(lib):
     assert c(1 << 20, 1, 8, 1, 128, fake(0), fake(1), None) == UNSUPPORTED  # qkv over 2 GiB
 
 
+def test_residual_rmsnorm_validation(lib):
+    n = lib.tp_residual_rmsnorm
+    F, B = tp.TP_F32, tp.TP_BF16
+    eps = ctypes.c_float(1e-5)
+    P, R, H, G, X = (fake(k) for k in range(5))
+    assert n(0, 0, 64, None, None, F, None, None, F, None, eps, None) == OK          # empty
+    assert n(-1, 2, 64, P, R, F, H, G, B, X, eps, None) == INVALID
+    assert n(2, 2, 0, P, R, F, H, G, B, X, eps, None) == INVALID
+    assert n(2, 2, 64, P, R, 7, H, G, B, X, eps, None) == INVALID                   # bad dtype
+    for bad in (-1.0, float("nan"), float("inf")):
+        assert n(2, 2, 64, P, R, F, H, G, B, X, ctypes.c_float(bad), None) == INVALID
+    assert n(2, 2, 64, P, R, F, None, G, B, X, eps, None) == INVALID                # no h
+    assert n(2, 2, 64, None, R, F, H, G, B, X, eps, None) == INVALID                # t > 0, no partials
+    assert n(0, 2, 64, None, None, F, H, G, B, X, eps, None) == INVALID             # nothing to add
+    assert n(2, 2, 64, P, R, F, H, G, B, None, eps, None) == INVALID                # gamma without x
+    assert n(2, 2, 60, P, R, F, H, G, B, X, eps, None) == MISALIGNED
+    assert n(2, 2, 40000, P, R, F, H, G, B, X, eps, None) == UNSUPPORTED
+    assert n(2, 2, 64, P, ctypes.c_void_p(FAKE + STEP + 8), F, H, G, B, X, eps, None) == MISALIGNED
+    near_h = ctypes.c_void_p(FAKE + 2 * STEP + 256)
+    assert n(2, 2, 64, P, near_h, F, H, G, B, X, eps, None) == INVALID             # h overlaps residual
+    assert n(2, 2, 64, P, R, F, H, G, B, near_h, eps, None) == INVALID             # x overlaps h
+    assert n(2, 2, 64, P, R, F, ctypes.c_void_p(FAKE + 128), G, B, X, eps, None) == INVALID  # h in partials
+
+
 def test_workspace_queries_are_host_only(lib):
     # calls that split K (9..64 tokens on the streaming kernel, up to 256 on
     # the tiled one) need counters + fp32 partials; few-token calls and

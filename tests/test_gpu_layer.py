@@ -94,3 +94,50 @@ def test_layer_prefill512_rank0(orc, layer):
     assert normwise_err(to_host(po0)[rows], po_ref[rows]) <= TOL
     T = torch()
     assert T.isfinite(y).all() and T.isfinite(y1.float()).all()
+
+
+def test_prenorm_block_decode32(orc, layer):
+    """The layer as a pre-norm block on the residual stream h (bf16), decode
+    32: x = RMSNorm(h); 8 ranks' attention blocks; h += sum of the o_proj
+    partials, x = RMSNorm(h); 8 ranks' MLPs; h += sum of the MLP partials,
+    x = RMSNorm(h).  Against the unsharded fp64 oracle (MLP on sampled rows)."""
+    T = torch()
+    I, S, eps = 32, 1, 1e-5
+    nql, nkl = NQ // T_, NKV // T_
+    h0 = datagen.gaussian("h", (I, D), 1.0, "bf16", 77)
+    gs = [datagen.rmsnorm_gamma(D, 40 + k, "bf16") for k in range(3)]
+    gd = [to_dev(g, "bf16") for g in gs]
+    h = to_dev(h0, "bf16")
+    x = empty((I, D), "bf16")
+    tp.residual_rmsnorm(None, h, h, gd[0], x, eps)
+    x1 = to_host(x).copy()
+    po = T.empty((T_, I, D), dtype=T.float32, device="cuda")
+    for r, R in enumerate(layer["ranks"]):
+        qkv = empty((I, (nql + 2 * nkl) * HD), "bf16")
+        tp.shard_attn_proj(tp.TP_ATTN_QKV, x, R["qkv"], qkv, nql, nkl, HD)
+        A = empty((I, nql * HD), "bf16")
+        tp.attn_core(qkv, A, S, nql, nkl, HD)
+        tp.shard_attn_proj(tp.TP_ATTN_O, A, R["o"], po[r], nql, nkl, HD)
+    tp.residual_rmsnorm(po, h, h, gd[1], x, eps)
+    T.cuda.synchronize()
+    h1, x2 = to_host(h).copy(), to_host(x).copy()
+    pm = T.empty((T_, I, D), dtype=T.float32, device="cuda")
+    for r, R in enumerate(layer["ranks"]):
+        H = empty((I, F // T_), "bf16")
+        tp.shard_mlp(x, *R["mlp"], H, pm[r])
+    tp.residual_rmsnorm(pm, h, h, gd[2], x, eps)
+    T.cuda.synchronize()
+    h2, x3 = to_host(h), to_host(x)
+
+    Wq, Wk, Wv, Wo = layer["attn"]
+    _, x1_ref = orc.residual_rmsnorm(None, h0, gs[0], eps)
+    assert normwise_err(x1, x1_ref) <= TOL
+    _, _, a_ref = orc.attn_block_rank(x1_ref, Wq, Wk, Wv, Wo, NQ, NKV, HD, S)
+    h1_ref, x2_ref = orc.residual_rmsnorm(a_ref[None], h0, gs[1], eps)
+    assert normwise_err(h1, h1_ref) <= TOL
+    assert normwise_err(x2, x2_ref) <= TOL
+    rows = [0, 17, 31]
+    _, y_ref = orc.mlp_full(x2_ref, *layer["mlp"], rows=rows)
+    h2_ref, x3_ref = orc.residual_rmsnorm(y_ref[None], h1_ref[rows], gs[2], eps)
+    assert normwise_err(h2[rows], h2_ref) <= TOL
+    assert normwise_err(x3[rows], x3_ref) <= TOL
