@@ -60,6 +60,10 @@ class Oracle:
         lib.orc_attn_core.argtypes = [_i64] * 5 + [_pd] * 2
         lib.orc_oproj_rank.restype = None
         lib.orc_oproj_rank.argtypes = [_i64] * 6 + [_pd] * 3
+        lib.orc_e4m3.restype = ctypes.c_double
+        lib.orc_e4m3.argtypes = [ctypes.c_ubyte]
+        lib.orc_dequant_fp8.restype = None
+        lib.orc_dequant_fp8.argtypes = [_i64, _i64, ctypes.POINTER(ctypes.c_ubyte), _pd, _pd]
         lib.orc_residual_rmsnorm.restype = None
         lib.orc_residual_rmsnorm.argtypes = [_i64] * 3 + [_pd] * 3 + [ctypes.c_double, _pd, _pd]
 
@@ -149,6 +153,20 @@ class Oracle:
         qkv = self.qkv_rank(X, Wq, Wk, Wv, n_q, n_kv, hd, t, r)
         A = self.attn_core(qkv, S, n_q // t, n_kv // t, hd)
         return qkv, A, self.oproj_rank(A, Wo, n_q, hd, t, r)
+
+    # ------------------------------------------------------------ FP8 weights
+    def e4m3(self, code: int) -> float:
+        return self.lib.orc_e4m3(code)
+
+    def dequant_fp8(self, codes, scales) -> np.ndarray:
+        """W[n, k] = scales[n] * e4m3(codes[n, k]) (fp64)."""
+        c = np.ascontiguousarray(codes, dtype=np.uint8)
+        sc = self._f64(scales)
+        N, K = c.shape
+        W = np.empty((N, K))
+        self.lib.orc_dequant_fp8(N, K, c.ctypes.data_as(ctypes.POINTER(ctypes.c_ubyte)),
+                                 self._p(sc), self._p(W))
+        return W
 
     # ------------------------------------------------------------ around the block
     def residual_rmsnorm(self, partials, residual, gamma=None, eps: float = 1e-5):

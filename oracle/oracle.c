@@ -231,3 +231,26 @@ void orc_residual_rmsnorm(int64_t t, int64_t I, int64_t D, const double *partial
     for (int64_t j = 0; j < D; ++j) x[i * D + j] = h[i * D + j] * inv * gamma[j];
   }
 }
+
+/*
+ * Weight-only FP8 storage for decode (the pages' cost frontier points are
+ * FP8; they give no storage convention, so the reading here is): each
+ * weight is one byte in the OCP E4M3 "fn" encoding -- sign bit, 4 exponent
+ * bits with bias 7, 3 mantissa bits; exponent 0 holds subnormals m/8 * 2^-6;
+ * all-ones exponent and mantissa is NaN; no infinities -- and every output
+ * row n carries one scale s[n]: W[n, k] = s[n] * e4m3(code[n, k]).
+ */
+double orc_e4m3(unsigned char code) {
+  const int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double v = (e == 0) ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -v : v;
+}
+
+/* W[n, k] = scales[n] * e4m3(codes[n, k]) for n < N rows of K bytes. */
+void orc_dequant_fp8(int64_t N, int64_t K, const unsigned char *codes, const double *scales,
+                     double *W) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) W[n * K + k] = scales[n] * orc_e4m3(codes[n * K + k]);
+}

@@ -30,6 +30,10 @@ MUTANTS = {
     "rms_no_gamma": ("* inv * gamma[j]", "* inv"),
     "rms_no_sqrt": ("1.0 / sqrt(ss / (double)D + eps)", "1.0 / (ss / (double)D + eps)"),
     "residual_dropped": ("double v = residual ? residual[i * D + j] : 0.0;", "double v = 0.0;"),
+    "e4m3_bias": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    "e4m3_no_subnormal": ("ldexp(m / 8.0, -6)", "ldexp(1.0 + m / 8.0, -7)"),
+    "e4m3_mantissa": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 16.0, e - 7)"),
+    "fp8_row_scale": ("scales[n] * orc_e4m3(codes[n * K + k])", "scales[k % N] * orc_e4m3(codes[n * K + k])"),
 }
 
 

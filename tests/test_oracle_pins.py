@@ -320,6 +320,45 @@ def pin_rmsnorm_closed_forms(orc):
     assert np.array_equal(h, P.sum(axis=0) + 0.5)
 
 
+def _e4m3_fraction(code: int):
+    """The E4M3 "fn" value of a byte as an exact Fraction (None for NaN),
+    written from the format's definition."""
+    sign = -1 if code & 0x80 else 1
+    exp, man = (code >> 3) & 0xF, code & 0x7
+    if exp == 0xF and man == 0x7:
+        return None
+    if exp == 0:
+        return sign * Fraction(man, 8) * Fraction(1, 2 ** 6)
+    return sign * (1 + Fraction(man, 8)) * (Fraction(2) ** (exp - 7))
+
+
+def pin_fp8_decode(orc):
+    """All 256 codes against the exact definition; closed forms (1, 2, 448 the
+    largest, 2^-9 the smallest subnormal, 2^-6 the smallest normal, -0, NaN);
+    positive codes increase monotonically."""
+    for c in range(256):
+        ref = _e4m3_fraction(c)
+        v = orc.e4m3(c)
+        if ref is None:
+            assert math.isnan(v), c
+        else:
+            assert Fraction(v) == ref, (c, v, ref)
+    assert orc.e4m3(0x38) == 1.0 and orc.e4m3(0x40) == 2.0 and orc.e4m3(0x7E) == 448.0
+    assert orc.e4m3(0x01) == 2.0 ** -9 and orc.e4m3(0x08) == 2.0 ** -6
+    assert orc.e4m3(0x80) == 0.0 and math.copysign(1.0, orc.e4m3(0x80)) == -1.0
+    assert math.isnan(orc.e4m3(0x7F)) and math.isnan(orc.e4m3(0xFF))
+    pos = [orc.e4m3(c) for c in range(0x7F)]
+    assert all(a < b for a, b in zip(pos, pos[1:]))
+
+
+def pin_fp8_dequant_rows(orc):
+    """Each row scales its decoded codes by its own scale."""
+    codes = np.array([[0x38, 0x40, 0xB8, 0x00], [0x7E, 0x01, 0x08, 0x30]], dtype=np.uint8)
+    W = orc.dequant_fp8(codes, [0.5, -2.0])
+    ref = np.array([[0.5, 1.0, -0.5, 0.0], [-896.0, -2.0 ** -8, -2.0 ** -5, -1.0]])
+    assert np.array_equal(W, ref)
+
+
 ALL_PINS = [
     pin_silu_closed_forms,
     pin_mlp_bruteforce_exact,
@@ -335,6 +374,8 @@ ALL_PINS = [
     pin_attention_block_sharded_equals_full,
     pin_residual_rmsnorm_bruteforce,
     pin_rmsnorm_closed_forms,
+    pin_fp8_decode,
+    pin_fp8_dequant_rows,
 ]
 
 
