@@ -26,8 +26,9 @@ The printed JSON line also carries
   detail:       per-config figures (MLP shard decode I=1/16/64/256 GB/s,
                 prefill 512 TFLOP/s at TP=8 and TP=1, Qwen2.5-1.5B TP=2 calls,
                 the layer at prefill 512, the partial reduce, the residual
-                update + RMSNorm after a block, and the layer as a pre-norm
-                block with those at decode 32).
+                update + RMSNorm after a block, the layer as a pre-norm block
+                with those at decode 32, and the MLP with weight-only FP8
+                storage at decode 1 and 8).
 """
 from __future__ import annotations
 
@@ -297,6 +298,35 @@ def detail(torch, tp, layer, calls):
             **st, GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM, 3),
             TFLOPs=round(m.flops() / (st["median_us"] * 1e-6) / 1e12, 1),
             tokens_per_s=round(I / (st["median_us"] * 1e-6)))
+    # the same rank shares with weight-only FP8 storage (E4M3 codes + one fp32
+    # scale per row): 8 seeded random shares, one byte per weight
+    Fl = F // TP
+    gen = T.Generator(device="cuda")
+    gen.manual_seed(8)
+
+    def codes(n, k):  # finite E4M3 codes with random signs (no 0x7F / 0xFF)
+        c = T.randint(0, 0x7F, (n, k), generator=gen, device="cuda", dtype=T.int32)
+        c |= T.randint(0, 2, (n, k), generator=gen, device="cuda", dtype=T.int32) << 7
+        return c.to(T.uint8)
+
+    def scales(n):
+        return T.rand((n,), generator=gen, device="cuda") * 1e-3 + 1e-4
+
+    fp8_ranks = [((codes(Fl, D), scales(Fl)), (codes(Fl, D), scales(Fl)),
+                  (codes(D, Fl), scales(D))) for _ in range(TP)]
+    for I in (1, 8):
+        X = to_dev(T, datagen.gaussian("X", (I, D), 1.0, "bf16", 1100 + I))
+        H = T.empty((I, Fl), dtype=T.bfloat16, device="cuda")
+        P = T.empty((I, D), dtype=T.float32, device="cuda")
+        fns = [(lambda w=w: tp.shard_mlp_fp8(X, *w, H, P)) for w in fp8_ranks]
+        st = stats(time_calls(T, fns, calls))
+        nbytes = 3 * D * Fl + 4 * (2 * Fl + D) + 2 * I * D + 4 * I * D
+        gbs = nbytes / (st["median_us"] * 1e-6) / 1e9
+        log(f"FP8 MLP TP=8 decode I={I}: {st['median_us']} us")
+        out[f"llama70b_mlp_fp8_tp8_decode_I{I}"] = dict(
+            **st, bytes_per_call=nbytes, GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM, 3),
+            tokens_per_s=round(I / (st["median_us"] * 1e-6)))
+    del fp8_ranks
     # the attention projections of the layer's rank shares at decode 32
     I = 32
     nql, nkl = NQ // TP, NKV // TP

@@ -39,6 +39,7 @@ SIGNATURES = {
                                           ctypes.c_int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "tp_partial_reduce": (ctypes.c_int, [_i32, _i64, _vp, ctypes.c_int, _vp, _vp]),
     "tp_attn_core": (ctypes.c_int, [_i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "tp_shard_mlp_fp8": (ctypes.c_int, [_i64, _i64, _i64] + [_vp] * 10),
     "tp_residual_rmsnorm": (ctypes.c_int, [_i32, _i64, _i64, _vp, _vp, ctypes.c_int, _vp, _vp,
                                            ctypes.c_int, _vp, ctypes.c_float, _vp]),
 }
@@ -215,6 +216,30 @@ def partial_reduce(partials, Y, stream=None) -> None:
         raise ValueError("Y must hold one partial's elements")
     _check("tp_partial_reduce", lib().tp_partial_reduce(t, n, _ptr(partials), _dt(Y), _ptr(Y),
                                                         _stream(stream, dev)))
+
+
+def shard_mlp_fp8(X, gate, up, down, H, P, stream=None) -> None:
+    """Weight-only FP8 MLP rank share for decode (I <= 8): gate, up, down are
+    (codes uint8, scales float32) pairs -- gate/up codes [F_local, D] with
+    scales [F_local], down codes [D, F_local] with scales [D]; X and H bf16,
+    P float32."""
+    torch = _torch()
+    (Wg, sg), (Wu, su), (Wd, sd) = gate, up, down
+    dev = _dev(X, Wg, sg, Wu, su, Wd, sd, H, P)
+    I, D = X.shape
+    F_local = Wg.shape[0]
+    if X.dtype != torch.bfloat16 or H.dtype != torch.bfloat16 or P.dtype != torch.float32:
+        raise TypeError("X and H bfloat16, P float32")
+    for W, s_, shape in ((Wg, sg, (F_local, D)), (Wu, su, (F_local, D)), (Wd, sd, (D, F_local))):
+        if W.dtype != torch.uint8 or tuple(W.shape) != shape:
+            raise ValueError(f"FP8 codes must be uint8 {shape}")
+        if s_.dtype != torch.float32 or s_.numel() != shape[0]:
+            raise ValueError("scales must be float32, one per output row")
+    if tuple(H.shape) != (I, F_local) or tuple(P.shape) != (I, D):
+        raise ValueError("H [I, F_local], P [I, D]")
+    _check("tp_shard_mlp_fp8", lib().tp_shard_mlp_fp8(
+        I, D, F_local, _ptr(X), _ptr(Wg), _ptr(sg), _ptr(Wu), _ptr(su), _ptr(Wd), _ptr(sd),
+        _ptr(H), _ptr(P), _stream(stream, dev)))
 
 
 def residual_rmsnorm(partials, residual, h, gamma=None, x=None, eps: float = 1e-5,

@@ -61,34 +61,6 @@ __device__ __forceinline__ void store_dt<float>(void* out, int64_t idx, float v)
   static_cast<float*>(out)[idx] = v;
 }
 
-// Sum V values per lane over the 64 lanes of a wavefront.  Afterwards lane l
-// holds the total of value index l / (64 / V) in v[0].  Step S exchanges
-// half of the CNT = V >> (S+1) live values with the lane 32 >> S away.
-template <int V, int S>
-__device__ __forceinline__ void wave_fold_step(float (&v)[V], int lane) {
-  constexpr int CNT = V >> (S + 1);
-  if constexpr (CNT >= 1) {
-    constexpr int M = 32 >> S;
-    const bool upper = (lane & M) != 0;
-#pragma unroll
-    for (int q = 0; q < CNT; ++q) {
-      const float send = upper ? v[q] : v[q + CNT];
-      const float keep = upper ? v[q + CNT] : v[q];
-      v[q] = keep + __shfl_xor(send, M, 64);
-    }
-    wave_fold_step<V, S + 1>(v, lane);
-  } else {
-#pragma unroll
-    for (int m = 32 >> S; m >= 1; m >>= 1) v[0] += __shfl_xor(v[0], m, 64);
-  }
-}
-
-template <int V>
-__device__ __forceinline__ void wave_fold(float (&v)[V], int lane) {
-  static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V must be a power of two <= 64");
-  wave_fold_step<V, 0>(v, lane);
-}
-
 // X  [I, K] (row stride ldx elements), W0/W1 [N, K] (W1: up matrix, SwiGLU only)
 // out [I, N] (row stride ldo elements): fp32 (EPI_F32) or T.
 template <typename T, int NI, int J, int R, int EPI>

@@ -29,6 +29,17 @@ template <typename T, int EPI>
 hipError_t gemv_launch(int I, int K, int N, const T* X, int64_t ldx, const T* W0,
                        const T* W1, void* out, int64_t ldo, hipStream_t stream);
 
+// Weight-only FP8 few-token product: y[i, n] = S[n] * sum_k X[i, k] e4m3(W[n, k]),
+// X bf16, W one OCP E4M3 byte per weight, S fp32 per row (EPI_F32 or
+// EPI_SWIGLU with W1/S1 the up matrix); I <= 8, K a multiple of 16 and at
+// most kFp8MaxK.
+constexpr int kFp8MaxTokens = 8;
+constexpr int64_t kFp8MaxK = 16384;
+template <int EPI>
+hipError_t gemv_fp8_launch(int I, int K, int N, const uint16_t* X, const uint8_t* W0,
+                           const float* S0, const uint8_t* W1, const float* S1, void* out,
+                           int64_t ldo, hipStream_t stream);
+
 // Same product on bf16 MFMA for 9..64 tokens, weights streamed once from HBM,
 // K split over workgroups; `workspace` (splitk_workspace_bytes) holds the
 // arrival counters and the fp32 partial sums (layout above).

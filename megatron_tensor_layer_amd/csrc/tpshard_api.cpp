@@ -227,6 +227,41 @@ tp_status_t tp_partial_reduce(int32_t t, int64_t n, const float* partials, tp_dt
   return launched(tpk::reduce_launch(t, n, partials, out_dt == TP_BF16, Y, s));
 }
 
+tp_status_t tp_shard_mlp_fp8(int64_t I, int64_t D, int64_t F_local, const void* X,
+                             const void* W_gate, const float* s_gate, const void* W_up,
+                             const float* s_up, const void* W_down, const float* s_down,
+                             void* H, float* P, void* stream) {
+  if (I < 0 || !dims_ok(D) || !dims_ok(F_local)) return TP_ERR_INVALID;
+  if (I == 0) return TP_OK;
+  if (!X || !W_gate || !s_gate || !W_up || !s_up || !W_down || !s_down || !H || !P)
+    return TP_ERR_INVALID;
+  if ((D % 16) || (F_local % 16)) return TP_ERR_MISALIGNED;
+  if (I > tpk::kFp8MaxTokens || D > tpk::kFp8MaxK || F_local > tpk::kFp8MaxK)
+    return TP_ERR_UNSUPPORTED;
+  for (const void* p : {X, W_gate, W_up, W_down, static_cast<const void*>(H),
+                        static_cast<const void*>(P)})
+    if (!aligned16(p)) return TP_ERR_MISALIGNED;
+  for (const float* p : {s_gate, s_up, s_down})
+    if (reinterpret_cast<uintptr_t>(p) & 3u) return TP_ERR_MISALIGNED;
+  const Range rX = rng(X, I * D * 2), rG = rng(W_gate, F_local * D), rU = rng(W_up, F_local * D),
+              rD = rng(W_down, D * F_local), rsg = rng(s_gate, F_local * 4),
+              rsu = rng(s_up, F_local * 4), rsd = rng(s_down, D * 4),
+              rH = rng(H, I * F_local * 2), rP = rng(P, I * D * 4);
+  for (Range in : {rX, rG, rU, rD, rsg, rsu, rsd})
+    if (overlap(rH, in) || overlap(rP, in)) return TP_ERR_INVALID;
+  if (overlap(rH, rP)) return TP_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  auto Xb = static_cast<const uint16_t*>(X);
+  hipError_t e = tpk::gemv_fp8_launch<tpk::EPI_SWIGLU>(
+      (int)I, (int)D, (int)F_local, Xb, static_cast<const uint8_t*>(W_gate), s_gate,
+      static_cast<const uint8_t*>(W_up), s_up, H, F_local, s);
+  if (e != hipSuccess) return TP_ERR_LAUNCH;
+  return launched(tpk::gemv_fp8_launch<tpk::EPI_F32>(
+      (int)I, (int)F_local, (int)D, static_cast<const uint16_t*>(H),
+      static_cast<const uint8_t*>(W_down), s_down, nullptr, nullptr, P, D, s));
+}
+
 tp_status_t tp_residual_rmsnorm(int32_t t, int64_t I, int64_t D, const float* partials,
                                 const void* residual, tp_dtype_t h_dt, void* h,
                                 const void* gamma, tp_dtype_t x_dt, void* x, float eps,

@@ -44,6 +44,7 @@ TENSOR_IDS = {
     "P": 9,        # stand-alone row-parallel partials [t, I, D] (reduce / norm cases)
     "h": 10,       # residual stream [I, D]
     "gamma": 11,   # RMSNorm scale [D]: 1 + N(0, sigma^2), near 1 like trained scales
+    "W_gate8": 12, "W_up8": 13, "W_down8": 14,  # FP8 weight-only MLP shards
 }
 
 _CHUNK = 1 << 24  # elements per draw, bounds the temporaries of the rounding
@@ -156,3 +157,46 @@ def rmsnorm_gamma(D: int, pool: int, dtype: str = "f32", sigma: float = 0.1) -> 
     if dtype == "bf16":
         _round_to_bf16_inplace(g)
     return g
+
+
+# Non-negative finite OCP E4M3 ("fn") values, in code order 0x00..0x7E (code
+# order is value order); used only to encode synthetic weights.
+_E4M3_POS = np.array([(m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+                      for e in range(16) for m in range(8)][:0x7F])
+
+
+def fp8_weights(name: str, shape, sigma: float, pool: int):
+    """Synthetic FP8 weight-only storage of an [N, K] matrix: N(0, sigma^2)
+    weights, one fp32 scale per row (row absmax / 448, the largest E4M3
+    value) and each weight / scale encoded as the nearest E4M3 code (ties to
+    the even code).  Returns (codes uint8 [N, K], scales float32 [N])."""
+    w = gaussian(name, shape, sigma, "f32", pool).astype(np.float64)
+    amax = np.abs(w).max(axis=1)
+    scales = (np.where(amax > 0, amax, 1.0) / 448.0).astype(np.float32)
+    q = np.abs(w) / scales.astype(np.float64)[:, None]
+    hi = np.clip(np.searchsorted(_E4M3_POS, q), 1, 0x7E)
+    lo = hi - 1
+    dlo, dhi = q - _E4M3_POS[lo], _E4M3_POS[hi] - q
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    codes = np.where(pick_hi, hi, lo).astype(np.uint8)
+    codes |= np.where(w < 0, 0x80, 0).astype(np.uint8)
+    return codes, scales
+
+
+def fp8_mlp_weights(D: int, F: int, pool: int):
+    """FP8 storage of a full MLP: (gate, up [F, D], down [D, F]) as
+    (codes, scales) pairs, weights N(0, 1/D)."""
+    sigma = D ** -0.5
+    return (fp8_weights("W_gate8", (F, D), sigma, pool),
+            fp8_weights("W_up8", (F, D), sigma, pool),
+            fp8_weights("W_down8", (D, F), sigma, pool))
+
+
+def fp8_mlp_rank_shards(fp8_full, t: int, r: int):
+    """Rank r's contiguous F block of FP8 MLP storage: gate/up rows and down
+    columns (the down scales are per output row, so they are shared)."""
+    (cg, sg), (cu, su), (cd, sd) = fp8_full
+    blk = rank_block(cg.shape[0], t, r)
+    return ((np.ascontiguousarray(cg[blk]), sg[blk].copy()),
+            (np.ascontiguousarray(cu[blk]), su[blk].copy()),
+            (np.ascontiguousarray(cd[:, blk]), sd.copy()))

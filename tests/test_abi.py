@@ -143,6 +143,25 @@ def test_residual_rmsnorm_validation(lib):
     assert n(2, 2, 64, P, R, F, ctypes.c_void_p(FAKE + 128), G, B, X, eps, None) == INVALID  # h in partials
 
 
+def test_mlp_fp8_validation(lib):
+    m = lib.tp_shard_mlp_fp8
+    args = [fake(k) for k in range(10)]  # X, Wg, sg, Wu, su, Wd, sd, H, P, stream
+    args[9] = None
+    assert m(0, 64, 128, *args) == OK
+    assert m(-1, 64, 128, *args) == INVALID
+    assert m(9, 64, 128, *args) == UNSUPPORTED                       # decode only: I <= 8
+    assert m(1, 24, 128, *args) == MISALIGNED                        # D not a multiple of 16
+    assert m(1, 32768, 128, *args) == UNSUPPORTED                    # K above 16384
+    bad = list(args)
+    bad[2] = None
+    assert m(1, 64, 128, *bad) == INVALID                            # missing scale
+    bad[2] = ctypes.c_void_p(FAKE + 2 * STEP + 2)
+    assert m(1, 64, 128, *bad) == MISALIGNED                         # scale not 4-byte aligned
+    bad = list(args)
+    bad[7] = ctypes.c_void_p(FAKE + 16)                              # H inside X
+    assert m(1, 64, 128, *bad) == INVALID
+
+
 def test_workspace_queries_are_host_only(lib):
     # calls that split K (9..64 tokens on the streaming kernel, up to 256 on
     # the tiled one) need counters + fp32 partials; few-token calls and

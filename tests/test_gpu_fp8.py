@@ -1,0 +1,101 @@
+"""GPU parity of tp_shard_mlp_fp8 (weight-only FP8 storage, OCP E4M3 with a
+fp32 scale per output row; bf16 activations) against the fp64 oracle on the
+dequantized weights.  Bar: normwise 2e-2 (bf16 inputs and H, fp32 sums)."""
+import numpy as np
+import pytest
+
+import megatron_tensor_layer_amd as tp
+from megatron_tensor_layer_amd import datagen
+from tests.common import normwise_err
+from tests.gpu_util import empty, to_dev, to_host, torch
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+
+
+def _dev_fp8(pair):
+    T = torch()
+    codes, scales = pair
+    return (T.from_numpy(np.ascontiguousarray(codes)).cuda(),
+            T.from_numpy(np.ascontiguousarray(scales, dtype=np.float32)).cuda())
+
+
+def _run(X, shards):
+    I, D = X.shape
+    F_local = shards[0][0].shape[0]
+    H = empty((I, F_local), "bf16")
+    P = empty((I, D), "f32")
+    tp.shard_mlp_fp8(to_dev(X, "bf16"), *(_dev_fp8(s) for s in shards), H, P)
+    torch().cuda.synchronize()
+    return to_host(H), to_host(P)
+
+
+def _reference(orc, X, shards):
+    (cg, sg), (cu, su), (cd, sd) = shards
+    return orc.mlp_full(X, orc.dequant_fp8(cg, sg), orc.dequant_fp8(cu, su),
+                        orc.dequant_fp8(cd, sd))
+
+
+def _shards(D, Fl, pool):
+    return (datagen.fp8_weights("W_gate8", (Fl, D), D ** -0.5, pool),
+            datagen.fp8_weights("W_up8", (Fl, D), D ** -0.5, pool),
+            datagen.fp8_weights("W_down8", (D, Fl), D ** -0.5, pool))
+
+
+@pytest.fixture(scope="module")
+def llama_fp8():
+    return _shards(8192, 3584, 60)
+
+
+@pytest.mark.parametrize("I", [1, 2, 4, 8])
+def test_llama_rank_share_decode(orc, llama_fp8, I):
+    """One Llama-3.1-70B TP=8 MLP rank share (D = 8192, F_local = 3584)."""
+    D = 8192
+    shards = llama_fp8
+    X = datagen.gaussian("X", (I, D), 1.0, "bf16", 600 + I)
+    H, P = _run(X, shards)
+    H_ref, P_ref = _reference(orc, X, shards)
+    assert normwise_err(H, H_ref) <= TOL
+    assert normwise_err(P, P_ref) <= TOL
+
+
+@pytest.mark.parametrize("I", [1, 8])
+def test_qwen_tp2_partials_sum_to_layer(orc, I):
+    """Qwen2.5-1.5B MLP (D = 1536, F = 8960) at TP=2: each rank's FP8 share
+    against the oracle, and the two partials sum to the unsharded layer."""
+    D, F, t = 1536, 8960, 2
+    full = datagen.fp8_mlp_weights(D, F, 61)
+    X = datagen.gaussian("X", (I, D), 1.0, "bf16", 610 + I)
+    Ps = []
+    for r in range(t):
+        shards = datagen.fp8_mlp_rank_shards(full, t, r)
+        H, P = _run(X, shards)
+        H_ref, P_ref = _reference(orc, X, shards)
+        assert normwise_err(H, H_ref) <= TOL
+        assert normwise_err(P, P_ref) <= TOL
+        Ps.append(P)
+    _, Y_ref = _reference(orc, X, full)
+    assert normwise_err(Ps[0] + Ps[1], Y_ref) <= TOL
+
+
+@pytest.mark.parametrize("I,D,Fl", [(3, 16, 16), (5, 48, 80), (8, 1040, 272), (1, 16384, 16)])
+def test_small_and_ragged_shapes(orc, I, D, Fl):
+    """K of one 16-byte chunk, chunks not filling a wave, two chunks per lane."""
+    shards = _shards(D, Fl, 62)
+    X = datagen.gaussian("X", (I, D), 1.0, "bf16", 620 + I)
+    H, P = _run(X, shards)
+    H_ref, P_ref = _reference(orc, X, shards)
+    assert normwise_err(H, H_ref) <= TOL
+    assert normwise_err(P, P_ref) <= TOL
+
+
+def test_deterministic_and_unsupported(orc):
+    D, Fl = 1536, 4480
+    shards = _shards(D, Fl, 63)
+    X = datagen.gaussian("X", (8, D), 1.0, "bf16", 630)
+    a, b = _run(X, shards), _run(X, shards)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    X9 = to_dev(datagen.gaussian("X", (9, D), 1.0, "bf16", 631), "bf16")
+    with pytest.raises(tp.TPError, match="UNSUPPORTED"):
+        tp.shard_mlp_fp8(X9, *(_dev_fp8(s) for s in shards), empty((9, Fl), "bf16"),
+                         empty((9, D), "f32"))
