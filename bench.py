@@ -389,6 +389,24 @@ def detail(torch, tp, layer, calls):
         gbs = wl.ResidualNormShape(TP, I, D).bytes() / (st["median_us"] * 1e-6) / 1e9
         out[f"residual_rmsnorm_t8_I{I}"] = dict(**st, GBps=round(gbs, 1),
                                                 frac_hbm=round(gbs / PEAK_HBM, 3))
+    # the sequence-parallel form at prefill 512: 8 ranks' reduce-scatter + norm
+    # on their 64 rows each, x gathered in place into one [512, D] buffer
+    I = 512
+    Pp = T.randn((TP, I, D), device="cuda")
+    h = to_dev(T, datagen.gaussian("h", (I, D), 1.0, "bf16", 4512))
+    x = T.empty((I, D), dtype=T.bfloat16, device="cuda")
+    g = layer.gammas[1]
+    Is = I // TP
+
+    def sp_all():
+        for r in range(TP):
+            sl = slice(r * Is, (r + 1) * Is)
+            tp.reduce_scatter_rmsnorm(Pp, r, h[sl], h[sl], g, x[sl])
+
+    st = stats(time_calls(T, [sp_all], calls // 2))
+    gbs = wl.ResidualNormShape(TP, I, D).bytes() / (st["median_us"] * 1e-6) / 1e9
+    out["sequence_parallel_norm_t8_I512_all_ranks"] = dict(**st, GBps=round(gbs, 1),
+                                                           frac_hbm=round(gbs / PEAK_HBM, 3))
     # the layer as a pre-norm block (RMSNorm, attention block, residual + RMSNorm,
     # MLP, residual + RMSNorm), decode 32
     I = 32

@@ -197,6 +197,29 @@ tp_status_t tp_residual_rmsnorm(int32_t t, int64_t I, int64_t D, const float* pa
                                 void* stream);
 
 /*
+ * The sequence-parallel form of tp_residual_rmsnorm ([L4] §4.5): the
+ * all-reduce after a row-parallel block becomes a reduce-scatter -- rank
+ * `rank` of t receives the sum of the t partials for its own I/t token rows
+ * -- followed by the residual update and RMSNorm on those rows only, and an
+ * all-gather of x before the next column-parallel projection.  This call is
+ * rank `rank`'s reduce-scatter plus norm, with the t partials all on this
+ * device:
+ *   rows     i in [rank*I/t, (rank+1)*I/t)  (t must divide I)
+ *   partials [t, I, D] fp32, the full partials of every rank
+ *   residual [I/t, D] h_dt, this rank's rows of the residual stream, or NULL
+ *   h        [I/t, D] h_dt out; may be the residual pointer itself
+ *   gamma    [D] x_dt, x [I/t, D] x_dt out (both NULL: h only); point x at
+ *            row rank*I/t of a full [I, D] buffer and, over all ranks, the
+ *            buffer holds the all-gathered x
+ * Same values as tp_residual_rmsnorm on those rows.  D a multiple of 8, at
+ * most 32768.  Errors as tp_residual_rmsnorm.
+ */
+tp_status_t tp_reduce_scatter_rmsnorm(int32_t t, int32_t rank, int64_t I, int64_t D,
+                                      const float* partials, const void* residual,
+                                      tp_dtype_t h_dt, void* h, const void* gamma,
+                                      tp_dtype_t x_dt, void* x, float eps, void* stream);
+
+/*
  * Attention core of one rank (test support, not a projection): each rank
  * computes its own heads' attention completely ([L4] §4.2).  Scaled dot
  * product (scale 1/sqrt(head_dim)), causal inside each sequence, no rotary

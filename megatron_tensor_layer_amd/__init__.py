@@ -39,6 +39,9 @@ SIGNATURES = {
                                           ctypes.c_int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "tp_partial_reduce": (ctypes.c_int, [_i32, _i64, _vp, ctypes.c_int, _vp, _vp]),
     "tp_attn_core": (ctypes.c_int, [_i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "tp_reduce_scatter_rmsnorm": (ctypes.c_int, [_i32, _i32, _i64, _i64, _vp, _vp, ctypes.c_int,
+                                                 _vp, _vp, ctypes.c_int, _vp, ctypes.c_float,
+                                                 _vp]),
     "tp_shard_mlp_fp8": (ctypes.c_int, [_i64, _i64, _i64] + [_vp] * 10),
     "tp_residual_rmsnorm": (ctypes.c_int, [_i32, _i64, _i64, _vp, _vp, ctypes.c_int, _vp, _vp,
                                            ctypes.c_int, _vp, ctypes.c_float, _vp]),
@@ -271,6 +274,35 @@ def residual_rmsnorm(partials, residual, h, gamma=None, x=None, eps: float = 1e-
         t, I, D, _ptr(partials) if partials is not None else None,
         _ptr(residual) if residual is not None else None, _dt(h), _ptr(h),
         _ptr(gamma) if gamma is not None else None, x_dt,
+        _ptr(x) if x is not None else None, float(eps), _stream(stream, dev)))
+
+
+def reduce_scatter_rmsnorm(partials, rank: int, residual, h, gamma=None, x=None,
+                           eps: float = 1e-5, stream=None) -> None:
+    """Sequence-parallel rank `rank`: rows [rank*I/t, (rank+1)*I/t) of
+    h = residual + sum_r partials[r], then x = RMSNorm(h) * gamma.  partials
+    [t, I, D] float32; residual, h, x [I/t, D] (x may be a row slice of a full
+    [I, D] buffer: over all ranks it then holds the all-gathered x)."""
+    torch = _torch()
+    tensors = [a for a in (partials, residual, h, gamma, x) if a is not None]
+    dev = _dev(*tensors)
+    if partials.dtype != torch.float32 or partials.dim() != 3:
+        raise ValueError("partials must be float32 [t, I, D]")
+    t, I, D = partials.shape
+    if tuple(h.shape) != (I // t, D):
+        raise ValueError("h must be [I/t, D]")
+    if residual is not None and (residual.dtype != h.dtype or residual.shape != h.shape):
+        raise ValueError("residual must match h")
+    if (gamma is None) != (x is None):
+        raise ValueError("gamma and x go together")
+    x_dt = TP_F32
+    if x is not None:
+        if x.dtype != gamma.dtype or x.shape != h.shape or gamma.numel() != D:
+            raise ValueError("x [I/t, D] and gamma [D] must share a dtype")
+        x_dt = _dt(x)
+    _check("tp_reduce_scatter_rmsnorm", lib().tp_reduce_scatter_rmsnorm(
+        t, rank, I, D, _ptr(partials), _ptr(residual) if residual is not None else None,
+        _dt(h), _ptr(h), _ptr(gamma) if gamma is not None else None, x_dt,
         _ptr(x) if x is not None else None, float(eps), _stream(stream, dev)))
 
 

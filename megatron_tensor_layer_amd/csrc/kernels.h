@@ -68,11 +68,13 @@ hipError_t reduce_launch(int t, int64_t n, const float* P, bool out_bf16, void* 
                          hipStream_t stream);
 
 // h = residual + sum_r P_r (rank order), then x = RMSNorm(h as stored) * gamma
-// (x == nullptr: h only); one workgroup per row, D <= kNormMaxD.
+// (x == nullptr: h only) for I rows; one workgroup per row, D <= kNormMaxD.
+// P points at the first of the I rows in rank 0's partial; each rank's
+// partial holds p_rows rows (I for full rows, more for a sequence shard).
 constexpr int kNormMaxD = 32768;
-hipError_t residual_rmsnorm_launch(int t, int I, int D, const float* P, const void* residual,
-                                   bool h_bf16, void* h, const void* gamma, bool x_bf16, void* x,
-                                   float eps, hipStream_t stream);
+hipError_t residual_rmsnorm_launch(int t, int I, int D, const float* P, int64_t p_rows,
+                                   const void* residual, bool h_bf16, void* h, const void* gamma,
+                                   bool x_bf16, void* x, float eps, hipStream_t stream);
 
 hipError_t attn_core_launch(int I, int S, int nq, int nkv, int hd, const uint16_t* qkv,
                             uint16_t* A, hipStream_t stream);

@@ -98,11 +98,11 @@ residual_rmsnorm_kernel(int t, int D, const float* __restrict__ P, const void* r
 
 }  // namespace
 
-hipError_t residual_rmsnorm_launch(int t, int I, int D, const float* P, const void* residual,
-                                   bool h_bf16, void* h, const void* gamma, bool x_bf16, void* x,
-                                   float eps, hipStream_t stream) {
+hipError_t residual_rmsnorm_launch(int t, int I, int D, const float* P, int64_t p_rows,
+                                   const void* residual, bool h_bf16, void* h, const void* gamma,
+                                   bool x_bf16, void* x, float eps, hipStream_t stream) {
   const int c4 = D / 4;
-  const int64_t plane4 = (int64_t)I * c4;
+  const int64_t plane4 = p_rows * c4;  // one rank's partial, in float4
   const int cpt = (c4 + kThreads - 1) / kThreads;
 #define TPK_LAUNCH(N)                                                                            \
   hipLaunchKernelGGL(residual_rmsnorm_kernel<N>, dim3(I), dim3(kThreads), 0, stream, t, D, P,    \

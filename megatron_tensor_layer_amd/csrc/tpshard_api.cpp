@@ -290,9 +290,43 @@ tp_status_t tp_residual_rmsnorm(int32_t t, int64_t I, int64_t D, const float* pa
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  return launched(tpk::residual_rmsnorm_launch(t, (int)I, (int)D, partials, residual,
+  return launched(tpk::residual_rmsnorm_launch(t, (int)I, (int)D, partials, I, residual,
                                                h_dt == TP_BF16, h, gamma, x_dt == TP_BF16, x,
                                                eps, s));
+}
+
+tp_status_t tp_reduce_scatter_rmsnorm(int32_t t, int32_t rank, int64_t I, int64_t D,
+                                      const float* partials, const void* residual,
+                                      tp_dtype_t h_dt, void* h, const void* gamma,
+                                      tp_dtype_t x_dt, void* x, float eps, void* stream) {
+  if (t < 1 || rank < 0 || rank >= t || I < 0 || I > INT32_MAX || !dims_ok(D) ||
+      !dtype_ok(h_dt) || !dtype_ok(x_dt))
+    return TP_ERR_INVALID;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return TP_ERR_INVALID;
+  if (I % t) return TP_ERR_INVALID;  // the sequence splits evenly over the ranks
+  if (I == 0) return TP_OK;
+  if (!partials || !h || (!gamma) != (!x)) return TP_ERR_INVALID;
+  if (D % 8) return TP_ERR_MISALIGNED;
+  if (D > tpk::kNormMaxD) return TP_ERR_UNSUPPORTED;
+  for (const void* p : {static_cast<const void*>(partials), residual, static_cast<const void*>(h),
+                        gamma, static_cast<const void*>(x)})
+    if (p && !aligned16(p)) return TP_ERR_MISALIGNED;
+  const int64_t Is = I / t, ns = Is * D;
+  const Range rP = rng(partials, (int64_t)t * I * D * 4),
+              rR = rng(residual, residual ? ns * esize(h_dt) : 0), rH = rng(h, ns * esize(h_dt)),
+              rG = rng(gamma, gamma ? D * esize(x_dt) : 0), rX = rng(x, x ? ns * esize(x_dt) : 0);
+  if (overlap(rH, rP)) return TP_ERR_INVALID;
+  if (residual && residual != h && overlap(rH, rR)) return TP_ERR_INVALID;
+  if (x) {
+    for (Range o : {rP, rR, rH, rG})
+      if (overlap(rX, o)) return TP_ERR_INVALID;
+    if (overlap(rH, rG)) return TP_ERR_INVALID;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  return launched(tpk::residual_rmsnorm_launch(t, (int)Is, (int)D, partials + rank * ns, I,
+                                               residual, h_dt == TP_BF16, h, gamma,
+                                               x_dt == TP_BF16, x, eps, s));
 }
 
 tp_status_t tp_attn_core(int64_t I, int64_t S, int64_t n_q_local, int64_t n_kv_local,

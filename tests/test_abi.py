@@ -143,6 +143,19 @@ def test_residual_rmsnorm_validation(lib):
     assert n(2, 2, 64, P, R, F, ctypes.c_void_p(FAKE + 128), G, B, X, eps, None) == INVALID  # h in partials
 
 
+def test_reduce_scatter_rmsnorm_validation(lib):
+    n = lib.tp_reduce_scatter_rmsnorm
+    F = tp.TP_F32
+    eps = ctypes.c_float(1e-5)
+    P, R, H, G, X = (fake(k) for k in range(5))
+    assert n(4, 0, 0, 64, P, R, F, H, G, F, X, eps, None) == OK
+    assert n(4, 4, 8, 64, P, R, F, H, G, F, X, eps, None) == INVALID   # rank out of range
+    assert n(0, 0, 8, 64, P, R, F, H, G, F, X, eps, None) == INVALID   # no ranks
+    assert n(3, 0, 8, 64, P, R, F, H, G, F, X, eps, None) == INVALID   # t does not divide I
+    assert n(4, 1, 8, 64, None, R, F, H, G, F, X, eps, None) == INVALID
+    assert n(4, 1, 8, 60, P, R, F, H, G, F, X, eps, None) == MISALIGNED
+
+
 def test_mlp_fp8_validation(lib):
     m = lib.tp_shard_mlp_fp8
     args = [fake(k) for k in range(10)]  # X, Wg, sg, Wu, su, Wd, sd, H, P, stream

@@ -79,3 +79,29 @@ def test_residual_rmsnorm_errors_touch_nothing():
                             to_dev(np.ones(64, np.float32), "f32"), h, 1e-5)  # x == h
     T.cuda.synchronize()
     assert np.array_equal(to_host(h), before, equal_nan=True)
+
+
+@pytest.mark.parametrize("t,I,D,h_dt", [(8, 512, 8192, "bf16"), (2, 64, 1536, "f32"),
+                                        (4, 4, 264, "bf16")])
+def test_sequence_parallel_reduce_scatter_norm_allgather(orc, t, I, D, h_dt):
+    """Each rank's reduce-scatter + norm on its I/t rows, x written into its
+    rows of one [I, D] buffer (the all-gather): the same bits as the
+    all-reduce form, and the oracle's values."""
+    P, R, g = _inputs(t, I, D, h_dt, "bf16", 900 + t)
+    T = torch()
+    Pd, gd = to_dev(P, "f32"), to_dev(g, "bf16")
+    Is = I // t
+    h_sp = to_dev(R, h_dt)
+    x_sp = empty((I, D), "bf16")
+    for r in range(t):
+        tp.reduce_scatter_rmsnorm(Pd, r, h_sp[r * Is:(r + 1) * Is], h_sp[r * Is:(r + 1) * Is],
+                                  gd, x_sp[r * Is:(r + 1) * Is], 1e-5)
+    h_ar = to_dev(R, h_dt)
+    x_ar = empty((I, D), "bf16")
+    tp.residual_rmsnorm(Pd, h_ar, h_ar, gd, x_ar, 1e-5)
+    T.cuda.synchronize()
+    assert T.equal(h_sp, h_ar) and T.equal(x_sp, x_ar)
+    h_ref, x_ref = orc.residual_rmsnorm(P, R, g, 1e-5)
+    assert normwise_err(to_host(h_sp), h_ref) <= (1e-5 if h_dt == "f32" else 2e-2)
+    assert normwise_err(to_host(x_sp), x_ref) <= 2e-2
+

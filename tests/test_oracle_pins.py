@@ -359,6 +359,25 @@ def pin_fp8_dequant_rows(orc):
     assert np.array_equal(W, ref)
 
 
+def pin_sequence_shards_concatenate(orc):
+    """Sequence parallelism (reduce-scatter, norm on each rank's rows,
+    all-gather) gives the all-reduce layout's values: the residual update and
+    RMSNorm act row by row, so rank blocks of rows concatenate bit for bit."""
+    rng = np.random.default_rng(5)
+    t, I, D = 4, 8, 12
+    P = rng.standard_normal((t, I, D))
+    R = rng.standard_normal((I, D))
+    g = rng.uniform(0.5, 1.5, D)
+    h, x = orc.residual_rmsnorm(P, R, g, 1e-5)
+    hs, xs = [], []
+    for r in range(t):
+        rows = slice(r * I // t, (r + 1) * I // t)
+        a, b = orc.residual_rmsnorm(P[:, rows], R[rows], g, 1e-5)
+        hs.append(a)
+        xs.append(b)
+    assert np.array_equal(np.concatenate(hs), h) and np.array_equal(np.concatenate(xs), x)
+
+
 ALL_PINS = [
     pin_silu_closed_forms,
     pin_mlp_bruteforce_exact,
@@ -376,6 +395,7 @@ ALL_PINS = [
     pin_rmsnorm_closed_forms,
     pin_fp8_decode,
     pin_fp8_dequant_rows,
+    pin_sequence_shards_concatenate,
 ]
 
 
