@@ -60,6 +60,8 @@ class Oracle:
         lib.orc_attn_core.argtypes = [_i64] * 5 + [_pd] * 2
         lib.orc_oproj_rank.restype = None
         lib.orc_oproj_rank.argtypes = [_i64] * 6 + [_pd] * 3
+        lib.orc_attn_decode.restype = None
+        lib.orc_attn_decode.argtypes = [_i64] * 5 + [ctypes.POINTER(ctypes.c_int)] + [_pd] * 4
         lib.orc_e4m3.restype = ctypes.c_double
         lib.orc_e4m3.argtypes = [ctypes.c_ubyte]
         lib.orc_dequant_fp8.restype = None
@@ -146,6 +148,19 @@ class Oracle:
         self.lib.orc_oproj_rank(I, D, n_q, hd, t, r, self._p(A_r), self._p(Wo),
                                 self._p(P))
         return P
+
+    def attn_decode(self, qkv, Kc, Vc, lens, nq_l: int, nkv_l: int, hd: int) -> np.ndarray:
+        """Decode attention over the KV cache: positions < lens[b]-1 from Kc/Vc
+        [B, nkv_l, Lmax, hd], position lens[b]-1 from the new token's k, v in qkv."""
+        Q, K, V = self._f64(qkv), self._f64(Kc), self._f64(Vc)
+        B, _, Lmax, _ = K.shape
+        ln = np.ascontiguousarray(lens, dtype=np.int32)
+        assert ln.min() >= 1 and ln.max() <= Lmax
+        A = np.empty((B, nq_l * hd))
+        self.lib.orc_attn_decode(B, nq_l, nkv_l, hd, Lmax,
+                                 ln.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), self._p(Q),
+                                 self._p(K), self._p(V), self._p(A))
+        return A
 
     # ------------------------------------------------------------ chains
     def attn_block_rank(self, X, Wq, Wk, Wv, Wo, n_q, n_kv, hd, S, t=1, r=0):

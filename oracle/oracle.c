@@ -254,3 +254,52 @@ void orc_dequant_fp8(int64_t N, int64_t K, const unsigned char *codes, const dou
   for (int64_t n = 0; n < N; ++n)
     for (int64_t k = 0; k < K; ++k) W[n * K + k] = scales[n] * orc_e4m3(codes[n * K + k]);
 }
+
+/*
+ * Decode attention of one rank over its KV cache, lecture §4.4: the cache is
+ * split with the heads, each rank storing and reading only the KV groups of
+ * its own query heads (a group is stored on every rank that needs it once
+ * the ranks outnumber the groups).  Sequence b has lens[b] positions: 0 ..
+ * lens[b]-2 are in the cache, lens[b]-1 is the new token, whose k and v come
+ * from the QKV projection's output.  Local head j reads local group
+ * floor(j nkv / nq); scores are scaled by 1/sqrt(hd), softmax over all
+ * lens[b] positions (no mask: every position is in the past).
+ *   qkv  [B, (nq + 2 nkv) hd]   columns [q heads | k heads | v heads]
+ *   Kc   [B, nkv, Lmax, hd], Vc [B, nkv, Lmax, hd]
+ *   A    [B, nq hd]
+ */
+void orc_attn_decode(int64_t B, int64_t nq, int64_t nkv, int64_t hd, int64_t Lmax,
+                     const int *lens, const double *qkv, const double *Kc, const double *Vc,
+                     double *A) {
+  const int64_t N = (nq + 2 * nkv) * hd;
+  const double scale = 1.0 / sqrt((double)hd);
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t b = 0; b < B; ++b)
+    for (int64_t j = 0; j < nq; ++j) {
+      const int64_t g = (j * nkv) / nq, L = lens[b];
+      const double *q = qkv + b * N + j * hd;
+      double *w = malloc(sizeof(double) * (size_t)L);
+      double m = -INFINITY;
+      for (int64_t p = 0; p < L; ++p) {
+        const double *k = (p == L - 1) ? qkv + b * N + (nq + g) * hd
+                                       : Kc + ((b * nkv + g) * Lmax + p) * hd;
+        w[p] = dot(q, k, hd) * scale;
+        if (w[p] > m) m = w[p];
+      }
+      double den = 0.0;
+      for (int64_t p = 0; p < L; ++p) {
+        w[p] = exp(w[p] - m);
+        den += w[p];
+      }
+      for (int64_t c = 0; c < hd; ++c) {
+        double acc = 0.0;
+        for (int64_t p = 0; p < L; ++p) {
+          const double *v = (p == L - 1) ? qkv + b * N + (nq + nkv + g) * hd
+                                         : Vc + ((b * nkv + g) * Lmax + p) * hd;
+          acc += (w[p] / den) * v[c];
+        }
+        A[b * (nq * hd) + j * hd + c] = acc;
+      }
+      free(w);
+    }
+}

@@ -33,6 +33,11 @@ MUTANTS = {
     "e4m3_bias": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
     "e4m3_no_subnormal": ("ldexp(m / 8.0, -6)", "ldexp(1.0 + m / 8.0, -7)"),
     "e4m3_mantissa": ("ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 16.0, e - 7)"),
+    "decode_drops_new_token": ("for (int64_t p = 0; p < L; ++p) {\n        const double *k", "for (int64_t p = 0; p + 1 < L; ++p) {\n        const double *k"),
+    "decode_new_k_from_cache": ("const double *k = (p == L - 1) ? qkv + b * N + (nq + g) * hd", "const double *k = (p == L) ? qkv + b * N + (nq + g) * hd"),
+    "decode_gqa_map": ("const int64_t g = (j * nkv) / nq, L = lens[b];", "const int64_t g = j % nkv, L = lens[b];"),
+    "decode_cache_batch": (": Kc + ((b * nkv + g) * Lmax + p) * hd;", ": Kc + (g * Lmax + p) * hd;"),
+    "decode_v_new_token": ("const double *v = (p == L - 1) ? qkv + b * N + (nq + nkv + g) * hd", "const double *v = (p == L - 1) ? qkv + b * N + (nq + g) * hd"),
     "fp8_row_scale": ("scales[n] * orc_e4m3(codes[n * K + k])", "scales[k % N] * orc_e4m3(codes[n * K + k])"),
 }
 

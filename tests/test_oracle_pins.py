@@ -378,6 +378,54 @@ def pin_sequence_shards_concatenate(orc):
     assert np.array_equal(np.concatenate(hs), h) and np.array_equal(np.concatenate(xs), x)
 
 
+def _decode_case(rng, B, nq, nkv, hd, Lmax, lens):
+    """qkv of the new tokens and caches whose entries past each sequence's
+    previous tokens hold NaN (they must never be read)."""
+    N = (nq + 2 * nkv) * hd
+    qkv = rng.standard_normal((B, N))
+    Kc = np.full((B, nkv, Lmax, hd), np.nan)
+    Vc = np.full((B, nkv, Lmax, hd), np.nan)
+    for b, L in enumerate(lens):
+        Kc[b, :, :L - 1] = rng.standard_normal((nkv, L - 1, hd))
+        Vc[b, :, :L - 1] = rng.standard_normal((nkv, L - 1, hd))
+    return qkv, Kc, Vc
+
+
+def pin_attn_decode(orc):
+    """Decode attention over the KV cache: one position gives the new token's
+    v; equal keys give the mean of v; entries past lens[b] are never read;
+    a cache filled with a causal sequence's first tokens reproduces the
+    causal attention core's last row (itself pinned by brute force)."""
+    rng = np.random.default_rng(21)
+    nq, nkv, hd = 4, 2, 8
+    qkv, Kc, Vc = _decode_case(rng, 3, nq, nkv, hd, 6, [1, 1, 1])
+    A = orc.attn_decode(qkv, Kc, Vc, [1, 1, 1], nq, nkv, hd)
+    for j in range(nq):
+        g = j * nkv // nq
+        assert np.array_equal(A[:, j * hd:(j + 1) * hd],
+                              qkv[:, (nq + nkv + g) * hd:(nq + nkv + g + 1) * hd])
+    qkv, Kc, Vc = _decode_case(rng, 2, nq, nkv, hd, 7, [5, 7])
+    for b, L in enumerate([5, 7]):
+        Kc[b, :, :L - 1] = qkv[b, nq * hd:(nq + nkv) * hd].reshape(nkv, 1, hd)
+    A = orc.attn_decode(qkv, Kc, Vc, [5, 7], nq, nkv, hd)
+    for b, L in enumerate([5, 7]):
+        for j in range(nq):
+            g = j * nkv // nq
+            vs = np.concatenate([Vc[b, g, :L - 1],
+                                 qkv[b, (nq + nkv + g) * hd:(nq + nkv + g + 1) * hd][None]])
+            assert np.allclose(A[b, j * hd:(j + 1) * hd], vs.mean(axis=0), rtol=1e-13, atol=1e-14)
+    S = 9
+    seq = rng.standard_normal((S, (nq + 2 * nkv) * hd))
+    Kc = np.full((1, nkv, 12, hd), np.nan)
+    Vc = np.full((1, nkv, 12, hd), np.nan)
+    for g in range(nkv):
+        Kc[0, g, :S - 1] = seq[:S - 1, (nq + g) * hd:(nq + g + 1) * hd]
+        Vc[0, g, :S - 1] = seq[:S - 1, (nq + nkv + g) * hd:(nq + nkv + g + 1) * hd]
+    A = orc.attn_decode(seq[S - 1:], Kc, Vc, [S], nq, nkv, hd)
+    ref = orc.attn_core(seq, S, nq, nkv, hd)[S - 1]
+    assert np.allclose(A[0], ref, rtol=1e-12, atol=1e-13)
+
+
 ALL_PINS = [
     pin_silu_closed_forms,
     pin_mlp_bruteforce_exact,
@@ -396,6 +444,7 @@ ALL_PINS = [
     pin_fp8_decode,
     pin_fp8_dequant_rows,
     pin_sequence_shards_concatenate,
+    pin_attn_decode,
 ]
 
 
