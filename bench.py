@@ -27,8 +27,9 @@ The printed JSON line also carries
                 prefill 512 TFLOP/s at TP=8 and TP=1, Qwen2.5-1.5B TP=2 calls,
                 the layer at prefill 512, the partial reduce, the residual
                 update + RMSNorm after a block, the layer as a pre-norm block
-                with those at decode 32, and the MLP with weight-only FP8
-                storage at decode 1 and 8).
+                with those at decode 32, the MLP with weight-only FP8
+                storage at decode 1 and 8, and decode attention over a
+                rank's KV cache).
 """
 from __future__ import annotations
 
@@ -389,6 +390,28 @@ def detail(torch, tp, layer, calls):
         gbs = wl.ResidualNormShape(TP, I, D).bytes() / (st["median_us"] * 1e-6) / 1e9
         out[f"residual_rmsnorm_t8_I{I}"] = dict(**st, GBps=round(gbs, 1),
                                                 frac_hbm=round(gbs / PEAK_HBM, 3))
+    # decode attention of a TP=8 rank over its KV cache (8 query heads, 1 KV
+    # group, head_dim 128), 32 sequences at full cache length; cache copies
+    # rotate so the reads come from HBM, not the Infinity Cache
+    B, nql, nkl = 32, NQ // TP, NKV // TP
+    qkv = to_dev(T, datagen.gaussian("A", (B, (nql + 2 * nkl) * HD), 1.0, "bf16", 4700))
+    A = T.empty((B, nql * HD), dtype=T.bfloat16, device="cuda")
+    for L in (2048, 8192):
+        cache_b = B * nkl * L * HD * 2
+        copies = max(2, -(-300_000_000 // (2 * cache_b)))
+        caches = [(T.randn((B, nkl, L, HD), device="cuda").to(T.bfloat16),
+                   T.randn((B, nkl, HD, L), device="cuda").to(T.bfloat16)) for _ in range(copies)]
+        lens = T.full((B,), L, dtype=T.int32, device="cuda")
+        fns = [(lambda kv=kv: tp.attn_decode(lens, qkv, kv[0], kv[1], A, nql, nkl, HD))
+               for kv in caches]
+        st = stats(time_calls(T, fns, calls // 2))
+        nbytes = 2 * cache_b + qkv.numel() * 2 + A.numel() * 2
+        gbs = nbytes / (st["median_us"] * 1e-6) / 1e9
+        out[f"llama70b_attn_decode_tp8_B32_L{L}"] = dict(**st, bytes_per_call=nbytes,
+                                                        GBps=round(gbs, 1),
+                                                        frac_hbm=round(gbs / PEAK_HBM, 3))
+        log(f"decode attention B=32 L={L}: {st['median_us']} us")
+        del caches
     # the sequence-parallel form at prefill 512: 8 ranks' reduce-scatter + norm
     # on their 64 rows each, x gathered in place into one [512, D] buffer
     I = 512

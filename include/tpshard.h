@@ -220,6 +220,39 @@ tp_status_t tp_reduce_scatter_rmsnorm(int32_t t, int32_t rank, int64_t I, int64_
                                       tp_dtype_t x_dt, void* x, float eps, void* stream);
 
 /*
+ * Decode attention of one rank over its KV cache ([L4] §4.4: the cache is
+ * split with the heads -- a rank stores and reads only the KV groups of its
+ * own query heads; once the ranks outnumber the groups, a group is stored on
+ * every rank whose heads use it).  For each of B sequences the new token
+ * attends to lens[b] positions: 0 .. lens[b]-2 from the cache, lens[b]-1 the
+ * new token itself, whose k and v are taken from qkv.  The call also stores
+ * that k and v into cache slot lens[b]-1, ready for the next step.  Local
+ * head j uses local group floor(j n_kv_local / n_q_local); scale
+ * 1/sqrt(head_dim); softmax over all lens[b] positions.
+ *   lens      [B] int32 device array, each in [1, L_max] (clamped to it)
+ *   qkv       [B, (n_q_local + 2 n_kv_local) head_dim] bf16, as TP_ATTN_QKV
+ *             writes it for the new tokens
+ *   K_cache   [B, n_kv_local, L_max, head_dim] bf16: row p holds position
+ *             p's k; read, and row lens[b]-1 written
+ *   V_cache   [B, n_kv_local, head_dim, L_max] bf16, transposed: column p
+ *             holds position p's v; read, and column lens[b]-1 written
+ *   A         [B, n_q_local head_dim] bf16 out
+ *   workspace as tp_shard_mlp (tp_attn_decode_workspace_size bytes, counter
+ *             area zero before first use, left zero)
+ * head_dim and L_max multiples of 8 (TP_ERR_MISALIGNED otherwise), head_dim
+ * at most 128; n_kv_local divides n_q_local, at most 32 heads per group; each
+ * cache below 2 GiB.
+ * Errors: TP_ERR_INVALID, TP_ERR_MISALIGNED, TP_ERR_UNSUPPORTED,
+ * TP_ERR_WORKSPACE, TP_ERR_LAUNCH.
+ */
+size_t tp_attn_decode_workspace_size(int64_t B, int64_t n_q_local, int64_t n_kv_local,
+                                     int64_t head_dim, int64_t L_max);
+tp_status_t tp_attn_decode(int64_t B, int64_t n_q_local, int64_t n_kv_local, int64_t head_dim,
+                           int64_t L_max, const int32_t* lens, const void* qkv, void* K_cache,
+                           void* V_cache, void* A, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * Attention core of one rank (test support, not a projection): each rank
  * computes its own heads' attention completely ([L4] §4.2).  Scaled dot
  * product (scale 1/sqrt(head_dim)), causal inside each sequence, no rotary

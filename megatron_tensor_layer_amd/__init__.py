@@ -42,6 +42,8 @@ SIGNATURES = {
     "tp_reduce_scatter_rmsnorm": (ctypes.c_int, [_i32, _i32, _i64, _i64, _vp, _vp, ctypes.c_int,
                                                  _vp, _vp, ctypes.c_int, _vp, ctypes.c_float,
                                                  _vp]),
+    "tp_attn_decode_workspace_size": (_sz, [_i64] * 5),
+    "tp_attn_decode": (ctypes.c_int, [_i64] * 5 + [_vp] * 6 + [_sz, _vp]),
     "tp_shard_mlp_fp8": (ctypes.c_int, [_i64, _i64, _i64] + [_vp] * 10),
     "tp_residual_rmsnorm": (ctypes.c_int, [_i32, _i64, _i64, _vp, _vp, ctypes.c_int, _vp, _vp,
                                            ctypes.c_int, _vp, ctypes.c_float, _vp]),
@@ -304,6 +306,35 @@ def reduce_scatter_rmsnorm(partials, rank: int, residual, h, gamma=None, x=None,
         t, rank, I, D, _ptr(partials), _ptr(residual) if residual is not None else None,
         _dt(h), _ptr(h), _ptr(gamma) if gamma is not None else None, x_dt,
         _ptr(x) if x is not None else None, float(eps), _stream(stream, dev)))
+
+
+def attn_decode(lens, qkv, K_cache, V_cache, A, n_q_local: int, n_kv_local: int,
+                head_dim: int, workspace=None, stream=None) -> None:
+    """Decode attention over the rank's KV cache: lens [B] int32, qkv [B, N_qkv]
+    bf16 (the new tokens), K_cache [B, n_kv_local, L_max, head_dim] and the
+    transposed V_cache [B, n_kv_local, head_dim, L_max] bf16 (position
+    lens[b]-1 is written with the new k, v), A [B, n_q_local * head_dim] bf16."""
+    torch = _torch()
+    dev = _dev(lens, qkv, K_cache, V_cache, A)
+    if lens.dtype != torch.int32:
+        raise TypeError("lens must be int32")
+    for a in (qkv, K_cache, V_cache, A):
+        if a.dtype != torch.bfloat16:
+            raise TypeError("qkv, caches and A are bfloat16")
+    B, nkv, L_max, hd = K_cache.shape
+    if nkv != n_kv_local or hd != head_dim or tuple(V_cache.shape) != (B, nkv, hd, L_max):
+        raise ValueError("K_cache [B, n_kv_local, L_max, head_dim], "
+                         "V_cache [B, n_kv_local, head_dim, L_max]")
+    if lens.numel() != B or qkv.shape[0] != B or tuple(A.shape) != (B, n_q_local * head_dim):
+        raise ValueError("lens [B], qkv [B, N_qkv], A [B, n_q_local * head_dim]")
+    if workspace is not None:
+        ws_ptr, ws_bytes = _user_workspace(workspace)
+    else:
+        ws_ptr, ws_bytes = _workspace(dev, lib().tp_attn_decode_workspace_size(
+            B, n_q_local, n_kv_local, head_dim, L_max))
+    _check("tp_attn_decode", lib().tp_attn_decode(
+        B, n_q_local, n_kv_local, head_dim, L_max, _ptr(lens), _ptr(qkv), _ptr(K_cache),
+        _ptr(V_cache), _ptr(A), ws_ptr, ws_bytes, _stream(stream, dev)))
 
 
 def attn_core(qkv, A, S: int, n_q_local: int, n_kv_local: int, head_dim: int,

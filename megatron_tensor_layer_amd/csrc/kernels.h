@@ -76,6 +76,14 @@ hipError_t residual_rmsnorm_launch(int t, int I, int D, const float* P, int64_t 
                                    const void* residual, bool h_bf16, void* h, const void* gamma,
                                    bool x_bf16, void* x, float eps, hipStream_t stream);
 
+// Decode attention over the rank's KV cache (head_dim <= 128, at most 32
+// query heads per KV group); `workspace` (attn_decode_workspace_bytes, 0
+// when the positions are not split) holds counters and chunk states.
+size_t attn_decode_workspace_bytes(int B, int nkv, int hd, int Lmax);
+hipError_t attn_decode_launch(int B, int nq, int nkv, int hd, int Lmax, const int* lens,
+                              const uint16_t* qkv, uint16_t* Kc, uint16_t* Vc, uint16_t* A,
+                              void* workspace, hipStream_t stream);
+
 hipError_t attn_core_launch(int I, int S, int nq, int nkv, int hd, const uint16_t* qkv,
                             uint16_t* A, hipStream_t stream);
 

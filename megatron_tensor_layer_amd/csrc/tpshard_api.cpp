@@ -329,6 +329,64 @@ tp_status_t tp_reduce_scatter_rmsnorm(int32_t t, int32_t rank, int64_t I, int64_
                                                x_dt == TP_BF16, x, eps, s));
 }
 
+namespace {
+// Shared checks of the decode-attention sizes; TP_OK if supported.
+tp_status_t decode_sizes(int64_t B, int64_t nq, int64_t nkv, int64_t hd, int64_t Lmax) {
+  if (B < 0 || B > INT32_MAX || nq < 1 || nq > 65535 || nkv < 1 || nkv > nq || hd < 1 ||
+      Lmax < 1 || Lmax > INT32_MAX)
+    return TP_ERR_INVALID;
+  if (nq % nkv) return TP_ERR_INVALID;  // every KV group serves the same number of heads
+  if (hd % 8 || Lmax % 8) return TP_ERR_MISALIGNED;
+  if (hd > 128 || nq / nkv > 32) return TP_ERR_UNSUPPORTED;
+  if (B * nkv * Lmax * hd * 2 >= (int64_t(1) << 31)) return TP_ERR_UNSUPPORTED;
+  if (B * (nq + 2 * nkv) * hd * 2 >= (int64_t(1) << 31)) return TP_ERR_UNSUPPORTED;
+  return TP_OK;
+}
+}  // namespace
+
+size_t tp_attn_decode_workspace_size(int64_t B, int64_t n_q_local, int64_t n_kv_local,
+                                     int64_t head_dim, int64_t L_max) {
+  if (decode_sizes(B, n_q_local, n_kv_local, head_dim, L_max) != TP_OK || B == 0) return 0;
+  return tpk::attn_decode_workspace_bytes((int)B, (int)n_kv_local, (int)head_dim, (int)L_max);
+}
+
+tp_status_t tp_attn_decode(int64_t B, int64_t n_q_local, int64_t n_kv_local, int64_t head_dim,
+                           int64_t L_max, const int32_t* lens, const void* qkv, void* K_cache,
+                           void* V_cache, void* A, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  const tp_status_t st = decode_sizes(B, n_q_local, n_kv_local, head_dim, L_max);
+  if (st != TP_OK) return st;
+  if (B == 0) return TP_OK;
+  if (!lens || !qkv || !K_cache || !V_cache || !A) return TP_ERR_INVALID;
+  if (!aligned16(qkv) || !aligned16(K_cache) || !aligned16(V_cache) || !aligned16(A) ||
+      (reinterpret_cast<uintptr_t>(lens) & 3u))
+    return TP_ERR_MISALIGNED;
+  const int64_t N = (n_q_local + 2 * n_kv_local) * head_dim;
+  const int64_t cache = B * n_kv_local * L_max * head_dim * 2;
+  const Range rL = rng(lens, B * 4), rQ = rng(qkv, B * N * 2), rK = rng(K_cache, cache),
+              rV = rng(V_cache, cache), rA = rng(A, B * n_q_local * head_dim * 2);
+  for (Range in : {rL, rQ, rK, rV})
+    if (overlap(rA, in)) return TP_ERR_INVALID;
+  for (Range in : {rL, rQ, rV})
+    if (overlap(rK, in)) return TP_ERR_INVALID;
+  for (Range in : {rL, rQ})
+    if (overlap(rV, in)) return TP_ERR_INVALID;
+  const size_t need = tp_attn_decode_workspace_size(B, n_q_local, n_kv_local, head_dim, L_max);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return TP_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return TP_ERR_MISALIGNED;
+    const Range rW = rng(workspace, (int64_t)need);
+    for (Range o : {rL, rQ, rK, rV, rA})
+      if (overlap(rW, o)) return TP_ERR_INVALID;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  return launched(tpk::attn_decode_launch(
+      (int)B, (int)n_q_local, (int)n_kv_local, (int)head_dim, (int)L_max, lens,
+      static_cast<const uint16_t*>(qkv), static_cast<uint16_t*>(K_cache),
+      static_cast<uint16_t*>(V_cache), static_cast<uint16_t*>(A), need ? workspace : nullptr, s));
+}
+
 tp_status_t tp_attn_core(int64_t I, int64_t S, int64_t n_q_local, int64_t n_kv_local,
                          int64_t head_dim, const void* qkv, void* A, void* stream) {
   if (I < 0 || I > INT32_MAX || !dims_ok(S) || !dims_ok(n_kv_local) || n_q_local < 1 ||

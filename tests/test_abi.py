@@ -156,6 +156,25 @@ def test_reduce_scatter_rmsnorm_validation(lib):
     assert n(4, 1, 8, 60, P, R, F, H, G, F, X, eps, None) == MISALIGNED
 
 
+def test_attn_decode_validation(lib):
+    d = lib.tp_attn_decode
+    L, Q, K, V, A = (fake(k) for k in range(5))
+    ws_need = lib.tp_attn_decode_workspace_size(4, 8, 1, 128, 2048)
+    assert ws_need > 0 and lib.tp_attn_decode_workspace_size(4, 8, 3, 128, 2048) == 0
+    W = fake(6)
+    assert d(0, 8, 1, 128, 2048, None, None, None, None, None, None, 0, None) == OK
+    assert d(4, 8, 3, 128, 2048, L, Q, K, V, A, W, ws_need, None) == INVALID   # groups uneven
+    assert d(4, 8, 1, 136, 2048, L, Q, K, V, A, W, ws_need, None) == UNSUPPORTED
+    assert d(4, 8, 1, 60, 2048, L, Q, K, V, A, W, ws_need, None) == MISALIGNED
+    assert d(4, 8, 1, 128, 2044, L, Q, K, V, A, W, ws_need, None) == MISALIGNED  # L_max % 8
+    assert d(4, 64, 1, 128, 2048, L, Q, K, V, A, W, ws_need, None) == UNSUPPORTED  # 64 heads/group
+    assert d(64, 8, 1, 128, 1 << 17, L, Q, K, V, A, W, ws_need, None) == UNSUPPORTED  # cache > 2 GiB
+    assert d(4, 8, 1, 128, 2048, L, Q, K, V, A, None, 0, None) == WORKSPACE
+    assert d(4, 8, 1, 128, 2048, None, Q, K, V, A, W, ws_need, None) == INVALID
+    assert d(4, 8, 1, 128, 2048, L, Q, K, ctypes.c_void_p(FAKE + 2 * STEP + 4096), A, W,
+             ws_need, None) == INVALID                                         # V inside K
+
+
 def test_mlp_fp8_validation(lib):
     m = lib.tp_shard_mlp_fp8
     args = [fake(k) for k in range(10)]  # X, Wg, sg, Wu, su, Wd, sd, H, P, stream
