@@ -55,6 +55,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
+}
+
 // Buffer descriptor words (raw addressing over [base, base + bytes)); kept
 // in SGPRs for the asm load below.
 __device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) {
@@ -334,53 +338,362 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
   }
 }
 
+// ---------------------------------------------------------------- 256 x 256
+// The same product with 256 x 256 workgroup tiles for many tokens (M >= 384):
+// per K element a CU copies 2 x 256 rows for 2 x 256 x 256 FLOPs, twice the
+// FLOPs per copied byte of the 128 x 128 tile.  At these shapes the global
+// -> LDS copy stream of a CU runs at about 24-26 B/clk however deep the
+// pipeline (the L1's misses in flight over their latency), which caps a
+// 128 x 128 tile near 41 % of MFMA peak and a 256 x 256 tile near 75 %.
+//   * eight waves in a 2 x 4 grid of 128 x 64 wave tiles (4 x 2 MFMA
+//     fragments, 128 fp32 accumulators per lane), no K groups;
+//   * K stages of 32 (64-byte tile rows, 32 KB per stage), five stages (all
+//     160 KB of LDS), four in flight; 16-byte chunk c of row r sits in slot
+//     c ^ ((r / 4) % 4), so each 16-lane phase of an operand read covers all
+//     64 banks once;
+//   * SwiGLU: the W tile is 128 gate rows then the same 128 up rows, and
+//     each wave holds 32 gate and the matching 32 up columns;
+//   * split K and the XCD-aware order as in the 128 x 128 kernel.
+constexpr int BB = 256;                          // tile rows of A and of W
+constexpr int BKB = 32;                          // K per stage
+constexpr int kRowBB = BKB * 2;                  // 64-byte tile rows
+constexpr int kStageBA = BB * kRowBB;            // 16 KB
+constexpr int kStageB = 2 * kStageBA;            // 32 KB
+constexpr int SB = 5;
+constexpr int kLdsB = SB * kStageB;              // 160 KB
+constexpr int kInstB = kStageB / 1024 / 8;       // copy instructions per wave per stage
+static_assert(kInstB == 4, "four 1 KB copies per wave per stage");
+
+__device__ __forceinline__ int lds_off64(int row, int chunk) {
+  return row * kRowBB + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+template <int EPI>
+__global__ void __launch_bounds__(kThreads)
+gemm_big_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
+                const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
+                void* __restrict__ out, int64_t ldo, int KR, unsigned* __restrict__ counters,
+                float* __restrict__ part) {
+  // S stages of (A tile, W tile); after the K loop the first word holds the
+  // split-K arrival flag
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+
+  const int mt_n = (M + BB - 1) / BB;
+  constexpr int kCols = (EPI == EPI_SWIGLU) ? BB / 2 : BB;  // output columns per tile
+  const int nt_n = (N + kCols - 1) / kCols;
+  const int tiles = mt_n * nt_n;
+  const int ns = (K + KR - 1) / KR;
+  const int G = tiles * ns;
+  int b = blockIdx.x;
+  const int G8 = G & ~7;
+  if (b < G8) b = (b & 7) * (G8 >> 3) + (b >> 3);
+  const int split = b / tiles;
+  const int tile = b % tiles;
+  const int tm = tile % mt_n, tn = tile / mt_n;
+  const int m0 = tm * BB, c0 = tn * kCols;
+  const int kb = split * KR, ke = min(K, kb + KR);
+
+  const u32x4_t ra = rsrc_words(A + (int64_t)m0 * lda, (uint32_t)min(BB, M - m0) * (uint32_t)lda * 2u);
+  const int wrows = min(kCols, N - c0);
+  const u32x4_t rw0 = rsrc_words(W0 + (int64_t)c0 * K, (uint32_t)wrows * (uint32_t)K * 2u);
+  const u32x4_t rw1 = rsrc_words((EPI == EPI_SWIGLU ? W1 : W0) + (int64_t)c0 * K,
+                                 (uint32_t)wrows * (uint32_t)K * 2u);
+
+  // Stage st into buffer buf: 32 instructions of 1 KB (16 tile rows each),
+  // 16 for A then 16 for W; wave w issues instructions w, w + 8, w + 16 and
+  // w + 24.  Lane l fills slot l % 4 of row 16 q + l / 4 with the logical
+  // chunk that lds_off64 places there.
+  const int rr = lane >> 2, sl = lane & 3;
+  const uint32_t lsm = lds_addr(smem);
+  auto issue = [&](int st, int buf) {
+    const uint32_t la = lsm + buf * kStageB;
+    const int k0 = kb + st * BKB;
+#pragma unroll
+    for (int h = 0; h < kInstB; ++h) {
+      const int q = wave + h * 8;             // 0..31; h < 2: A rows, else W rows
+      const int r = (q & 15) * 16 + rr;       // row in its 256-row tile
+      const int c = sl ^ ((r >> 2) & 3);
+      const int k = k0 + c * 8;
+      const bool kin = k < ke;
+      if (h < 2) {
+        const uint32_t oa = (kin && m0 + r < M) ? (uint32_t)r * (uint32_t)lda * 2u + (uint32_t)k * 2u
+                                                : kOob;
+        lds_dma16(ra, oa, la + q * 1024);
+      } else {
+        const int wr = (EPI == EPI_SWIGLU) ? (r & 127) : r;
+        const uint32_t ow = (kin && wr < wrows) ? (uint32_t)wr * (uint32_t)K * 2u + (uint32_t)k * 2u
+                                                : kOob;
+        lds_dma16((EPI == EPI_SWIGLU && r >= 128) ? rw1 : rw0, ow, la + q * 1024);
+      }
+    }
+  };
+
+  int brow[2];
+  if constexpr (EPI == EPI_SWIGLU) {
+    brow[0] = wn * 32;        // gate f = c0 + wn*32 + lane%32
+    brow[1] = 128 + wn * 32;  // up, same f
+  } else {
+    brow[0] = wn * 64;
+    brow[1] = wn * 64 + 32;
+  }
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Operands of one 16-wide K step (ks) of a stage, read one step ahead of
+  // the MFMAs that use them.
+  bf16x8_t af[2][4], bw[2][2];
+  auto read_ops = [&](int buf, int ks, bf16x8_t (&a)[4], bf16x8_t (&w)[2]) {
+    const unsigned char* sa = smem + buf * kStageB;
+    const unsigned char* sb = sa + kStageBA;
+    const int c = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[i] = *reinterpret_cast<const bf16x8_t*>(sa + lds_off64(wm * 128 + i * 32 + (lane & 31), c));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      w[j] = *reinterpret_cast<const bf16x8_t*>(sb + lds_off64(brow[j] + (lane & 31), c));
+  };
+  auto mfmas = [&](const bf16x8_t (&a)[4], const bf16x8_t (&w)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], w[j], acc[i][j], 0, 0, 0);
+  };
+
+  // All SB buffers hold stages in flight: stage kt + SB is copied into the
+  // buffer of stage kt once every wave has its last operands of stage kt in
+  // registers.  The barrier sits between the two K steps' MFMAs of a stage:
+  // the pipe drains the first step's MFMAs while the waves meet, and the
+  // second step's run while the next stage's first operands are read.
+  const int NT = (ke - kb + BKB - 1) / BKB;
+#pragma unroll
+  for (int st = 0; st < SB; ++st)
+    if (st < NT) issue(st, st);
+  if (NT >= SB)
+    wait_vmcnt<(SB - 1) * kInstB>();  // stage 0 has landed
+  else
+    wait_vmcnt<0>();
+  __syncthreads();
+  read_ops(0, 0, af[0], bw[0]);
+  int buf = 0;  // kt % SB
+  // The two K steps of stage kt: the next step's 6 operand reads are issued
+  // ahead of the current step's 8 MFMAs (the scheduler is held to that order).
+  auto first_half = [&]() {
+    read_ops(buf, 1, af[1], bw[1]);
+    mfmas(af[0], bw[0]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // MFMA
+    __builtin_amdgcn_sched_barrier(0);                  // nothing moves past here
+  };
+  auto second_half = [&]() {
+    buf = buf == SB - 1 ? 0 : buf + 1;
+    read_ops(buf, 0, af[0], bw[0]);
+    mfmas(af[1], bw[1]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int kt = 0;
+  // steady state: stage kt + 1 has landed once the SB - 2 stages after it
+  // are the only ones in flight; stage kt + SB refills stage kt's buffer
+  for (; kt < NT - SB; ++kt) {
+    first_half();
+    wait_vmcnt<(SB - 2) * kInstB>();
+    wait_lgkmcnt0();  // this wave's reads of stage kt are in registers
+    __syncthreads();  // everyone's have; stage kt + 1 is in LDS
+    issue(kt + SB, buf);
+    second_half();
+  }
+  // the last stages: nothing more to copy
+  for (; kt < NT - 1; ++kt) {
+    first_half();
+    if (kt + SB - 1 < NT)
+      wait_vmcnt<(SB - 2) * kInstB>();
+    else
+      wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    __syncthreads();
+    second_half();
+  }
+  read_ops(buf, 1, af[1], bw[1]);
+  mfmas(af[0], bw[0]);
+  mfmas(af[1], bw[1]);
+
+  if (ns == 1) {
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int col = c0 + wn * 32 + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm * 128 + i * 32 + acc_row32(r, lane);
+          if (m < M && col < N)
+            store_out<EPI_DT>(out, ldo, m, col, silu(acc[i][0][r]) * acc[i][1][r]);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = c0 + wn * 64 + j * 32 + (lane & 31);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + wm * 128 + i * 32 + acc_row32(r, lane);
+            if (m < M && col < N) store_out<EPI>(out, ldo, m, col, acc[i][j][r]);
+          }
+        }
+    }
+    return;
+  }
+
+  // ---- split K: partial tile [BB][BB] in W-tile row order, then arrival
+  const int64_t tile_elems = (int64_t)BB * BB;
+  const __amdgpu_buffer_rsrc_t pr =
+      make_rsrc(part, (uint32_t)((int64_t)ns * tiles * tile_elems * 4));
+  const int64_t tbase = (int64_t)tile * tile_elems;
+  const int64_t plane = (int64_t)tiles * tile_elems;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int tc = brow[j] + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tr = wm * 128 + i * 32 + acc_row32(r, lane);
+        const float v = acc[i][j][r];
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __builtin_bit_cast(uint32_t, v), pr,
+            (uint32_t)((split * plane + tbase + tr * BB + tc) * 4), 0, kAuxSys);
+      }
+    }
+  int* is_last = reinterpret_cast<int*>(smem);  // the stages are consumed
+  wait_vmcnt<0>();  // partial stores have reached memory
+  __syncthreads();
+  if (tid == 0) *is_last = arrive_last(counters + tile, (unsigned)ns);
+  __syncthreads();
+  if (!*is_last) return;
+
+  auto sum_splits = [&](int64_t q) {
+    f32x4_t s4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < ns; s += 8) {
+      f32x4_t v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[e] = __builtin_bit_cast(
+            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                         pr, s + e < ns ? (uint32_t)((q + (s + e) * plane) * 4) : kOob, 0,
+                         kAuxSys));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s4 += v[e];
+    }
+    return s4;
+  };
+  constexpr int kQ = kCols / 4;
+  for (int idx = tid; idx < BB * kQ; idx += kThreads) {
+    const int tr = idx / kQ, tc = (idx % kQ) * 4;
+    const int m = m0 + tr;
+    if (m >= M) continue;
+    const f32x4_t s4 = sum_splits(tbase + tr * BB + tc);
+    f32x4_t v;
+    if constexpr (EPI == EPI_SWIGLU) {
+      const f32x4_t u = sum_splits(tbase + tr * BB + 128 + tc);
+      v = f32x4_t{silu(s4.x) * u.x, silu(s4.y) * u.y, silu(s4.z) * u.z, silu(s4.w) * u.w};
+    } else {
+      v = s4;
+    }
+    const int n = min(4, N - (c0 + tc));
+    for (int e = 0; e < n; ++e)
+      store_out<EPI == EPI_F32 ? EPI_F32 : EPI_DT>(out, ldo, m, c0 + tc + e, v[e]);
+  }
+}
+
 struct Plan {
+  bool big = false;  // 256 x 256 tiles
   int tiles = 0;
   int ns = 0;  // K splits
   int kr = 0;  // K per split
   int grid = 0;
 };
 
-// Split K when the tiles alone leave CUs idle: pick the split count that
-// minimises the busiest CU's share of work (in whole tiles), charging each
-// extra split a little for its partial round trip; at least 8 stages of K
-// per split, and the partials stay addressable with 32-bit offsets.
+// Cost model (CU cycles) for a tile size and split count.  A workgroup's
+// main loop runs at the rate its copy stream reaches next to the MFMA work,
+// measured on this chip at the prefill shapes with every CU busy: about
+// 21 B/clk per CU for 128 x 128 tiles and 12.5 B/clk for 256 x 256 (whose
+// copies then interleave less well with the longer MFMA runs), or at the
+// MFMA rate if that is lower.  Workgroups run in rounds of one per CU; with
+// split K each workgroup also writes its partial tile and the last of a
+// tile's workgroups reads all of them, each at the slower of a CU's stream
+// (about 24 B/clk) and its share of HBM (about 2 KB/clk for the chip).
+double plan_cost(int tiles, int ns, bool big, int K) {
+  const int bm = big ? BB : BM, bn = big ? BB : BN;
+  const double rate = big ? 12.5 : 21.0;
+  const double kspl = std::ceil((double)K / BK / ns) * BK;  // K per split
+  const double copy = (double)(bm + bn) * kspl * 2.0 / rate;
+  const double mfma = 2.0 * bm * bn * kspl / (4.0 * 1024.0) / 0.9;
+  const double rounds = std::ceil((double)tiles * ns / kCUs);
+  const double tile_bytes = (double)bm * bn * 4.0;
+  if (ns == 1) return rounds * std::max(copy, mfma) + 1500.0;
+  const double hbm = 2080.0;  // B/clk, the whole chip
+  const double wgs = (double)tiles * ns;
+  const double write = std::max(tile_bytes / 24.0, std::min(wgs, (double)kCUs) * tile_bytes / hbm);
+  const double reduce = std::max(ns * tile_bytes / 24.0, wgs * tile_bytes / hbm);
+  return rounds * (std::max(copy, mfma) + write) + reduce + 1500.0;
+}
+
+// Split K when the tiles alone leave CUs idle: the split count and tile size
+// of least modelled cost; at least 8 stages of K per split, at most 256 MB of
+// partials and one arrival counter per tile.
+constexpr double kMaxPartialBytes = 256.0 * 1024 * 1024;
 Plan make_plan(int M, int N, int K, bool swiglu) {
-  Plan pl;
-  const int cols = swiglu ? BN / 2 : BN;
-  pl.tiles = ((M + BM - 1) / BM) * ((N + cols - 1) / cols);
+  Plan best_pl;
+  double best = 1e300;
   const int kst = (K + BK - 1) / BK;  // K stages in all
   const int max_ns = std::max(1, std::min(16, kst / 8));
-  int best_ns = 1;
-  double best = 1e30;
-  for (int ns = 1; ns <= max_ns; ++ns) {
-    if (ns > 1 && ((double)ns * pl.tiles * BM * BN * 4.0 >= 2147483648.0 ||
-                   pl.tiles > kWsMaxCounters))
-      break;
-    const double busiest = std::ceil((double)pl.tiles * ns / kCUs) / ns;
-    const double cost = busiest * (1.0 + 0.04 * (ns - 1));
-    if (cost < best - 1e-9) {
-      best = cost;
-      best_ns = ns;
+  for (int big = 0; big < 2; ++big) {
+    if (big && M < 384) continue;
+    const int bm = big ? BB : BM, bn = big ? BB : BN;
+    const int cols = swiglu ? bn / 2 : bn;
+    const int tiles = ((M + bm - 1) / bm) * ((N + cols - 1) / cols);
+    for (int ns = 1; ns <= max_ns; ++ns) {
+      if (ns > 1 && ((double)ns * tiles * bm * bn * 4.0 > kMaxPartialBytes || tiles > kWsMaxCounters))
+        break;
+      const double cost = plan_cost(tiles, ns, big, K);
+      if (cost < best * (1.0 - 1e-9)) {
+        best = cost;
+        best_pl.big = big;
+        best_pl.tiles = tiles;
+        best_pl.ns = ns;
+      }
     }
   }
-  const int sps = (kst + best_ns - 1) / best_ns;  // stages per split
-  pl.kr = sps * BK;
-  pl.ns = (K + pl.kr - 1) / pl.kr;
-  pl.grid = pl.tiles * pl.ns;
-  return pl;
+  const int sps = (kst + best_pl.ns - 1) / best_pl.ns;  // stages per split
+  best_pl.kr = sps * BK;
+  best_pl.ns = (K + best_pl.kr - 1) / best_pl.kr;
+  best_pl.grid = best_pl.tiles * best_pl.ns;
+  return best_pl;
 }
 
 size_t plan_bytes(const Plan& pl) {
   if (pl.ns <= 1) return 0;
-  return kWsCounterBytes + (size_t)pl.ns * pl.tiles * BM * BN * sizeof(float);
+  const size_t te = pl.big ? (size_t)BB * BB : (size_t)BM * BN;
+  return kWsCounterBytes + (size_t)pl.ns * pl.tiles * te * sizeof(float);
 }
 
 template <int EPI>
 hipError_t launch_plan(const Plan& pl, int M, int N, int K, const uint16_t* A, int64_t lda,
                        const uint16_t* W0, const uint16_t* W1, void* out, int64_t ldo,
                        void* workspace, hipStream_t stream) {
-  auto kern = gemm_kernel<EPI>;
+  auto kern = pl.big ? gemm_big_kernel<EPI> : gemm_kernel<EPI>;
   unsigned* counters = nullptr;
   float* part = nullptr;
   if (pl.ns > 1) {
