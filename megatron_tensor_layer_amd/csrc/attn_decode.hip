@@ -16,9 +16,10 @@
 // columns (all heads of a group share each K and V read), online softmax
 // per head with one cross-half exchange per block, O^T += V^T P^T with P^T
 // taken from registers.  The V cache is stored transposed ([head_dim,
-// positions] per sequence and group), so the V^T operand -- 8 positions of
-// one head_dim row, in the order the S^T accumulator holds them -- is two
-// 8-byte loads straight from memory, with no transpose through LDS.
+// positions] per sequence and group), and the K rows of a block are loaded in
+// an order that makes each lane's S^T accumulator hold consecutive positions,
+// so the V^T operand -- 8 positions of one head_dim row -- is one 16-byte
+// load straight from memory, with no transpose through LDS.
 // The waves merge through LDS; with several chunks, each workgroup writes
 // its softmax state (max, sum, unnormalised O) to the workspace and the last
 // of the sequence-group's chunks to arrive (one atomic) merges them.
@@ -39,6 +40,14 @@ __device__ __forceinline__ int acc_row32(int r, int lane) {
   return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
 }
 
+// Position (within a block of 32) whose K row feeds S^T row i: bits 2 and 3
+// swapped.  Accumulator elements 8 ks .. 8 ks + 7 of a lane in half h then
+// hold positions 16 ks + 8 h + 0..7, consecutive, so the matching V^T operand
+// of the P V step is one 16-byte load.
+__device__ __forceinline__ int key_pos(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
 // Workspace record of one chunk: 32 heads x (hd_pad O values), then 32 (max,
 // sum) pairs.
 __host__ __device__ __forceinline__ int64_t rec_floats(int hdp) { return 32 * (int64_t)hdp + 64; }
@@ -57,6 +66,7 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
   __shared__ float mls[NWV][2][64];
   __shared__ float ots[NWV - 1][HDT][16][64];
   __shared__ int is_last;
+  __shared__ u32x4_t qs[KS][64];  // the Q operand, lane-linear
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -84,15 +94,19 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
       Vc[cache0 + (int64_t)d * Lmax + (len - 1)] = qkv[(int64_t)b * N + vcol + d];
   }
 
-  // Q as the B operand: head h = lane % 32 of the group, chunk 2 ks + lane/32
+  // Q as the B operand: head h = lane % 32 of the group, chunk 2 ks + lane/32.
+  // It is the same for every wave and every block, so it waits in LDS (wave
+  // 0 stages it) and is read again per block instead of holding registers.
   const int h = lane & 31;
-  bf16x8_t qf[KS];
+  if (w == 0) {
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int ch = 2 * ks + (lane >> 5);
-    const uint32_t off = (h < G && ch * 8 < hd) ? (uint32_t)((g * G + h) * hd + ch * 8) * 2u : kOob;
-    qf[ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rq, off));
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch = 2 * ks + (lane >> 5);
+      const uint32_t off = (h < G && ch * 8 < hd) ? (uint32_t)((g * G + h) * hd + ch * 8) * 2u : kOob;
+      qs[ks][lane] = buf_load16(rq, off);
+    }
   }
+  __syncthreads();
 
   f32x16_t ot[HDT];
 #pragma unroll
@@ -107,7 +121,7 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
   // this wave's blocks kb = k0 + 32 w, + 32 NWV, ...; the next block's K and
   // V are loaded while the current one is processed (past k1: zero)
   auto load_k = [&](int kb, bf16x8_t (&kf)[KS]) {
-    const int p = kb + (lane & 31);
+    const int p = kb + key_pos(lane & 31);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int ch = 2 * ks + (lane >> 5);
@@ -117,55 +131,47 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
     }
   };
   // V^T operand of 16-position step ks, tile t: head_dim row d = t*32 +
-  // lane%32, positions kb + 16 ks + 4 (lane/32) + {0..3} and + 8 + {0..3}
-  // -- the key order of the S^T accumulator.  A group of 4 that runs past
-  // len-2 keeps only its cache positions (the rest of the slot may hold
-  // anything); past k1 or head_dim, zero.
-  auto load_v = [&](int kb, u32x2_t (&vr)[2][HDT][2]) {
+  // lane%32, positions kb + 16 ks + 8 (lane/32) + 0..7 -- the key order of
+  // the S^T accumulator; past k1 or head_dim, zero.  A group of 8 that runs
+  // past len-2 is masked down to its cache positions when it is used (the
+  // rest of the slot may hold anything), so no load is waited on early.
+  auto load_v = [&](int kb, u32x4_t (&vr)[2][HDT]) {
     const int half = lane >> 5;
 #pragma unroll
     for (int t = 0; t < HDT; ++t) {
       const int d = t * 32 + (lane & 31);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int part = 0; part < 2; ++part) {
-          const int p0 = kb + ks * 16 + part * 8 + half * 4;
-          const int nv = len - 1 - p0;  // cache positions in the group, if below 4
-          const uint32_t off = (kb < k1 && d < hd && nv > 0)
-                                   ? ((uint32_t)d * (uint32_t)Lmax + (uint32_t)p0) * 2u : kOob;
-          u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0);
-          v.x &= nv >= 2 ? 0xffffffffu : nv == 1 ? 0xffffu : 0u;
-          v.y &= nv >= 4 ? 0xffffffffu : nv == 3 ? 0xffffu : 0u;
-          vr[ks][t][part] = v;
-        }
+      for (int ks = 0; ks < 2; ++ks) {
+        const int p0 = kb + ks * 16 + half * 8;
+        const uint32_t off = (kb < k1 && d < hd && p0 < len - 1)
+                                 ? ((uint32_t)d * (uint32_t)Lmax + (uint32_t)p0) * 2u : kOob;
+        vr[ks][t] = buf_load16(rv, off);
+      }
     }
   };
-  bf16x8_t kf[KS];
-  u32x2_t vr[2][HDT][2];
-  load_k(k0 + 32 * w, kf);
-  load_v(k0 + 32 * w, vr);
-  for (int kb = k0 + 32 * w; kb < k1; kb += 32 * NWV) {
+  auto v_mask = [&](int kb, int ks) {  // keep positions below len-1
+    const int nv = len - 1 - (kb + ks * 16 + (lane >> 5) * 8);
+    u32x4_t m;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m[q] = nv >= 2 * q + 2 ? 0xffffffffu : nv == 2 * q + 1 ? 0xffffu : 0u;
+    return m;
+  };
+  // One block: S^T = K Q^T, online softmax, O^T += V^T P^T.  The next
+  // block's K and V are loaded before the current block is processed.
+  auto process = [&](int kb, const bf16x8_t (&kf)[KS], const u32x4_t (&vc)[2][HDT]) {
     f32x16_t st;
 #pragma unroll
     for (int r = 0; r < 16; ++r) st[r] = 0.0f;
+    asm volatile("" ::: "memory");  // read Q from LDS again: do not hold it across blocks
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st, 0, 0, 0);
-    u32x2_t vc[2][HDT][2];  // this block's V^T operands; the registers refill below
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int t = 0; t < HDT; ++t)
-#pragma unroll
-        for (int part = 0; part < 2; ++part) vc[ks][t][part] = vr[ks][t][part];
-    load_k(kb + 32 * NWV, kf);
-    load_v(kb + 32 * NWV, vr);
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], __builtin_bit_cast(bf16x8_t, qs[ks][lane]),
+                                                   st, 0, 0, 0);
     float x[16];
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = kb + acc_row32(r, lane);
+      const int key = kb + key_pos(acc_row32(r, lane));
       x[r] = key < k1 ? st[r] * scale : -INFINITY;
       mx = fmaxf(mx, x[r]);
     }
@@ -186,20 +192,34 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
     m = mnew;
 #pragma unroll
     for (int t = 0; t < HDT; ++t) ot[t] *= corr;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4_t vm = v_mask(kb, ks);
 #pragma unroll
       for (int t = 0; t < HDT; ++t) {
-        const u32x4_t vv = u32x4_t{vc[ks][t][0].x, vc[ks][t][0].y, vc[ks][t][1].x, vc[ks][t][1].y};
+        const u32x4_t vv = vc[ks][t] & vm;
         ot[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pb[ks],
                                                         ot[t], 0, 0, 0);
       }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  };
+  constexpr int kStep = 32 * NWV;
+  bf16x8_t kf[KS];
+  u32x4_t vr[2][HDT];
+  load_k(k0 + 32 * w, kf);
+  load_v(k0 + 32 * w, vr);
+  for (int kb = k0 + 32 * w; kb < k1; kb += kStep) {
+    bf16x8_t kc[KS];
+    u32x4_t vc[2][HDT];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kc[ks] = kf[ks];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int t = 0; t < HDT; ++t) vc[ks][t] = vr[ks][t];
+    load_k(kb + kStep, kf);
+    load_v(kb + kStep, vr);
+    process(kb, kc, vc);
   }
 
   // ---- the new token (position len-1) into chunk 0's wave 0: one more
@@ -210,7 +230,7 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
     for (int ks = 0; ks < KS; ++ks) {
       const int ch = 2 * ks + (lane >> 5);
       const u32x4_t kn = buf_load16(rq, ch * 8 < hd ? (uint32_t)(kcol + ch * 8) * 2u : kOob);
-      const u32x4_t qq = __builtin_bit_cast(u32x4_t, qf[ks]);
+      const u32x4_t qq = qs[ks][lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e) dot = dot2_bf16(qq[e], kn[e], dot);
     }
