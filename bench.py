@@ -28,7 +28,7 @@ The printed JSON line also carries
                 the layer at prefill 512, the partial reduce, the residual
                 update + RMSNorm after a block, the layer as a pre-norm block
                 with those at decode 32, the MLP with weight-only FP8
-                storage at decode 1 and 8, and decode attention over a
+                storage at decode 1, 8 and 32, and decode attention over a
                 rank's KV cache).
 """
 from __future__ import annotations
@@ -315,7 +315,7 @@ def detail(torch, tp, layer, calls):
 
     fp8_ranks = [((codes(Fl, D), scales(Fl)), (codes(Fl, D), scales(Fl)),
                   (codes(D, Fl), scales(D))) for _ in range(TP)]
-    for I in (1, 8):
+    for I in (1, 8, 32):
         X = to_dev(T, datagen.gaussian("X", (I, D), 1.0, "bf16", 1100 + I))
         H = T.empty((I, Fl), dtype=T.bfloat16, device="cuda")
         P = T.empty((I, D), dtype=T.float32, device="cuda")

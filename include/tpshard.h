@@ -108,7 +108,7 @@ tp_status_t tp_shard_mlp(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * tp_shard_mlp with weight-only FP8 storage, for decode (I <= 8 tokens).  The
+ * tp_shard_mlp with weight-only FP8 storage, for decode (1..64 tokens).  The
  * pages' cost frontier is FP8 throughout but they give no storage convention;
  * the one used here: every weight is one byte in the OCP E4M3 ("fn") encoding
  * (sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, 0x7F and
@@ -123,15 +123,21 @@ tp_status_t tp_shard_mlp(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt,
  *   W_up    [F_local, D]  E4M3 codes, s_up   [F_local] fp32
  *   W_down  [D, F_local]  E4M3 codes, s_down [D] fp32 (scales per output row)
  *   H       [I, F_local]  bf16 written; P [I, D] fp32 overwritten
- * D and F_local multiples of 16 and at most 16384; I at most 8
- * (TP_ERR_UNSUPPORTED beyond).  No workspace.  Scales 4-byte aligned, every
- * other pointer 16-byte aligned.
- * Errors: TP_ERR_INVALID, TP_ERR_MISALIGNED, TP_ERR_UNSUPPORTED, TP_ERR_LAUNCH.
+ *   workspace as tp_shard_mlp: tp_shard_mlp_fp8_workspace_size bytes (0 for
+ *           up to 4 tokens), counter area zero before first use, left zero
+ * D and F_local multiples of 16.  Up to 4 tokens (D, F_local at most 16384)
+ * the weights stream through VALU dot products; 5..64 tokens (or larger K)
+ * through the split-K MFMA kernel; otherwise TP_ERR_UNSUPPORTED.  Scales
+ * 4-byte aligned, every other pointer 16-byte aligned.
+ * Errors: TP_ERR_INVALID, TP_ERR_MISALIGNED, TP_ERR_UNSUPPORTED,
+ * TP_ERR_WORKSPACE, TP_ERR_LAUNCH.
  */
+size_t tp_shard_mlp_fp8_workspace_size(int64_t I, int64_t D, int64_t F_local);
 tp_status_t tp_shard_mlp_fp8(int64_t I, int64_t D, int64_t F_local, const void* X,
                              const void* W_gate, const float* s_gate, const void* W_up,
                              const float* s_up, const void* W_down, const float* s_down,
-                             void* H, float* P, void* stream);
+                             void* H, float* P, void* workspace, size_t workspace_bytes,
+                             void* stream);
 
 /* Workspace bytes tp_shard_attn_proj needs (0 if none); host-only. */
 size_t tp_shard_attn_proj_workspace_size(tp_attn_phase_t phase, int64_t I, int64_t D,

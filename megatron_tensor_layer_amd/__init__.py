@@ -44,7 +44,8 @@ SIGNATURES = {
                                                  _vp]),
     "tp_attn_decode_workspace_size": (_sz, [_i64] * 5),
     "tp_attn_decode": (ctypes.c_int, [_i64] * 5 + [_vp] * 6 + [_sz, _vp]),
-    "tp_shard_mlp_fp8": (ctypes.c_int, [_i64, _i64, _i64] + [_vp] * 10),
+    "tp_shard_mlp_fp8_workspace_size": (_sz, [_i64] * 3),
+    "tp_shard_mlp_fp8": (ctypes.c_int, [_i64, _i64, _i64] + [_vp] * 10 + [_sz, _vp]),
     "tp_residual_rmsnorm": (ctypes.c_int, [_i32, _i64, _i64, _vp, _vp, ctypes.c_int, _vp, _vp,
                                            ctypes.c_int, _vp, ctypes.c_float, _vp]),
 }
@@ -223,11 +224,12 @@ def partial_reduce(partials, Y, stream=None) -> None:
                                                         _stream(stream, dev)))
 
 
-def shard_mlp_fp8(X, gate, up, down, H, P, stream=None) -> None:
-    """Weight-only FP8 MLP rank share for decode (I <= 8): gate, up, down are
-    (codes uint8, scales float32) pairs -- gate/up codes [F_local, D] with
+def shard_mlp_fp8(X, gate, up, down, H, P, workspace=None, stream=None) -> None:
+    """Weight-only FP8 MLP rank share for decode (1..64 tokens): gate, up, down
+    are (codes uint8, scales float32) pairs -- gate/up codes [F_local, D] with
     scales [F_local], down codes [D, F_local] with scales [D]; X and H bf16,
-    P float32."""
+    P float32.  Past 8 tokens the call needs a workspace (the binding keeps
+    one per device unless one is passed)."""
     torch = _torch()
     (Wg, sg), (Wu, su), (Wd, sd) = gate, up, down
     dev = _dev(X, Wg, sg, Wu, su, Wd, sd, H, P)
@@ -242,9 +244,13 @@ def shard_mlp_fp8(X, gate, up, down, H, P, stream=None) -> None:
             raise ValueError("scales must be float32, one per output row")
     if tuple(H.shape) != (I, F_local) or tuple(P.shape) != (I, D):
         raise ValueError("H [I, F_local], P [I, D]")
+    if workspace is not None:
+        ws_ptr, ws_bytes = _user_workspace(workspace)
+    else:
+        ws_ptr, ws_bytes = _workspace(dev, lib().tp_shard_mlp_fp8_workspace_size(I, D, F_local))
     _check("tp_shard_mlp_fp8", lib().tp_shard_mlp_fp8(
         I, D, F_local, _ptr(X), _ptr(Wg), _ptr(sg), _ptr(Wu), _ptr(su), _ptr(Wd), _ptr(sd),
-        _ptr(H), _ptr(P), _stream(stream, dev)))
+        _ptr(H), _ptr(P), ws_ptr, ws_bytes, _stream(stream, dev)))
 
 
 def residual_rmsnorm(partials, residual, h, gamma=None, x=None, eps: float = 1e-5,

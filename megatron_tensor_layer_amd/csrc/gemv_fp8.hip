@@ -16,20 +16,6 @@ namespace tpk {
 
 namespace {
 
-// 16 fp8 codes -> two 8-element bf16 chunks (K 0..7, K 8..15), exact.
-__device__ __forceinline__ void decode16(const u32x4_t& w, u32x4_t& lo, u32x4_t& hi) {
-  uint32_t p[8];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], false);  // bytes 0, 1
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], true);   // bytes 2, 3
-    p[2 * q] = pack_bf16x2(a[0], a[1]);
-    p[2 * q + 1] = pack_bf16x2(b[0], b[1]);
-  }
-  lo = u32x4_t{p[0], p[1], p[2], p[3]};
-  hi = u32x4_t{p[4], p[5], p[6], p[7]};
-}
-
 __device__ __forceinline__ float dot8(const u32x4_t& w, const u32x4_t& x, float acc) {
   acc = dot2_bf16(w.x, x.x, acc);
   acc = dot2_bf16(w.y, x.y, acc);

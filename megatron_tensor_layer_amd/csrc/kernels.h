@@ -49,10 +49,19 @@ size_t splitk_workspace_bytes(int I, int K, int N, bool swiglu);
 // Whether the split-K kernel is the better choice for this projection: it is
 // unless the activations of a full K range do not fit LDS (many tokens, long K).
 bool splitk_suits(int I, int K, int N, bool swiglu);
+// Whether the split-K kernel can run this projection at all (a K range of
+// activations fits LDS); the FP8 path has no tiled alternative.
+bool splitk_plannable(int I, int K, int N, bool swiglu);
 template <int EPI>
 hipError_t splitk_launch(int I, int K, int N, const uint16_t* X, const uint16_t* W0,
                          const uint16_t* W1, void* out, int64_t ldo, void* workspace,
                          hipStream_t stream);
+// The weight-only FP8 form of the same kernel (weights as in gemv_fp8_launch:
+// E4M3 codes, one fp32 scale per row); same plan and workspace as bf16.
+template <int EPI>
+hipError_t splitk_fp8_launch(int I, int K, int N, const uint16_t* X, const uint8_t* W0,
+                             const float* S0, const uint8_t* W1, const float* S1, void* out,
+                             int64_t ldo, void* workspace, hipStream_t stream);
 
 // Same product on bf16 MFMA for any M (128 x 128 tiles).  When the tiles
 // cannot fill the chip, K is split over workgroups and `workspace`

@@ -24,7 +24,13 @@
 //     store, or silu(gate) * up (lecture §4.1: the SwiGLU elementwise op is
 //     local to the rank).  A SwiGLU row block holds the gate tiles and the up
 //     tiles of the same F block, so the epilogue has both;
-//   * one kernel launch per projection: no separate reduction pass.
+//   * one kernel launch per projection: no separate reduction pass;
+//   * weight-only FP8 (OCP E4M3 codes, one fp32 scale per output row): a
+//     group of 128 K is 128 bytes per row, two load instructions of 8 rows x
+//     128 bytes; each 16-byte chunk of codes is decoded exactly to two bf16
+//     chunks on its way into the transpose tile, four groups in flight (the
+//     bf16 path's bytes in flight), and the finishing workgroup multiplies
+//     each summed row by its scale before the epilogue.
 #include "common.h"
 #include "kernels.h"
 
@@ -49,13 +55,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // matrix (N rows): block rb covers rows [16 NW rb, 16 NW (rb + 1)).  SwiGLU
 // (gate W0 and up W1, N rows each): block rb covers F rows f0 = 8 NW rb ..
 // f0 + 8 NW, its first NW/2 tiles from gate, the other NW/2 from up.
-template <int MT, int P, int EPI>
+template <int MT, int P, int EPI, bool F8>
 __global__ void __launch_bounds__(1024)
 splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
-              const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int KR,
+              const void* __restrict__ W0, const void* __restrict__ W1,
+              const float* __restrict__ S0, const float* __restrict__ S1, int KR,
               unsigned* __restrict__ counters, float* __restrict__ part, int NR,
               void* __restrict__ out, int64_t ldo) {
   constexpr int TOK = 16 * MT;
+  constexpr int ES = F8 ? 1 : 2;    // bytes per weight
+  constexpr int LPG = F8 ? 2 : 4;   // load instructions per 128-K group
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   __shared__ int is_last;
   const int NW = blockDim.x >> 6;
@@ -85,7 +94,7 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
 
   // ---- this wave's 16 weight rows: uniform base, rows past the matrix read zero
   int wrow0;
-  const uint16_t* wmat;
+  const void* wmat;
   if constexpr (EPI == EPI_SWIGLU) {
     const int half = NW / 2;
     wrow0 = rb * 16 * half + 16 * (wave % half);
@@ -96,21 +105,27 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   }
   const int rows = max(0, min(16, N - wrow0));
   const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(wmat + (int64_t)wrow0 * K, (uint32_t)rows * (uint32_t)K * 2u);
+      make_rsrc(static_cast<const unsigned char*>(wmat) + (int64_t)wrow0 * K * ES,
+                (uint32_t)rows * (uint32_t)K * (uint32_t)ES);
   const int NG = (kend - k0 + kGK - 1) / kGK;
 
-  // group g, instruction p: rows 4p + lane/16, 16-byte chunk lane%16 of the group
-  auto issue = [&](int g, u32x4_t (&v)[4]) {
-    const int k = k0 + g * kGK + (lane & 15) * 8;
+  // group g, instruction p: bf16 rows 4p + lane/16, 16-byte chunk lane%16
+  // (8 K) of the group; FP8 rows 8p + lane/8, 16-byte chunk lane%8 (16 K)
+  auto issue = [&](int g, u32x4_t (&v)[LPG]) {
+    constexpr int KPC = 16 / ES;     // K per 16-byte chunk
+    constexpr int CPR = kGK / KPC;   // chunks per row of a group: 16 (bf16), 8 (FP8)
+    constexpr int RPI = 64 / CPR;    // rows per load instruction: 4, 8
+    static_assert(RPI * LPG == 16, "a group is 16 rows");
+    const int k = k0 + g * kGK + (lane % CPR) * KPC;
     const bool ok = g < NG && k < kend;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t r = 4 * p + (lane >> 4);
-      v[p] = buf_load16<kAuxNT>(wr, ok ? (r * (uint32_t)K + (uint32_t)k) * 2u : kOob);
+    for (int p = 0; p < LPG; ++p) {
+      const uint32_t r = RPI * p + lane / CPR;
+      v[p] = buf_load16<kAuxNT>(wr, ok ? (r * (uint32_t)K + (uint32_t)k) * (uint32_t)ES : kOob);
     }
   };
 
-  u32x4_t wv[P][4];
+  u32x4_t wv[P][LPG];
 #pragma unroll
   for (int b = 0; b < P; ++b) issue(b, wv[b]);
   f32x4_t acc[MT];
@@ -126,11 +141,22 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
     for (int b = 0; b < P; ++b) {
       const int g = g0 + b;
       wait_vmcnt<(P - 1) * 4>();
-      // transpose through the tile: row r = 4p + lane/16 at slot (lane%16) ^ r
+      // transpose through the tile: row r, bf16 chunk c at slot c ^ r
+      if constexpr (F8) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int r = 4 * p + (lane >> 4);
-        *reinterpret_cast<u32x4_t*>(tile + r * 256 + (((lane & 15) ^ r) * 16)) = wv[b][p];
+        for (int p = 0; p < LPG; ++p) {
+          const int r = 8 * p + (lane >> 3), c = 2 * (lane & 7);
+          u32x4_t lo, hi;
+          decode16(wv[b][p], lo, hi);
+          *reinterpret_cast<u32x4_t*>(tile + r * 256 + ((c ^ r) * 16)) = lo;
+          *reinterpret_cast<u32x4_t*>(tile + r * 256 + (((c + 1) ^ r) * 16)) = hi;
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < LPG; ++p) {
+          const int r = 4 * p + (lane >> 4);
+          *reinterpret_cast<u32x4_t*>(tile + r * 256 + (((lane & 15) ^ r) * 16)) = wv[b][p];
+        }
       }
       issue(g + P, wv[b]);  // past the end: out-of-range offsets, nothing fetched
       if (g < NG) {
@@ -207,15 +233,26 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   for (int idx = tid; idx < I * cq; idx += NW * 64) {
     const int m = idx / cq, c = (idx % cq) * 4;
     const int64_t q = (int64_t)m * NR + rs0 + c;
-    const f32x4_t s4 = sum_splits(q);
+    f32x4_t s4 = sum_splits(q);
+    const int n = min(4, ncols - c);
     f32x4_t v;
     if constexpr (EPI == EPI_SWIGLU) {
-      const f32x4_t u = sum_splits(q + cols);
+      f32x4_t u = sum_splits(q + cols);
+      if constexpr (F8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s4[e] *= e < n ? S0[cbase + c + e] : 0.0f;
+          u[e] *= e < n ? S1[cbase + c + e] : 0.0f;
+        }
+      }
       v = f32x4_t{silu(s4.x) * u.x, silu(s4.y) * u.y, silu(s4.z) * u.z, silu(s4.w) * u.w};
     } else {
+      if constexpr (F8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s4[e] *= e < n ? S0[cbase + c + e] : 0.0f;
+      }
       v = s4;
     }
-    const int n = min(4, ncols - c);
     if constexpr (EPI == EPI_F32) {
       float* o = static_cast<float*>(out) + (int64_t)m * ldo + cbase + c;
       if (n == 4 && ((reinterpret_cast<uintptr_t>(o) & 15) == 0)) {
@@ -296,11 +333,11 @@ Plan make_plan(int I, int K, int N, bool swiglu) {
   }
 }
 
-template <int MT, int EPI>
-hipError_t launch_plan(const Plan& pl, int I, int K, int N, const uint16_t* X,
-                       const uint16_t* W0, const uint16_t* W1, void* out, int64_t ldo,
-                       void* workspace, hipStream_t stream) {
-  auto kern = splitk_kernel<MT, 2, EPI>;
+template <int MT, int EPI, bool F8 = false>
+hipError_t launch_plan(const Plan& pl, int I, int K, int N, const uint16_t* X, const void* W0,
+                       const void* W1, void* out, int64_t ldo, void* workspace,
+                       hipStream_t stream, const float* S0 = nullptr, const float* S1 = nullptr) {
+  auto kern = splitk_kernel<MT, F8 ? 4 : 2, EPI, F8>;
   static bool attr_set = false;  // raising the dynamic-LDS limit once per process is enough
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -312,7 +349,7 @@ hipError_t launch_plan(const Plan& pl, int I, int K, int N, const uint16_t* X,
   auto* counters = static_cast<unsigned*>(workspace);
   float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsCounterBytes);
   hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(pl.nw * 64), pl.lds, stream, I, K, N, X, W0, W1,
-                     pl.kr, counters, part, pl.nr, out, ldo);
+                     S0, S1, pl.kr, counters, part, pl.nr, out, ldo);
   return hipGetLastError();
 }
 
@@ -324,6 +361,11 @@ bool splitk_suits(int I, int K, int N, bool swiglu) {
   if (pl.grid == 0) return false;
   // K range cut below half the target by LDS: the tiled kernel does better
   return 2 * (pl.kr / kGK) >= target_groups(K, weight_tiles(N, swiglu));
+}
+
+bool splitk_plannable(int I, int K, int N, bool swiglu) {
+  return I >= 1 && I <= kSplitKMaxTokens && K <= kSplitKMaxK &&
+         make_plan(I, K, N, swiglu).grid > 0;
 }
 
 size_t splitk_workspace_bytes(int I, int K, int N, bool swiglu) {
@@ -349,5 +391,27 @@ template hipError_t splitk_launch<EPI_DT>(int, int, int, const uint16_t*, const 
 template hipError_t splitk_launch<EPI_SWIGLU>(int, int, int, const uint16_t*, const uint16_t*,
                                               const uint16_t*, void*, int64_t, void*,
                                               hipStream_t);
+
+template <int EPI>
+hipError_t splitk_fp8_launch(int I, int K, int N, const uint16_t* X, const uint8_t* W0,
+                             const float* S0, const uint8_t* W1, const float* S1, void* out,
+                             int64_t ldo, void* workspace, hipStream_t stream) {
+  const Plan pl = make_plan(I, K, N, EPI == EPI_SWIGLU);
+  if (pl.grid == 0) return hipErrorInvalidValue;
+#define TPK_F8(MTV) \
+  launch_plan<MTV, EPI, true>(pl, I, K, N, X, W0, W1, out, ldo, workspace, stream, S0, S1)
+  if (I <= 16) return TPK_F8(1);
+  if (I <= 32) return TPK_F8(2);
+  if (I <= 48) return TPK_F8(3);
+  return TPK_F8(4);
+#undef TPK_F8
+}
+
+template hipError_t splitk_fp8_launch<EPI_F32>(int, int, int, const uint16_t*, const uint8_t*,
+                                               const float*, const uint8_t*, const float*, void*,
+                                               int64_t, void*, hipStream_t);
+template hipError_t splitk_fp8_launch<EPI_SWIGLU>(int, int, int, const uint16_t*, const uint8_t*,
+                                                  const float*, const uint8_t*, const float*,
+                                                  void*, int64_t, void*, hipStream_t);
 
 }  // namespace tpk

@@ -177,13 +177,26 @@ def test_attn_decode_validation(lib):
 
 def test_mlp_fp8_validation(lib):
     m = lib.tp_shard_mlp_fp8
-    args = [fake(k) for k in range(10)]  # X, Wg, sg, Wu, su, Wd, sd, H, P, stream
-    args[9] = None
+    # X, Wg, sg, Wu, su, Wd, sd, H, P, workspace, workspace_bytes, stream
+    args = [fake(k) for k in range(9)] + [None, 0, None]
     assert m(0, 64, 128, *args) == OK
     assert m(-1, 64, 128, *args) == INVALID
-    assert m(9, 64, 128, *args) == UNSUPPORTED                       # decode only: I <= 8
+    assert m(65, 64, 128, *args) == UNSUPPORTED                      # decode only: I <= 64
+    assert m(9, 64, 128, *args) == WORKSPACE                         # split K: needs one
     assert m(1, 24, 128, *args) == MISALIGNED                        # D not a multiple of 16
-    assert m(1, 32768, 128, *args) == UNSUPPORTED                    # K above 16384
+    assert m(1, 32768, 128, *args) == WORKSPACE                      # K above 16384: split K
+    assert lib.tp_shard_mlp_fp8_workspace_size(4, 8192, 3584) == 0     # VALU kernel
+    assert lib.tp_shard_mlp_fp8_workspace_size(5, 8192, 3584) > 0      # split K from 5
+    need = lib.tp_shard_mlp_fp8_workspace_size(32, 8192, 3584)
+    assert need > 8192 and lib.tp_shard_mlp_fp8_workspace_size(65, 8192, 3584) == 0
+    small = lib.tp_shard_mlp_fp8_workspace_size(32, 64, 128)
+    ws = list(args)
+    ws[9], ws[10] = ctypes.c_void_p(FAKE + 9 * STEP + 8), small
+    assert m(32, 64, 128, *ws) == MISALIGNED                         # workspace not aligned
+    ws[9] = fake(7)
+    assert m(32, 64, 128, *ws) == INVALID                            # workspace is H
+    ws[9], ws[10] = fake(9), small - 1
+    assert m(32, 64, 128, *ws) == WORKSPACE                          # too small
     bad = list(args)
     bad[2] = None
     assert m(1, 64, 128, *bad) == INVALID                            # missing scale

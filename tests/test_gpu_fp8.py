@@ -1,6 +1,7 @@
 """GPU parity of tp_shard_mlp_fp8 (weight-only FP8 storage, OCP E4M3 with a
 fp32 scale per output row; bf16 activations) against the fp64 oracle on the
-dequantized weights.  Bar: normwise 2e-2 (bf16 inputs and H, fp32 sums)."""
+dequantized weights: the few-token kernel (1..8 tokens) and the split-K MFMA
+kernel (9..64).  Bar: normwise 2e-2 (bf16 inputs and H, fp32 sums)."""
 import numpy as np
 import pytest
 
@@ -30,10 +31,10 @@ def _run(X, shards):
     return to_host(H), to_host(P)
 
 
-def _reference(orc, X, shards):
+def _reference(orc, X, shards, rows=None):
     (cg, sg), (cu, su), (cd, sd) = shards
     return orc.mlp_full(X, orc.dequant_fp8(cg, sg), orc.dequant_fp8(cu, su),
-                        orc.dequant_fp8(cd, sd))
+                        orc.dequant_fp8(cd, sd), rows=rows)
 
 
 def _shards(D, Fl, pool):
@@ -59,7 +60,20 @@ def test_llama_rank_share_decode(orc, llama_fp8, I):
     assert normwise_err(P, P_ref) <= TOL
 
 
-@pytest.mark.parametrize("I", [1, 8])
+@pytest.mark.parametrize("I", [16, 32, 64])
+def test_llama_rank_share_split_k(orc, llama_fp8, I):
+    """9..64 tokens: the split-K MFMA kernel on the same rank share; sampled
+    rows (first, middle, last) against the oracle."""
+    D = 8192
+    X = datagen.gaussian("X", (I, D), 1.0, "bf16", 640 + I)
+    H, P = _run(X, llama_fp8)
+    rows = sorted({0, I // 2, I - 1})
+    H_ref, P_ref = _reference(orc, X, llama_fp8, rows=rows)
+    assert normwise_err(H[rows], H_ref) <= TOL
+    assert normwise_err(P[rows], P_ref) <= TOL
+
+
+@pytest.mark.parametrize("I", [1, 8, 24])
 def test_qwen_tp2_partials_sum_to_layer(orc, I):
     """Qwen2.5-1.5B MLP (D = 1536, F = 8960) at TP=2: each rank's FP8 share
     against the oracle, and the two partials sum to the unsharded layer."""
@@ -78,9 +92,12 @@ def test_qwen_tp2_partials_sum_to_layer(orc, I):
     assert normwise_err(Ps[0] + Ps[1], Y_ref) <= TOL
 
 
-@pytest.mark.parametrize("I,D,Fl", [(3, 16, 16), (5, 48, 80), (8, 1040, 272), (1, 16384, 16)])
+@pytest.mark.parametrize("I,D,Fl", [(3, 16, 16), (5, 48, 80), (8, 1040, 272), (1, 16384, 16),
+                                    (9, 48, 80), (17, 1040, 272), (40, 272, 1040),
+                                    (64, 1536, 4480), (2, 32768, 64)])
 def test_small_and_ragged_shapes(orc, I, D, Fl):
-    """K of one 16-byte chunk, chunks not filling a wave, two chunks per lane."""
+    """K of one 16-byte chunk, chunks not filling a wave, two chunks per lane;
+    split K with ragged K ranges and row tiles; K past the few-token limit."""
     shards = _shards(D, Fl, 62)
     X = datagen.gaussian("X", (I, D), 1.0, "bf16", 620 + I)
     H, P = _run(X, shards)
@@ -95,7 +112,10 @@ def test_deterministic_and_unsupported(orc):
     X = datagen.gaussian("X", (8, D), 1.0, "bf16", 630)
     a, b = _run(X, shards), _run(X, shards)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
-    X9 = to_dev(datagen.gaussian("X", (9, D), 1.0, "bf16", 631), "bf16")
+    X33 = datagen.gaussian("X", (33, D), 1.0, "bf16", 632)  # split K: fixed summation order
+    a, b = _run(X33, shards), _run(X33, shards)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    X65 = to_dev(datagen.gaussian("X", (65, D), 1.0, "bf16", 631), "bf16")
     with pytest.raises(tp.TPError, match="UNSUPPORTED"):
-        tp.shard_mlp_fp8(X9, *(_dev_fp8(s) for s in shards), empty((9, Fl), "bf16"),
-                         empty((9, D), "f32"))
+        tp.shard_mlp_fp8(X65, *(_dev_fp8(s) for s in shards), empty((65, Fl), "bf16"),
+                         empty((65, D), "f32"))
