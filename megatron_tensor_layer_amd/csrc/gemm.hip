@@ -49,40 +49,8 @@ constexpr int kCUs = 256;
 static_assert(4 * 16 * 64 * 4 <= kStageA, "a wave pair's K-group reduction fits one stage buffer");
 static_assert(4 * kStageA + 4 <= kLds, "the arrival flag follows the reduction area");
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
-}
-
 __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
-}
-
-// Buffer descriptor words (raw addressing over [base, base + bytes)); kept
-// in SGPRs for the asm load below.
-__device__ __forceinline__ u32x4_t rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return u32x4_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
-}
-
-// 16 bytes per lane from buffer offset `voff` straight into LDS at
-// lds_base + 16 * lane (buffer_load_dwordx4 ... lds; M0 holds lds_base).
-// Written as asm so that the compiler does not add its own wait for it before
-// every LDS read: the kernel orders these loads itself, with an explicit
-// vmcnt wait and a barrier before the stage they fill is read.  No register
-// is written, so nothing in flight can be overwritten.
-__device__ __forceinline__ void lds_dma16(u32x4_t rsrc, uint32_t voff, uint32_t lds_base) {
-  asm volatile(
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %1, 0 offen lds"
-      :
-      : "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
-      : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
 // LDS byte offset of (row, logical 16-byte chunk) inside one operand tile.

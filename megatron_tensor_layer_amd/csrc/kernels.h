@@ -63,6 +63,17 @@ hipError_t splitk_fp8_launch(int I, int K, int N, const uint16_t* X, const uint8
                              const float* S0, const uint8_t* W1, const float* S1, void* out,
                              int64_t ldo, void* workspace, hipStream_t stream);
 
+// Same product for 9..32 tokens with each workgroup covering the whole K
+// axis of two 16-row weight tiles (no workspace); rowstream_suits says when
+// it beats the split-K kernel.
+constexpr int kRowStreamMaxTokens = 32;
+constexpr int kRowStreamMaxK = 1 << 20;
+int rowstream_slice(int K);
+bool rowstream_suits(int I, int K, int N, bool swiglu);
+template <int EPI>
+hipError_t rowstream_launch(int I, int K, int N, const uint16_t* X, const uint16_t* W0,
+                            const uint16_t* W1, void* out, int64_t ldo, hipStream_t stream);
+
 // Same product on bf16 MFMA for any M (128 x 128 tiles).  When the tiles
 // cannot fill the chip, K is split over workgroups and `workspace`
 // (gemm_workspace_bytes, 0 when not split) holds the arrival counters and

@@ -1,0 +1,274 @@
+// Decode projections for 9..32 tokens whose weight matrix has enough rows to
+// give every CU its own: y[m, n] = sum_k X[m, k] W[n, k] on bf16 MFMA, each
+// workgroup covering the whole K axis of its rows, so no partial sums leave
+// the workgroup.
+//
+// Decode reads each weight of the rank's shard once per step (lecture
+// "Distributed Serving", §1.1 and §3.4).  Splitting K over workgroups lets
+// each stage a slice of the activations once, but its cross-workgroup finish
+// (partials written, one atomic, the last arrival reading them back) is a
+// chain of dependent memory round trips at the end of the kernel.  Here:
+//   * a workgroup owns two 16-row weight tiles (a gate tile and the up tile
+//     of the same 16 F rows for SwiGLU) and eight waves: wave w streams tile
+//     w % 2 over K slice w / 2 of four, rows whole cache lines at a time (one
+//     load instruction: 4 rows x 256 contiguous bytes), two groups of 128 K
+//     in flight, each group transposed through a private 4 KB LDS tile into
+//     the B operand of v_mfma_f32_16x16x32_bf16;
+//   * the activations stream through LDS in chunks of 256 K per slice,
+//     double-buffered, by direct global->LDS copies (16-byte slots
+//     XOR-swizzled by token); every CU reads all of X, which at these token
+//     counts is no more than its share of the weights;
+//   * the four K slices of a tile are summed through LDS in slice order
+//     (deterministic) and stored with the epilogue (fp32, bf16, silu(g) * u).
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace tpk {
+
+namespace {
+
+constexpr int kGK = 128;        // K per streamed weight group
+constexpr int kKC = 256;        // K per activation chunk (two groups)
+constexpr int kKW = 4;          // K slices per workgroup
+constexpr int kTiles = 2;       // 16-row weight tiles per workgroup
+constexpr int kWaves = kKW * kTiles;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTileBytes = 16 * kGK * 2;   // one wave's transpose tile
+constexpr uint32_t kOob = 0x80000000u;
+
+template <int MT>
+constexpr int xslice_bytes() { return 16 * MT * kKC * 2; }          // one slice's chunk
+template <int MT>
+constexpr int xbuf_bytes() { return kKW * xslice_bytes<MT>(); }      // one chunk of all slices
+template <int MT>
+constexpr int lds_bytes() { return 2 * xbuf_bytes<MT>() + kWaves * kTileBytes; }
+static_assert(lds_bytes<2>() <= 160 * 1024, "two chunks of 32 tokens and the tiles fit LDS");
+
+// X DMA instructions per wave per chunk: each slice's chunk is 16 MT token
+// rows of 512 bytes = 8 MT instructions of 1 KB.
+template <int MT>
+constexpr int xpw() { return kKW * 8 * MT / kWaves; }
+
+template <int MT, int EPI, int P>
+__global__ void __launch_bounds__(kThreads)
+rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
+                 const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int KS,
+                 void* __restrict__ out, int64_t ldo) {
+  constexpr int XPW = xpw<MT>();
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tw = wave & 1, sl = wave >> 1;  // tile, K slice
+  unsigned char* tile = lds + 2 * xbuf_bytes<MT>() + wave * kTileBytes;
+
+  // ---- this wave's 16 weight rows; rows past the matrix read zero
+  int wrow0;
+  const uint16_t* wmat;
+  if constexpr (EPI == EPI_SWIGLU) {
+    wrow0 = blockIdx.x * 16;  // the same F rows of gate (tile 0) and up (tile 1)
+    wmat = tw == 0 ? W0 : W1;
+  } else {
+    wrow0 = blockIdx.x * 32 + tw * 16;
+    wmat = W0;
+  }
+  const int rows = max(0, min(16, N - wrow0));
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(wmat + (int64_t)wrow0 * K, (uint32_t)rows * (uint32_t)K * 2u);
+  const int kb = sl * KS, ke = min(K, kb + KS);  // this wave's K slice
+  const int NC = KS / kKC;                       // chunks per slice (same for all)
+  const int NG = 2 * NC;
+
+  // group g of the slice, instruction p: rows 4p + lane/16, chunk lane%16
+  auto issue_w = [&](int g, u32x4_t (&v)[4]) {
+    const int k = kb + g * kGK + (lane & 15) * 8;
+    const bool ok = g < NG && k < ke;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t r = 4 * p + (lane >> 4);
+      v[p] = buf_load16<kAuxNT>(wr, ok ? (r * (uint32_t)K + (uint32_t)k) * 2u : kOob);
+    }
+  };
+
+  // chunk c of every slice into buffer c & 1: instruction q of the chunk
+  // covers slice q / (8 MT), token rows 2 (q % (8 MT)) + lane / 32; lane
+  // fills slot lane % 32 of its row with chunk slot ^ (token & 15).  Chunks
+  // past the end (and tokens past I) are zero-filled.
+  const u32x4_t xr = rsrc_words(X, (uint32_t)I * (uint32_t)K * 2u);
+  const uint32_t lx = lds_addr(lds);
+  auto issue_x = [&](int c) {
+    const uint32_t base = lx + (c & 1) * xbuf_bytes<MT>();
+#pragma unroll
+    for (int h = 0; h < XPW; ++h) {
+      const int q = wave + h * kWaves;
+      const int s = q / (8 * MT);
+      const int t = 2 * (q % (8 * MT)) + (lane >> 5);
+      const int slot = lane & 31;
+      const int k = s * KS + c * kKC + ((slot ^ (t & 15)) * 8);
+      const bool ok = c < NC && t < I && k < min(K, (s + 1) * KS);
+      lds_dma16(xr, ok ? ((uint32_t)t * (uint32_t)K + (uint32_t)k) * 2u : kOob, base + q * 1024);
+    }
+  };
+
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t wv[P][4];
+
+  // P weight groups are in flight per wave (P = 2: one chunk ahead, 4: two).
+  // Order of this wave's loads: W(0 .. P-3), X(0), W(P-2), W(P-1), then per
+  // chunk step c: X(c + 1) and, as groups 2c and 2c + 1 are consumed,
+  // W(2c + P) and W(2c + P + 1).  So X(c) is always followed by exactly two
+  // weight groups and W(g) by 4 (P - 1) + 2 XPW (P = 4) or 4 + XPW (P = 2)
+  // loads.  Past the end the offsets are out of range (zero, nothing
+  // fetched), so the counts never change.
+  static_assert(P == 2 || P == 4, "two or four groups in flight");
+  constexpr int kAfterW = P == 4 ? 12 + 2 * XPW : 4 + XPW;
+#pragma unroll
+  for (int g = 0; g < P - 2; ++g) issue_w(g, wv[g]);
+  issue_x(0);
+  issue_w(P - 2, wv[P - 2]);
+  issue_w(P - 1, wv[P - 1]);
+  // one chunk step; `par` = c % 2 is a constant in each unrolled copy, so the
+  // weight register set of each group is known at compile time
+  auto step = [&](int c, auto par) {
+    wait_vmcnt<8>();  // X(c) has landed: only the two groups after it may not
+    __syncthreads();  // everyone's part of X(c); chunk c - 1's buffer is free
+    issue_x(c + 1);
+    const unsigned char* xs = lds + (c & 1) * xbuf_bytes<MT>() + sl * xslice_bytes<MT>();
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int g = 2 * c + b;
+      u32x4_t (&w)[4] = wv[(2 * decltype(par)::value + b) % P];
+      wait_vmcnt<kAfterW>();  // W(g) has landed
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int r = 4 * p + (lane >> 4);
+        *reinterpret_cast<u32x4_t*>(tile + r * 256 + (((lane & 15) ^ r) * 16)) = w[p];
+      }
+      issue_w(g + P, w);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = lane & 15, ch = 4 * j + (lane >> 4);
+        const bf16x8_t bw = *reinterpret_cast<const bf16x8_t*>(tile + n * 256 + ((ch ^ n) * 16));
+        const int xc = b * 16 + ch;  // 16-byte chunk within the 256-K chunk
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int t = mt * 16 + (lane & 15);
+          const bf16x8_t ax =
+              *reinterpret_cast<const bf16x8_t*>(xs + t * (kKC * 2) + ((xc ^ (t & 15)) * 16));
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ax, bw, acc[mt], 0, 0, 0);
+        }
+      }
+    }
+  };
+  for (int c = 0; c < NC; c += 2) {
+    step(c, std::integral_constant<int, 0>{});
+    if (c + 1 < NC) step(c + 1, std::integral_constant<int, 1>{});
+  }
+
+  // ---- the four slices of each tile, summed in slice order through LDS
+  wait_vmcnt<0>();  // the zero-fill copies past the end have landed
+  __syncthreads();
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds);  // [wave][mt][lane]
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * 64 + lane] = acc[mt];
+  __syncthreads();
+  if (wave >= kTiles) return;
+  // wave tw: tile tw's sums; C[m = 4 (lane / 16) + e][n = lane % 16]
+  f32x4_t sum[kTiles][MT];
+#pragma unroll
+  for (int t2 = 0; t2 < kTiles; ++t2)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4_t s4 = red[((t2 + 0 * kTiles) * MT + mt) * 64 + lane];
+#pragma unroll
+      for (int s = 1; s < kKW; ++s) s4 += red[((t2 + s * kTiles) * MT + mt) * 64 + lane];
+      sum[t2][mt] = s4;
+    }
+  if constexpr (EPI == EPI_SWIGLU) {
+    if (wave != 0) return;
+    const int col = blockIdx.x * 16 + (lane & 15);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = mt * 16 + (lane >> 4) * 4 + e;
+        if (m < I && col < N)
+          static_cast<uint16_t*>(out)[(int64_t)m * ldo + col] =
+              f32_to_bf16_bits(silu(sum[0][mt][e]) * sum[1][mt][e]);
+      }
+  } else {
+    const int col = blockIdx.x * 32 + wave * 16 + (lane & 15);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = mt * 16 + (lane >> 4) * 4 + e;
+        const float v = wave == 0 ? sum[0][mt][e] : sum[1][mt][e];
+        if (m < I && col < N) {
+          if constexpr (EPI == EPI_F32)
+            static_cast<float*>(out)[(int64_t)m * ldo + col] = v;
+          else
+            static_cast<uint16_t*>(out)[(int64_t)m * ldo + col] = f32_to_bf16_bits(v);
+        }
+      }
+  }
+}
+
+template <int MT, int EPI>
+hipError_t launch_mt(int I, int K, int N, const uint16_t* X, const uint16_t* W0,
+                     const uint16_t* W1, void* out, int64_t ldo, hipStream_t stream) {
+  auto kern = rowstream_kernel<MT, EPI, 2>;  // 4 groups in flight measured slower
+  static bool attr_set = false;  // raising the dynamic-LDS limit once per process is enough
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes<MT>());
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int KS = rowstream_slice(K);
+  const int grid = EPI == EPI_SWIGLU ? (N + 15) / 16 : (N + 31) / 32;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds_bytes<MT>(), stream, I, K, N, X, W0,
+                     W1, KS, out, ldo);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int rowstream_slice(int K) {  // K per slice: whole 256-K chunks
+  const int per = (K + kKW - 1) / kKW;
+  return (per + kKC - 1) / kKC * kKC;
+}
+
+// Measured against the split-K kernel on MI355X at 9..32 tokens: faster
+// whenever the grid fills the chip (N / 32 >= 240 rows pairs: Llama-70B
+// o_proj 7.5 us against 9.2 at 32 tokens, down 15.3 against 16.5) or K is
+// short enough for the split-K finish to dominate (K <= 4096); slower for
+// the TP=8 gate/up (K = 8192 on 224 workgroups: 28.6 against 27.2), whose
+// per-CU stream, not the finish, is the limit.
+bool rowstream_suits(int I, int K, int N, bool swiglu) {
+  if (I < 9 || I > kRowStreamMaxTokens || K < 1024 || K > kRowStreamMaxK) return false;
+  const int grid = swiglu ? (N + 15) / 16 : (N + 31) / 32;
+  if (grid < 128 || grid > 256) return false;  // about one workgroup per CU
+  return grid >= 240 || K <= 4096;
+}
+
+template <int EPI>
+hipError_t rowstream_launch(int I, int K, int N, const uint16_t* X, const uint16_t* W0,
+                            const uint16_t* W1, void* out, int64_t ldo, hipStream_t stream) {
+  if (I < 1 || I > kRowStreamMaxTokens || K < 1 || K > kRowStreamMaxK || N < 1)
+    return hipErrorInvalidValue;
+  if (I <= 16) return launch_mt<1, EPI>(I, K, N, X, W0, W1, out, ldo, stream);
+  return launch_mt<2, EPI>(I, K, N, X, W0, W1, out, ldo, stream);
+}
+
+template hipError_t rowstream_launch<EPI_F32>(int, int, int, const uint16_t*, const uint16_t*,
+                                              const uint16_t*, void*, int64_t, hipStream_t);
+template hipError_t rowstream_launch<EPI_DT>(int, int, int, const uint16_t*, const uint16_t*,
+                                             const uint16_t*, void*, int64_t, hipStream_t);
+template hipError_t rowstream_launch<EPI_SWIGLU>(int, int, int, const uint16_t*, const uint16_t*,
+                                                 const uint16_t*, void*, int64_t, hipStream_t);
+
+}  // namespace tpk

@@ -45,12 +45,6 @@ constexpr int kGK = 128;                // K elements per streamed group
 constexpr int kLdsMax = 160 * 1024 - 1024;  // dynamic LDS budget (static LDS sits before it)
 constexpr int kCUs = 256;
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
-}
-
 // Row space of the partial sums: row block rb holds NW 16-row tiles.  Single
 // matrix (N rows): block rb covers rows [16 NW rb, 16 NW (rb + 1)).  SwiGLU
 // (gate W0 and up W1, N rows each): block rb covers F rows f0 = 8 NW rb ..

@@ -38,12 +38,15 @@ bool dims_ok(int64_t v) { return v >= 1 && v <= kMaxDim; }
 tp_status_t launched(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_LAUNCH; }
 
 // Kernel family for a bf16 projection of I tokens with contraction length K.
-enum class Path { Gemv, SplitK, Gemm };
+enum class Path { Gemv, RowStream, SplitK, Gemm };
 Path bf16_path(int64_t I, int64_t K, int64_t N, bool swiglu) {
   // few tokens: weight streaming on VALU; past K = kGemvMaxK16 / 2 the
   // 8-token variant runs out of registers, so 5..8 tokens go to MFMA there
   const int64_t kmax = (I <= 4) ? tpk::kGemvMaxK16 : tpk::kGemvMaxK16 / 2;
   if (I <= tpk::kGemvMaxTokens && K <= kmax) return Path::Gemv;
+  if (I <= tpk::kRowStreamMaxTokens && K <= tpk::kRowStreamMaxK && N <= INT32_MAX &&
+      tpk::rowstream_suits((int)I, (int)K, (int)N, swiglu))
+    return Path::RowStream;
   if (I <= tpk::kSplitKMaxTokens && K <= tpk::kSplitKMaxK &&
       tpk::splitk_suits((int)I, (int)K, (int)N, swiglu))
     return Path::SplitK;
@@ -55,6 +58,7 @@ size_t proj_workspace(int64_t I, int64_t K, int64_t N, bool swiglu, tp_dtype_t d
   if (dt != TP_BF16 || I < 1) return 0;
   switch (bf16_path(I, K, N, swiglu)) {
     case Path::Gemv: return 0;
+    case Path::RowStream: return 0;
     case Path::SplitK: return tpk::splitk_workspace_bytes((int)I, (int)K, (int)N, swiglu);
     case Path::Gemm: return tpk::gemm_workspace_bytes((int)I, (int)N, (int)K, swiglu);
   }
@@ -76,6 +80,8 @@ hipError_t project(int64_t I, int64_t K, int64_t N, tp_dtype_t dt, const void* i
     switch (bf16_path(I, K, N, EPI == tpk::EPI_SWIGLU)) {
       case Path::Gemv:
         return gemv_launch<uint16_t, EPI>((int)I, (int)K, (int)N, X, K, A0, A1, out, N, s);
+      case Path::RowStream:
+        return tpk::rowstream_launch<EPI>((int)I, (int)K, (int)N, X, A0, A1, out, N, s);
       case Path::SplitK:
         return tpk::splitk_launch<EPI>((int)I, (int)K, (int)N, X, A0, A1, out, N, ws, s);
       case Path::Gemm:

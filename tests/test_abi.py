@@ -221,7 +221,8 @@ def test_workspace_queries_are_host_only(lib):
     assert ws(0, 8192, 3584, tp.TP_BF16) == 0 and ws(32, 0, 3584, tp.TP_BF16) == 0
     wa = lib.tp_shard_attn_proj_workspace_size
     assert wa(tp.TP_ATTN_QKV, 32, 8192, 8, 1, 128, tp.TP_BF16) > 0
-    assert wa(tp.TP_ATTN_O, 32, 8192, 8, 1, 128, tp.TP_BF16) > 0
+    assert wa(tp.TP_ATTN_O, 32, 8192, 8, 1, 128, tp.TP_BF16) == 0   # whole-K row blocks
+    assert wa(tp.TP_ATTN_O, 32, 1536, 6, 1, 128, tp.TP_BF16) > 0    # split K (Qwen o_proj)
     assert wa(tp.TP_ATTN_QKV, 1, 8192, 8, 1, 128, tp.TP_BF16) == 0
     assert wa(7, 32, 8192, 8, 1, 128, tp.TP_BF16) == 0
 

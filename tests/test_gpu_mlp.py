@@ -27,7 +27,7 @@ def gpu_mlp(X, Wg_r, Wu_r, Wd_r, dtype):
     return H, P
 
 
-# (I, D, F_local, t, r, dtype): few-token kernel (I <= 8), MFMA kernel (I > 8),
+# (I, D, F_local, t, r, dtype): few-token kernel (I <= 8), MFMA kernels (I > 8),
 # weight-streaming MFMA kernel (9..64 tokens), ragged K tiles and steps
 # (D = 264, 520, 1000), ragged F tiles (F_local = 200, 328, 136, 24, 1000),
 # long K (lanes holding 4 and 8 chunks), the fp32 path in 8- and 4-token launches
@@ -39,6 +39,9 @@ SMALL = [
     (64, 136, 72, 2, 1, "bf16"), (65, 264, 200, 1, 0, "bf16"), (130, 520, 136, 2, 1, "bf16"),
     (257, 264, 200, 2, 1, "bf16"), (33, 72, 24, 2, 1, "bf16"), (48, 1000, 1000, 1, 0, "bf16"),
     (16, 2048, 4096, 1, 0, "bf16"),
+    # whole-K row blocks (9..32 tokens, 128..256 workgroups): gate/up with a
+    # ragged last K slice, down with a ragged last row block, a full grid
+    (20, 1040, 2064, 1, 0, "bf16"), (9, 4104, 1032, 1, 0, "bf16"), (32, 1024, 4096, 1, 0, "bf16"),
     (4, 256, 512, 2, 0, "f32"), (11, 264, 200, 2, 1, "f32"), (3, 9216, 64, 1, 0, "f32"),
 ]
 
