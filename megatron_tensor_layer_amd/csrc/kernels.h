@@ -69,6 +69,8 @@ hipError_t splitk_fp8_launch(int I, int K, int N, const uint16_t* X, const uint8
 constexpr int kRowStreamMaxTokens = 32;
 constexpr int kRowStreamMaxK = 1 << 20;
 int rowstream_slice(int K);
+int rowstream_rows(int N, bool swiglu);
+int rowstream_grid(int N, bool swiglu);
 bool rowstream_suits(int I, int K, int N, bool swiglu);
 template <int EPI>
 hipError_t rowstream_launch(int I, int K, int N, const uint16_t* X, const uint16_t* W0,

@@ -8,8 +8,9 @@
 // each stage a slice of the activations once, but its cross-workgroup finish
 // (partials written, one atomic, the last arrival reading them back) is a
 // chain of dependent memory round trips at the end of the kernel.  Here:
-//   * a workgroup owns two 16-row weight tiles (a gate tile and the up tile
-//     of the same 16 F rows for SwiGLU) and eight waves: wave w streams tile
+//   * a workgroup owns two weight tiles of up to 16 rows (a gate tile and the
+//     up tile of the same F rows for SwiGLU), as few rows as give about one
+//     workgroup per CU, and eight waves: wave w streams tile
 //     w % 2 over K slice w / 2 of four, rows whole cache lines at a time (one
 //     load instruction: 4 rows x 256 contiguous bytes), two groups of 128 K
 //     in flight, each group transposed through a private 4 KB LDS tile into
@@ -37,6 +38,7 @@ constexpr int kWaves = kKW * kTiles;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileBytes = 16 * kGK * 2;   // one wave's transpose tile
 constexpr uint32_t kOob = 0x80000000u;
+constexpr int kCUs = 256;
 
 template <int MT>
 constexpr int xslice_bytes() { return 16 * MT * kKC * 2; }          // one slice's chunk
@@ -55,7 +57,7 @@ template <int MT, int EPI, int P>
 __global__ void __launch_bounds__(kThreads)
 rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
                  const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int KS,
-                 void* __restrict__ out, int64_t ldo) {
+                 int RPT, void* __restrict__ out, int64_t ldo) {
   constexpr int XPW = xpw<MT>();
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -63,17 +65,18 @@ rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   const int tw = wave & 1, sl = wave >> 1;  // tile, K slice
   unsigned char* tile = lds + 2 * xbuf_bytes<MT>() + wave * kTileBytes;
 
-  // ---- this wave's 16 weight rows; rows past the matrix read zero
+  // ---- this wave's RPT (<= 16) weight rows, padded to a 16-row MFMA tile;
+  //      rows past RPT or past the matrix read zero and fetch nothing
   int wrow0;
   const uint16_t* wmat;
   if constexpr (EPI == EPI_SWIGLU) {
-    wrow0 = blockIdx.x * 16;  // the same F rows of gate (tile 0) and up (tile 1)
+    wrow0 = blockIdx.x * RPT;  // the same F rows of gate (tile 0) and up (tile 1)
     wmat = tw == 0 ? W0 : W1;
   } else {
-    wrow0 = blockIdx.x * 32 + tw * 16;
+    wrow0 = (blockIdx.x * 2 + tw) * RPT;
     wmat = W0;
   }
-  const int rows = max(0, min(16, N - wrow0));
+  const int rows = max(0, min(RPT, N - wrow0));
   const __amdgpu_buffer_rsrc_t wr =
       make_rsrc(wmat + (int64_t)wrow0 * K, (uint32_t)rows * (uint32_t)K * 2u);
   const int kb = sl * KS, ke = min(K, kb + KS);  // this wave's K slice
@@ -187,9 +190,11 @@ rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
       for (int s = 1; s < kKW; ++s) s4 += red[((t2 + s * kTiles) * MT + mt) * 64 + lane];
       sum[t2][mt] = s4;
     }
+  const int n = lane & 15;  // tile row of this lane's sums
+  if (n >= RPT) return;
   if constexpr (EPI == EPI_SWIGLU) {
     if (wave != 0) return;
-    const int col = blockIdx.x * 16 + (lane & 15);
+    const int col = blockIdx.x * RPT + n;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -200,7 +205,7 @@ rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
               f32_to_bf16_bits(silu(sum[0][mt][e]) * sum[1][mt][e]);
       }
   } else {
-    const int col = blockIdx.x * 32 + wave * 16 + (lane & 15);
+    const int col = (blockIdx.x * 2 + wave) * RPT + n;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -229,13 +234,27 @@ hipError_t launch_mt(int I, int K, int N, const uint16_t* X, const uint16_t* W0,
     attr_set = true;
   }
   const int KS = rowstream_slice(K);
-  const int grid = EPI == EPI_SWIGLU ? (N + 15) / 16 : (N + 31) / 32;
+  const int rpt = rowstream_rows(N, EPI == EPI_SWIGLU);
+  const int grid = rowstream_grid(N, EPI == EPI_SWIGLU);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds_bytes<MT>(), stream, I, K, N, X, W0,
-                     W1, KS, out, ldo);
+                     W1, KS, rpt, out, ldo);
   return hipGetLastError();
 }
 
 }  // namespace
+
+// Rows per weight tile: the fewest (at most 16) that give about one
+// workgroup per CU -- 14 for the Llama-70B TP=8 gate/up (3584 F rows on 256
+// workgroups instead of 224 of 16).
+int rowstream_rows(int N, bool swiglu) {
+  const int per_wg = (N + kCUs - 1) / kCUs;  // rows of each matrix per workgroup
+  return std::min(16, swiglu ? per_wg : (per_wg + 1) / 2);
+}
+
+int rowstream_grid(int N, bool swiglu) {
+  const int rpt = rowstream_rows(N, swiglu);
+  return swiglu ? (N + rpt - 1) / rpt : (N + 2 * rpt - 1) / (2 * rpt);
+}
 
 int rowstream_slice(int K) {  // K per slice: whole 256-K chunks
   const int per = (K + kKW - 1) / kKW;
@@ -243,16 +262,17 @@ int rowstream_slice(int K) {  // K per slice: whole 256-K chunks
 }
 
 // Measured against the split-K kernel on MI355X at 9..32 tokens: faster
-// whenever the grid fills the chip (N / 32 >= 240 rows pairs: Llama-70B
-// o_proj 7.5 us against 9.2 at 32 tokens, down 15.3 against 16.5) or K is
-// short enough for the split-K finish to dominate (K <= 4096); slower for
-// the TP=8 gate/up (K = 8192 on 224 workgroups: 28.6 against 27.2), whose
-// per-CU stream, not the finish, is the limit.
+// when K is short enough for the split-K finish to dominate (Llama-70B TP=8
+// o_proj, K = 1024: 7.0 us against 9.2 at 32 tokens; down, K = 3584: 15.3
+// against 16.4), slower for the TP=8 gate/up (K = 8192: 28.6 against 27.3
+// on 224 workgroups of 16 rows, 30.0 on 256 of 14), where every CU
+// streaming all of X costs more than the finish saves.
 bool rowstream_suits(int I, int K, int N, bool swiglu) {
-  if (I < 9 || I > kRowStreamMaxTokens || K < 1024 || K > kRowStreamMaxK) return false;
-  const int grid = swiglu ? (N + 15) / 16 : (N + 31) / 32;
-  if (grid < 128 || grid > 256) return false;  // about one workgroup per CU
-  return grid >= 240 || K <= 4096;
+  if (I < 9 || I > kRowStreamMaxTokens || K < 1024 || K > 4096) return false;
+  // every CU reads all of X: keep a workgroup's weight rows (2 tiles) at
+  // least half its activation rows' worth, i.e. tiles of at least 8 rows
+  if (rowstream_rows(N, swiglu) < 8) return false;
+  return rowstream_grid(N, swiglu) <= kCUs;  // one round of workgroups
 }
 
 template <int EPI>
