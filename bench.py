@@ -106,12 +106,15 @@ def stats(us):
                 p90_us=round(q(0.9), 2))
 
 
-def src_hash(files=None):
-    """Hash of the kernel sources (all of csrc by default): stored counter
-    figures are used only while the kernels they were taken on are unchanged."""
-    if files is None:
-        files = sorted(str(p.relative_to(ROOT)) for p in
-                       (ROOT / "megatron_tensor_layer_amd" / "csrc").iterdir() if p.is_file())
+# Sources of everything a decode-size tp_shard_mlp call runs: the dispatch, the
+# split-K gate/up kernel, the whole-K row-stream down kernel and their headers.
+MLP_DECODE_SOURCES = tuple(f"megatron_tensor_layer_amd/csrc/{f}" for f in (
+    "tpshard_api.cpp", "kernels.h", "common.h", "splitk.hip", "rowstream.hip"))
+
+
+def src_hash(files=MLP_DECODE_SOURCES):
+    """Hash of the sources the counted kernels are built from: stored counter
+    figures are used only while those kernels are unchanged."""
     h = hashlib.sha256()
     for f in files:
         h.update((ROOT / f).read_bytes())

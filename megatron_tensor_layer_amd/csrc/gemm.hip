@@ -329,15 +329,17 @@ constexpr int kStageBA = BB * kRowBB;            // 16 KB
 constexpr int kStageB = 2 * kStageBA;            // 32 KB
 constexpr int SB = 5;
 constexpr int kLdsB = SB * kStageB;              // 160 KB
-constexpr int kInstB = kStageB / 1024 / 8;       // copy instructions per wave per stage
-static_assert(kInstB == 4, "four 1 KB copies per wave per stage");
 
 __device__ __forceinline__ int lds_off64(int row, int chunk) {
   return row * kRowBB + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
-template <int EPI>
-__global__ void __launch_bounds__(kThreads)
+// NWB waves: 8 in a 2 x 4 grid of 128 x 64 wave tiles (used), or 4 in a
+// 2 x 2 grid of 128 x 128 -- a third fewer LDS bytes per MFMA at one wave per
+// SIMD, but measured 3-4 % slower at 512 tokens (TP=1 gate/up 605 us
+// against 582), so only the 8-wave form is launched.
+template <int EPI, int NWB>
+__global__ void __launch_bounds__(NWB * 64)
 gemm_big_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
                 const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
                 void* __restrict__ out, int64_t ldo, int KR, unsigned* __restrict__ counters,
@@ -347,7 +349,11 @@ gemm_big_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
+  constexpr int WNW = NWB / 2;              // waves along N
+  constexpr int NF = 8 / WNW;               // 32-column fragments per wave: 2 or 4
+  constexpr int kInstB = 32 / NWB;          // copy instructions per wave per stage
+  constexpr int kThr = NWB * 64;
+  const int wm = wave / WNW, wn = wave % WNW;
 
   const int mt_n = (M + BB - 1) / BB;
   constexpr int kCols = (EPI == EPI_SWIGLU) ? BB / 2 : BB;  // output columns per tile
@@ -371,9 +377,9 @@ gemm_big_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda
                                  (uint32_t)wrows * (uint32_t)K * 2u);
 
   // Stage st into buffer buf: 32 instructions of 1 KB (16 tile rows each),
-  // 16 for A then 16 for W; wave w issues instructions w, w + 8, w + 16 and
-  // w + 24.  Lane l fills slot l % 4 of row 16 q + l / 4 with the logical
-  // chunk that lds_off64 places there.
+  // 16 for A then 16 for W; wave w issues instructions w, w + NWB, ...
+  // Lane l fills slot l % 4 of row 16 q + l / 4 with the logical chunk that
+  // lds_off64 places there.
   const int rr = lane >> 2, sl = lane & 3;
   const uint32_t lsm = lds_addr(smem);
   auto issue = [&](int st, int buf) {
@@ -381,12 +387,12 @@ gemm_big_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda
     const int k0 = kb + st * BKB;
 #pragma unroll
     for (int h = 0; h < kInstB; ++h) {
-      const int q = wave + h * 8;             // 0..31; h < 2: A rows, else W rows
+      const int q = wave + h * NWB;           // 0..31; q < 16: A rows, else W rows
       const int r = (q & 15) * 16 + rr;       // row in its 256-row tile
       const int c = sl ^ ((r >> 2) & 3);
       const int k = k0 + c * 8;
       const bool kin = k < ke;
-      if (h < 2) {
+      if (h < kInstB / 2) {
         const uint32_t oa = (kin && m0 + r < M) ? (uint32_t)r * (uint32_t)lda * 2u + (uint32_t)k * 2u
                                                 : kOob;
         lds_dma16(ra, oa, la + q * 1024);
@@ -399,27 +405,30 @@ gemm_big_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda
     }
   };
 
-  int brow[2];
-  if constexpr (EPI == EPI_SWIGLU) {
-    brow[0] = wn * 32;        // gate f = c0 + wn*32 + lane%32
-    brow[1] = 128 + wn * 32;  // up, same f
-  } else {
-    brow[0] = wn * 64;
-    brow[1] = wn * 64 + 32;
+  // W tile rows of this wave's fragments.  SwiGLU: the first NF/2 are gate
+  // rows of F = c0 + wn (128/WNW) + 32 j + lane%32, the last NF/2 the up
+  // rows of the same F.
+  int brow[NF];
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    if constexpr (EPI == EPI_SWIGLU)
+      brow[j] = (j < NF / 2 ? 0 : 128) + wn * (128 / WNW) + (j % (NF / 2)) * 32;
+    else
+      brow[j] = wn * (256 / WNW) + j * 32;
   }
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[4][NF];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NF; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   // Operands of one 16-wide K step (ks) of a stage, read one step ahead of
   // the MFMAs that use them.
-  bf16x8_t af[2][4], bw[2][2];
-  auto read_ops = [&](int buf, int ks, bf16x8_t (&a)[4], bf16x8_t (&w)[2]) {
+  bf16x8_t af[2][4], bw[2][NF];
+  auto read_ops = [&](int buf, int ks, bf16x8_t (&a)[4], bf16x8_t (&w)[NF]) {
     const unsigned char* sa = smem + buf * kStageB;
     const unsigned char* sb = sa + kStageBA;
     const int c = ks * 2 + (lane >> 5);
@@ -427,14 +436,14 @@ gemm_big_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda
     for (int i = 0; i < 4; ++i)
       a[i] = *reinterpret_cast<const bf16x8_t*>(sa + lds_off64(wm * 128 + i * 32 + (lane & 31), c));
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NF; ++j)
       w[j] = *reinterpret_cast<const bf16x8_t*>(sb + lds_off64(brow[j] + (lane & 31), c));
   };
-  auto mfmas = [&](const bf16x8_t (&a)[4], const bf16x8_t (&w)[2]) {
+  auto mfmas = [&](const bf16x8_t (&a)[4], const bf16x8_t (&w)[NF]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NF; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], w[j], acc[i][j], 0, 0, 0);
   };
 
@@ -454,21 +463,22 @@ gemm_big_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda
   __syncthreads();
   read_ops(0, 0, af[0], bw[0]);
   int buf = 0;  // kt % SB
-  // The two K steps of stage kt: the next step's 6 operand reads are issued
-  // ahead of the current step's 8 MFMAs (the scheduler is held to that order).
+  // The two K steps of stage kt: the next step's 4 + NF operand reads are
+  // issued ahead of the current step's 4 NF MFMAs (the scheduler is held to
+  // that order).
   auto first_half = [&]() {
     read_ops(buf, 1, af[1], bw[1]);
     mfmas(af[0], bw[0]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // DS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + NF, 0);  // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NF, 0);  // MFMA
     __builtin_amdgcn_sched_barrier(0);                  // nothing moves past here
   };
   auto second_half = [&]() {
     buf = buf == SB - 1 ? 0 : buf + 1;
     read_ops(buf, 0, af[0], bw[0]);
     mfmas(af[1], bw[1]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 + NF, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NF, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
   int kt = 0;
@@ -499,21 +509,24 @@ gemm_big_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda
 
   if (ns == 1) {
     if constexpr (EPI == EPI_SWIGLU) {
-      const int col = c0 + wn * 32 + (lane & 31);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < NF / 2; ++j) {
+        const int col = c0 + wn * (128 / WNW) + j * 32 + (lane & 31);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * 128 + i * 32 + acc_row32(r, lane);
-          if (m < M && col < N)
-            store_out<EPI_DT>(out, ldo, m, col, silu(acc[i][0][r]) * acc[i][1][r]);
-        }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = m0 + wm * 128 + i * 32 + acc_row32(r, lane);
+            if (m < M && col < N)
+              store_out<EPI_DT>(out, ldo, m, col, silu(acc[i][j][r]) * acc[i][j + NF / 2][r]);
+          }
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = c0 + wn * 64 + j * 32 + (lane & 31);
+        for (int j = 0; j < NF; ++j) {
+          const int col = c0 + wn * (256 / WNW) + j * 32 + (lane & 31);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int m = m0 + wm * 128 + i * 32 + acc_row32(r, lane);
@@ -533,7 +546,7 @@ gemm_big_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NF; ++j) {
       const int tc = brow[j] + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -567,7 +580,7 @@ gemm_big_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda
     return s4;
   };
   constexpr int kQ = kCols / 4;
-  for (int idx = tid; idx < BB * kQ; idx += kThreads) {
+  for (int idx = tid; idx < BB * kQ; idx += kThr) {
     const int tr = idx / kQ, tc = (idx % kQ) * 4;
     const int m = m0 + tr;
     if (m >= M) continue;
@@ -661,7 +674,8 @@ template <int EPI>
 hipError_t launch_plan(const Plan& pl, int M, int N, int K, const uint16_t* A, int64_t lda,
                        const uint16_t* W0, const uint16_t* W1, void* out, int64_t ldo,
                        void* workspace, hipStream_t stream) {
-  auto kern = pl.big ? gemm_big_kernel<EPI> : gemm_kernel<EPI>;
+  auto kern = pl.big ? gemm_big_kernel<EPI, 8> : gemm_kernel<EPI>;
+  const int threads = pl.big ? 8 * 64 : kThreads;
   unsigned* counters = nullptr;
   float* part = nullptr;
   if (pl.ns > 1) {
@@ -669,7 +683,7 @@ hipError_t launch_plan(const Plan& pl, int M, int N, int K, const uint16_t* A, i
     counters = static_cast<unsigned*>(workspace);
     part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsCounterBytes);
   }
-  hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(kThreads), 0, stream, M, N, K, A, lda, W0,
+  hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(threads), 0, stream, M, N, K, A, lda, W0,
                      W1, out, ldo, pl.kr, counters, part);
   return hipGetLastError();
 }
