@@ -206,44 +206,66 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   const int ncols = min(cols, N - cbase);
   const int cq = (ncols + 3) / 4;
   const int rs0 = rb * NW * 16;                             // block's first row-space column
-  // Sum of the ns split planes at element offset q (split 0), in split order.
-  // Eight loads are in flight per batch; offsets of splits past ns are out of
-  // range and read zero (x + 0 == x), so the batch needs no branch.
-  auto sum_splits = [&](int64_t q) {
-    f32x4_t s4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // Sums of the ns split planes at element offsets q[0 .. NQ) (NQ = 2 for
+  // SwiGLU: the gate and the up columns), each in split order.  Eight
+  // splits of every offset are in flight per batch -- gate and up together,
+  // one memory round trip; offsets of splits past ns are out of range and
+  // read zero (x + 0 == x), so the batch needs no branch.
+  auto sum_splits = [&](const auto& q, auto& s) {
+    constexpr int NQ = sizeof(s) / sizeof(s[0]);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) s[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int r = 0; r < ns; r += 8) {
-      f32x4_t v[8];
+      f32x4_t v[NQ][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        v[e] = __builtin_bit_cast(
-            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                         pr, r + e < ns ? (uint32_t)((q + (r + e) * plane) * 4) : kOob, 0,
-                         kAuxSys));
+      for (int i = 0; i < NQ; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s4 += v[e];
+        for (int e = 0; e < 8; ++e)
+          v[i][e] = __builtin_bit_cast(
+              f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                           pr, r + e < ns ? (uint32_t)((q[i] + (r + e) * plane) * 4) : kOob, 0,
+                           kAuxSys));
+#pragma unroll
+      for (int i = 0; i < NQ; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[i] += v[i][e];
     }
-    return s4;
   };
   for (int idx = tid; idx < I * cq; idx += NW * 64) {
     const int m = idx / cq, c = (idx % cq) * 4;
     const int64_t q = (int64_t)m * NR + rs0 + c;
-    f32x4_t s4 = sum_splits(q);
     const int n = min(4, ncols - c);
     f32x4_t v;
+    // FP8 row scales, loaded before the partials so both are in flight together
+    float sc0[4] = {1.f, 1.f, 1.f, 1.f}, sc1[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (F8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc0[e] = e < n ? S0[cbase + c + e] : 0.0f;
+        if constexpr (EPI == EPI_SWIGLU) sc1[e] = e < n ? S1[cbase + c + e] : 0.0f;
+      }
+    }
     if constexpr (EPI == EPI_SWIGLU) {
-      f32x4_t u = sum_splits(q + cols);
+      const int64_t qq[2] = {q, q + cols};
+      f32x4_t gu[2];
+      sum_splits(qq, gu);
+      f32x4_t s4 = gu[0], u = gu[1];
       if constexpr (F8) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s4[e] *= e < n ? S0[cbase + c + e] : 0.0f;
-          u[e] *= e < n ? S1[cbase + c + e] : 0.0f;
+          s4[e] *= sc0[e];
+          u[e] *= sc1[e];
         }
       }
       v = f32x4_t{silu(s4.x) * u.x, silu(s4.y) * u.y, silu(s4.z) * u.z, silu(s4.w) * u.w};
     } else {
+      const int64_t qq[1] = {q};
+      f32x4_t sv[1];
+      sum_splits(qq, sv);
+      f32x4_t s4 = sv[0];
       if constexpr (F8) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s4[e] *= e < n ? S0[cbase + c + e] : 0.0f;
+        for (int e = 0; e < 4; ++e) s4[e] *= sc0[e];
       }
       v = s4;
     }

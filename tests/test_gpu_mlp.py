@@ -121,7 +121,7 @@ def sample_rows(I):
     return sorted({0, I // 2, I - 1})
 
 
-@pytest.mark.parametrize("I", [1, 16, 64, 256])
+@pytest.mark.parametrize("I", [1, 16, 32, 64, 256])
 def test_llama_mlp_decode_tp8(orc, llama_mlp, I):
     """Llama-3.1-70B-shaped MLP, all 8 TP=8 rank shares on one GPU, decode I tokens;
     sampled token rows against the oracle (every row depends only on its own
@@ -190,7 +190,7 @@ def test_mlp_deterministic(llama_mlp):
     """Same inputs, same bits: no atomics, fixed summation orders."""
     L = llama_mlp
     T = torch()
-    for I in (1, 64, 512):
+    for I in (1, 32, 64, 512):
         X = to_dev(datagen.gaussian("X", (I, L["D"]), 1.0, "bf16", 9), "bf16")
         outs = []
         for _ in range(2):
