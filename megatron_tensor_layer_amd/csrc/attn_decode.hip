@@ -34,7 +34,9 @@ constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any record: reads 
 constexpr int kAuxSys = 17;             // sc0 sc1: system coherent
 constexpr int NWV = 4;
 constexpr int kMaxChunks = 32;  // position chunks per (sequence, group)
-constexpr int kTargetWgs = 512; // two per CU
+// one per CU: measured faster than two per CU (fewer chunk states to write
+// and merge) -- B = 32, L = 2048: 21.2 us against 22.9; L = 8192: 37.8 against 41.6
+constexpr int kTargetWgs = 256;
 
 __device__ __forceinline__ int acc_row32(int r, int lane) {
   return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
@@ -305,7 +307,7 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
   const int64_t nrec = (int64_t)gridDim.x;
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(part, (uint32_t)(nrec * rec * 4));
   const int64_t my = (int64_t)blockIdx.x * rec;
-  if (w == 0) {
+  if (w == 0 && h < G) {  // lanes of padding heads (h >= G) store nothing
     // lane holds head h, rows t*32 + 8 j + 4 (lane/32) + {0..3}: 16 bytes each
 #pragma unroll
     for (int t = 0; t < HDT; ++t)
@@ -328,12 +330,23 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
   __syncthreads();
   if (!is_last) return;
 
-  // ---- the last chunk to arrive merges the NC states.  All loads of a phase
-  //      are issued before any is used (one round trip each): the (max, sum)
-  //      pairs of every chunk and head to LDS, then per head the weights
-  //      e^(m_c - M) and 1/sum, then each thread sums 4 columns of one head
-  //      over the chunks in chunk order, 16 chunks' loads in flight.
+  // ---- the last chunk to arrive merges the NC states.  One memory round
+  //      trip: each thread first issues the loads of its (head, 4 columns)
+  //      item over the first 16 chunks, then the (max, sum) pairs of every
+  //      chunk and real head go to LDS; per head the weights e^(m_c - M) and
+  //      1/sum follow, and each thread sums its columns over the chunks in
+  //      chunk order (chunks past 16, if any, in further batches).
   const int64_t first = (int64_t)bg * NC * rec;
+  const int c4n = hd / 4;  // 4-column groups per head
+  const int q0 = threadIdx.x;
+  const bool item = q0 < G * c4n;
+  const int hh0 = item ? q0 / c4n : 0, col0 = item ? 4 * (q0 % c4n) : 0;
+  u32x4_t o[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    o[e] = __builtin_amdgcn_raw_buffer_load_b128(
+        pr, item && e < NC ? (uint32_t)((first + e * rec + hh0 * HDP + col0) * 4) : kOob, 0,
+        kAuxSys);
   float* mlp = &ots[0][0][0][0];  // [kMaxChunks][32] (max, sum) pairs
   static_assert((NWV - 1) * HDT * 16 * 64 >= 2 * kMaxChunks * 32, "merge scratch fits");
 #pragma unroll
@@ -341,13 +354,14 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
     const int i = threadIdx.x + 64 * NWV * j;  // chunk i / 32, head i % 32
     const int k = i >> 5, hh = i & 31;
     const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(
-        pr, k < NC ? (uint32_t)((first + k * rec + 32 * HDP + 2 * hh) * 4) : kOob, 0, kAuxSys);
+        pr, k < NC && hh < G ? (uint32_t)((first + k * rec + 32 * HDP + 2 * hh) * 4) : kOob, 0,
+        kAuxSys);
     const uint32_t mb = v.x, lb = v.y;  // scalars: bit_cast of a vector element misreads
     mlp[2 * i] = __builtin_bit_cast(float, mb);
     mlp[2 * i + 1] = __builtin_bit_cast(float, lb);
   }
   __syncthreads();
-  if (threadIdx.x < 32) {
+  if (threadIdx.x < G) {
     const int hh = threadIdx.x;
     float mm = -INFINITY;
     for (int k = 0; k < NC; ++k) mm = fmaxf(mm, mlp[2 * (k * 32 + hh)]);
@@ -361,20 +375,32 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
     fw[kMaxChunks * 32 + hh] = 1.0f / den;
   }
   __syncthreads();
-  const int c4n = hd / 4;  // 4-column groups per head
-  for (int q = threadIdx.x; q < G * c4n; q += 64 * NWV) {
+  for (int q = q0; q < G * c4n; q += 64 * NWV) {
     const int hh = q / c4n, col = 4 * (q % c4n);
     f32x4_t num = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < NC; k += 16) {
-      u32x4_t o[16];
+    if (q == q0) {  // the preloaded first 16 chunks
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (e < NC) num += __builtin_bit_cast(f32x4_t, o[e]) * fw[e * 32 + hh];
+    } else {
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         o[e] = __builtin_amdgcn_raw_buffer_load_b128(
+            pr, e < NC ? (uint32_t)((first + e * rec + hh * HDP + col) * 4) : kOob, 0, kAuxSys);
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (e < NC) num += __builtin_bit_cast(f32x4_t, o[e]) * fw[e * 32 + hh];
+    }
+    for (int k = 16; k < NC; k += 16) {
+      u32x4_t o2[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        o2[e] = __builtin_amdgcn_raw_buffer_load_b128(
             pr, k + e < NC ? (uint32_t)((first + (k + e) * rec + hh * HDP + col) * 4) : kOob, 0,
             kAuxSys);
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        if (k + e < NC) num += __builtin_bit_cast(f32x4_t, o[e]) * fw[(k + e) * 32 + hh];
+        if (k + e < NC) num += __builtin_bit_cast(f32x4_t, o2[e]) * fw[(k + e) * 32 + hh];
     }
     num *= fw[kMaxChunks * 32 + hh];
     u32x2_t packed;
