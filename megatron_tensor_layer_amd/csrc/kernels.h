@@ -75,6 +75,12 @@ bool rowstream_suits(int I, int K, int N, bool swiglu);
 template <int EPI>
 hipError_t rowstream_launch(int I, int K, int N, const uint16_t* X, const uint16_t* W0,
                             const uint16_t* W1, void* out, int64_t ldo, hipStream_t stream);
+// The weight-only FP8 form (weights as in gemv_fp8_launch; EPI_F32 or
+// EPI_SWIGLU; K a multiple of 16).
+template <int EPI>
+hipError_t rowstream_fp8_launch(int I, int K, int N, const uint16_t* X, const uint8_t* W0,
+                                const float* S0, const uint8_t* W1, const float* S1, void* out,
+                                int64_t ldo, hipStream_t stream);
 
 // Same product on bf16 MFMA for any M (128 x 128 tiles).  When the tiles
 // cannot fill the chip, K is split over workgroups and `workspace`

@@ -20,7 +20,12 @@
 //     XOR-swizzled by token); every CU reads all of X, which at these token
 //     counts is no more than its share of the weights;
 //   * the four K slices of a tile are summed through LDS in slice order
-//     (deterministic) and stored with the epilogue (fp32, bf16, silu(g) * u).
+//     (deterministic) and stored with the epilogue (fp32, bf16, silu(g) * u);
+//   * weight-only FP8 (OCP E4M3 codes, one fp32 scale per row): a group of
+//     128 K is 128 bytes per row, two load instructions of 8 rows x 128
+//     bytes, four groups in flight (the bf16 path's bytes); each 16-byte
+//     chunk of codes is decoded exactly into two bf16 chunks on its way into
+//     the transpose tile, and the summed rows are scaled in the epilogue.
 #include <type_traits>
 
 #include "common.h"
@@ -53,12 +58,15 @@ static_assert(lds_bytes<2>() <= 160 * 1024, "two chunks of 32 tokens and the til
 template <int MT>
 constexpr int xpw() { return kKW * 8 * MT / kWaves; }
 
-template <int MT, int EPI, int P>
+template <int MT, int EPI, int P, bool F8>
 __global__ void __launch_bounds__(kThreads)
 rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
-                 const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int KS,
+                 const void* __restrict__ W0, const void* __restrict__ W1,
+                 const float* __restrict__ S0, const float* __restrict__ S1, int KS,
                  int RPT, void* __restrict__ out, int64_t ldo) {
   constexpr int XPW = xpw<MT>();
+  constexpr int ES = F8 ? 1 : 2;   // bytes per weight
+  constexpr int LPG = F8 ? 2 : 4;  // load instructions per 128-K group
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -68,7 +76,7 @@ rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   // ---- this wave's RPT (<= 16) weight rows, padded to a 16-row MFMA tile;
   //      rows past RPT or past the matrix read zero and fetch nothing
   int wrow0;
-  const uint16_t* wmat;
+  const void* wmat;
   if constexpr (EPI == EPI_SWIGLU) {
     wrow0 = blockIdx.x * RPT;  // the same F rows of gate (tile 0) and up (tile 1)
     wmat = tw == 0 ? W0 : W1;
@@ -78,19 +86,25 @@ rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   }
   const int rows = max(0, min(RPT, N - wrow0));
   const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(wmat + (int64_t)wrow0 * K, (uint32_t)rows * (uint32_t)K * 2u);
+      make_rsrc(static_cast<const unsigned char*>(wmat) + (rows ? (int64_t)wrow0 * K * ES : 0),
+                (uint32_t)rows * (uint32_t)K * (uint32_t)ES);
   const int kb = sl * KS, ke = min(K, kb + KS);  // this wave's K slice
   const int NC = KS / kKC;                       // chunks per slice (same for all)
   const int NG = 2 * NC;
 
-  // group g of the slice, instruction p: rows 4p + lane/16, chunk lane%16
-  auto issue_w = [&](int g, u32x4_t (&v)[4]) {
-    const int k = kb + g * kGK + (lane & 15) * 8;
+  // group g of the slice, instruction p: bf16 rows 4p + lane/16, 16-byte
+  // chunk lane%16 (8 K); FP8 rows 8p + lane/8, chunk lane%8 (16 K)
+  auto issue_w = [&](int g, u32x4_t (&v)[LPG]) {
+    constexpr int KPC = 16 / ES;    // K per 16-byte chunk
+    constexpr int CPR = kGK / KPC;  // chunks per row of a group: 16 (bf16), 8 (FP8)
+    constexpr int RPI = 64 / CPR;   // rows per load instruction: 4, 8
+    static_assert(RPI * LPG == 16, "a group is 16 rows");
+    const int k = kb + g * kGK + (lane % CPR) * KPC;
     const bool ok = g < NG && k < ke;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t r = 4 * p + (lane >> 4);
-      v[p] = buf_load16<kAuxNT>(wr, ok ? (r * (uint32_t)K + (uint32_t)k) * 2u : kOob);
+    for (int p = 0; p < LPG; ++p) {
+      const uint32_t r = RPI * p + lane / CPR;
+      v[p] = buf_load16<kAuxNT>(wr, ok ? (r * (uint32_t)K + (uint32_t)k) * (uint32_t)ES : kOob);
     }
   };
 
@@ -117,17 +131,17 @@ rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   f32x4_t acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  u32x4_t wv[P][4];
+  u32x4_t wv[P][LPG];
 
   // P weight groups are in flight per wave (P = 2: one chunk ahead, 4: two).
   // Order of this wave's loads: W(0 .. P-3), X(0), W(P-2), W(P-1), then per
   // chunk step c: X(c + 1) and, as groups 2c and 2c + 1 are consumed,
   // W(2c + P) and W(2c + P + 1).  So X(c) is always followed by exactly two
   // weight groups and W(g) by 4 (P - 1) + 2 XPW (P = 4) or 4 + XPW (P = 2)
-  // loads.  Past the end the offsets are out of range (zero, nothing
-  // fetched), so the counts never change.
+  // loads (LPG per group: 4 bf16, 2 FP8).  Past the end the offsets are
+  // out of range (zero, nothing fetched), so the counts never change.
   static_assert(P == 2 || P == 4, "two or four groups in flight");
-  constexpr int kAfterW = P == 4 ? 12 + 2 * XPW : 4 + XPW;
+  constexpr int kAfterW = P == 4 ? 3 * LPG + 2 * XPW : LPG + XPW;
 #pragma unroll
   for (int g = 0; g < P - 2; ++g) issue_w(g, wv[g]);
   issue_x(0);
@@ -136,19 +150,32 @@ rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   // one chunk step; `par` = c % 2 is a constant in each unrolled copy, so the
   // weight register set of each group is known at compile time
   auto step = [&](int c, auto par) {
-    wait_vmcnt<8>();  // X(c) has landed: only the two groups after it may not
+    wait_vmcnt<2 * LPG>();  // X(c) has landed: only the two groups after it may not
     __syncthreads();  // everyone's part of X(c); chunk c - 1's buffer is free
     issue_x(c + 1);
     const unsigned char* xs = lds + (c & 1) * xbuf_bytes<MT>() + sl * xslice_bytes<MT>();
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int g = 2 * c + b;
-      u32x4_t (&w)[4] = wv[(2 * decltype(par)::value + b) % P];
+      u32x4_t (&w)[LPG] = wv[(2 * decltype(par)::value + b) % P];
       wait_vmcnt<kAfterW>();  // W(g) has landed
+      // transpose through the tile: row r, bf16 chunk c at slot c ^ r; an
+      // FP8 chunk of 16 codes decodes exactly into two bf16 chunks
+      if constexpr (F8) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int r = 4 * p + (lane >> 4);
-        *reinterpret_cast<u32x4_t*>(tile + r * 256 + (((lane & 15) ^ r) * 16)) = w[p];
+        for (int p = 0; p < LPG; ++p) {
+          const int r = 8 * p + (lane >> 3), c = 2 * (lane & 7);
+          u32x4_t lo, hi;
+          decode16(w[p], lo, hi);
+          *reinterpret_cast<u32x4_t*>(tile + r * 256 + ((c ^ r) * 16)) = lo;
+          *reinterpret_cast<u32x4_t*>(tile + r * 256 + (((c + 1) ^ r) * 16)) = hi;
+        }
+      } else {
+#pragma unroll
+        for (int p = 0; p < LPG; ++p) {
+          const int r = 4 * p + (lane >> 4);
+          *reinterpret_cast<u32x4_t*>(tile + r * 256 + (((lane & 15) ^ r) * 16)) = w[p];
+        }
       }
       issue_w(g + P, w);
 #pragma unroll
@@ -195,6 +222,9 @@ rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   if constexpr (EPI == EPI_SWIGLU) {
     if (wave != 0) return;
     const int col = blockIdx.x * RPT + n;
+    // FP8: the row scales of gate and up multiply the summed rows
+    const float sg = F8 ? (col < N ? S0[col] : 0.0f) : 1.0f;
+    const float su = F8 ? (col < N ? S1[col] : 0.0f) : 1.0f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -202,16 +232,17 @@ rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
         const int m = mt * 16 + (lane >> 4) * 4 + e;
         if (m < I && col < N)
           static_cast<uint16_t*>(out)[(int64_t)m * ldo + col] =
-              f32_to_bf16_bits(silu(sum[0][mt][e]) * sum[1][mt][e]);
+              f32_to_bf16_bits(silu(sum[0][mt][e] * sg) * (sum[1][mt][e] * su));
       }
   } else {
     const int col = (blockIdx.x * 2 + wave) * RPT + n;
+    const float sc = F8 ? (col < N ? S0[col] : 0.0f) : 1.0f;  // FP8 row scale
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = mt * 16 + (lane >> 4) * 4 + e;
-        const float v = wave == 0 ? sum[0][mt][e] : sum[1][mt][e];
+        const float v = (wave == 0 ? sum[0][mt][e] : sum[1][mt][e]) * sc;
         if (m < I && col < N) {
           if constexpr (EPI == EPI_F32)
             static_cast<float*>(out)[(int64_t)m * ldo + col] = v;
@@ -222,10 +253,13 @@ rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   }
 }
 
-template <int MT, int EPI>
-hipError_t launch_mt(int I, int K, int N, const uint16_t* X, const uint16_t* W0,
-                     const uint16_t* W1, void* out, int64_t ldo, hipStream_t stream) {
-  auto kern = rowstream_kernel<MT, EPI, 2>;  // 4 groups in flight measured slower
+template <int MT, int EPI, bool F8>
+hipError_t launch_mt(int I, int K, int N, const uint16_t* X, const void* W0, const void* W1,
+                     const float* S0, const float* S1, void* out, int64_t ldo,
+                     hipStream_t stream) {
+  // bf16: 2 groups of 128 K in flight per wave (4 measured slower); FP8: 4,
+  // the same bytes in flight
+  auto kern = rowstream_kernel<MT, EPI, F8 ? 4 : 2, F8>;
   static bool attr_set = false;  // raising the dynamic-LDS limit once per process is enough
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -237,7 +271,7 @@ hipError_t launch_mt(int I, int K, int N, const uint16_t* X, const uint16_t* W0,
   const int rpt = rowstream_rows(N, EPI == EPI_SWIGLU);
   const int grid = rowstream_grid(N, EPI == EPI_SWIGLU);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds_bytes<MT>(), stream, I, K, N, X, W0,
-                     W1, KS, rpt, out, ldo);
+                     W1, S0, S1, KS, rpt, out, ldo);
   return hipGetLastError();
 }
 
@@ -280,9 +314,27 @@ hipError_t rowstream_launch(int I, int K, int N, const uint16_t* X, const uint16
                             const uint16_t* W1, void* out, int64_t ldo, hipStream_t stream) {
   if (I < 1 || I > kRowStreamMaxTokens || K < 1 || K > kRowStreamMaxK || N < 1)
     return hipErrorInvalidValue;
-  if (I <= 16) return launch_mt<1, EPI>(I, K, N, X, W0, W1, out, ldo, stream);
-  return launch_mt<2, EPI>(I, K, N, X, W0, W1, out, ldo, stream);
+  if (I <= 16) return launch_mt<1, EPI, false>(I, K, N, X, W0, W1, nullptr, nullptr, out, ldo, stream);
+  return launch_mt<2, EPI, false>(I, K, N, X, W0, W1, nullptr, nullptr, out, ldo, stream);
 }
+
+template <int EPI>
+hipError_t rowstream_fp8_launch(int I, int K, int N, const uint16_t* X, const uint8_t* W0,
+                                const float* S0, const uint8_t* W1, const float* S1, void* out,
+                                int64_t ldo, hipStream_t stream) {
+  if (I < 1 || I > kRowStreamMaxTokens || K < 1 || K > kRowStreamMaxK || N < 1 || (K % 16))
+    return hipErrorInvalidValue;
+  if (I <= 16) return launch_mt<1, EPI, true>(I, K, N, X, W0, W1, S0, S1, out, ldo, stream);
+  return launch_mt<2, EPI, true>(I, K, N, X, W0, W1, S0, S1, out, ldo, stream);
+}
+
+template hipError_t rowstream_fp8_launch<EPI_F32>(int, int, int, const uint16_t*, const uint8_t*,
+                                                  const float*, const uint8_t*, const float*,
+                                                  void*, int64_t, hipStream_t);
+template hipError_t rowstream_fp8_launch<EPI_SWIGLU>(int, int, int, const uint16_t*,
+                                                     const uint8_t*, const float*,
+                                                     const uint8_t*, const float*, void*,
+                                                     int64_t, hipStream_t);
 
 template hipError_t rowstream_launch<EPI_F32>(int, int, int, const uint16_t*, const uint16_t*,
                                               const uint16_t*, void*, int64_t, hipStream_t);

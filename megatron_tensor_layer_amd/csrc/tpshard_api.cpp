@@ -249,14 +249,23 @@ Fp8Path fp8_path(int64_t I, int64_t D, int64_t F_local) {
     return Fp8Path::SplitK;
   return gemv_ok ? Fp8Path::Gemv : Fp8Path::None;
 }
+
+// On the MFMA path, the FP8 down projection streams whole K per workgroup
+// when the row-streaming kernel suits its shape (as the bf16 down does).
+bool fp8_down_rowstream(int64_t I, int64_t D, int64_t F_local) {
+  return I <= tpk::kRowStreamMaxTokens && F_local <= tpk::kRowStreamMaxK && D <= INT32_MAX &&
+         tpk::rowstream_suits((int)I, (int)F_local, (int)D, false);
+}
 }  // namespace
 
 size_t tp_shard_mlp_fp8_workspace_size(int64_t I, int64_t D, int64_t F_local) {
   if (I < 1 || I > kMaxDim || !dims_ok(D) || !dims_ok(F_local) || (D % 16) || (F_local % 16))
     return 0;
   if (fp8_path(I, D, F_local) != Fp8Path::SplitK) return 0;
-  return std::max(tpk::splitk_workspace_bytes((int)I, (int)D, (int)F_local, true),
-                  tpk::splitk_workspace_bytes((int)I, (int)F_local, (int)D, false));
+  const size_t down = fp8_down_rowstream(I, D, F_local)
+                          ? 0
+                          : tpk::splitk_workspace_bytes((int)I, (int)F_local, (int)D, false);
+  return std::max(tpk::splitk_workspace_bytes((int)I, (int)D, (int)F_local, true), down);
 }
 
 tp_status_t tp_shard_mlp_fp8(int64_t I, int64_t D, int64_t F_local, const void* X,
@@ -308,6 +317,9 @@ tp_status_t tp_shard_mlp_fp8(int64_t I, int64_t D, int64_t F_local, const void* 
   e = tpk::splitk_fp8_launch<tpk::EPI_SWIGLU>((int)I, (int)D, (int)F_local, Xb, g8, s_gate, u8,
                                               s_up, H, F_local, workspace, s);
   if (e != hipSuccess) return TP_ERR_LAUNCH;
+  if (fp8_down_rowstream(I, D, F_local))
+    return launched(tpk::rowstream_fp8_launch<tpk::EPI_F32>((int)I, (int)F_local, (int)D, Hb, d8,
+                                                            s_down, nullptr, nullptr, P, D, s));
   return launched(tpk::splitk_fp8_launch<tpk::EPI_F32>((int)I, (int)F_local, (int)D, Hb, d8,
                                                        s_down, nullptr, nullptr, P, D, workspace,
                                                        s));

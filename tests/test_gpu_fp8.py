@@ -94,7 +94,10 @@ def test_qwen_tp2_partials_sum_to_layer(orc, I):
 
 @pytest.mark.parametrize("I,D,Fl", [(3, 16, 16), (5, 48, 80), (8, 1040, 272), (1, 16384, 16),
                                     (9, 48, 80), (17, 1040, 272), (40, 272, 1040),
-                                    (64, 1536, 4480), (2, 32768, 64)])
+                                    (64, 1536, 4480), (2, 32768, 64),
+                                    # down on the whole-K row-streaming kernel: a ragged
+                                    # last row tile (9 rows per tile), a full grid
+                                    (20, 4112, 1040), (9, 4096, 2064)])
 def test_small_and_ragged_shapes(orc, I, D, Fl):
     """K of one 16-byte chunk, chunks not filling a wave, two chunks per lane;
     split K with ragged K ranges and row tiles; K past the few-token limit."""
