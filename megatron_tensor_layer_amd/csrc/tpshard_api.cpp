@@ -250,11 +250,13 @@ Fp8Path fp8_path(int64_t I, int64_t D, int64_t F_local) {
   return gemv_ok ? Fp8Path::Gemv : Fp8Path::None;
 }
 
-// On the MFMA path, the FP8 down projection streams whole K per workgroup
-// when the row-streaming kernel suits its shape (as the bf16 down does).
+// On the MFMA path (from 5 tokens), the FP8 down projection streams whole K
+// per workgroup when the row-streaming kernel suits its shape, as the bf16
+// down does from 9 tokens: at 5..8 tokens it beats split K too (Llama TP=8
+// MLP: 31.0 us against 33.1-33.5).
 bool fp8_down_rowstream(int64_t I, int64_t D, int64_t F_local) {
   return I <= tpk::kRowStreamMaxTokens && F_local <= tpk::kRowStreamMaxK && D <= INT32_MAX &&
-         tpk::rowstream_suits((int)I, (int)F_local, (int)D, false);
+         tpk::rowstream_suits((int)std::max<int64_t>(I, 9), (int)F_local, (int)D, false);
 }
 }  // namespace
 

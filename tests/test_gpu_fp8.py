@@ -97,7 +97,7 @@ def test_qwen_tp2_partials_sum_to_layer(orc, I):
                                     (64, 1536, 4480), (2, 32768, 64),
                                     # down on the whole-K row-streaming kernel: a ragged
                                     # last row tile (9 rows per tile), a full grid
-                                    (20, 4112, 1040), (9, 4096, 2064)])
+                                    (20, 4112, 1040), (9, 4096, 2064), (6, 4112, 1040)])
 def test_small_and_ragged_shapes(orc, I, D, Fl):
     """K of one 16-byte chunk, chunks not filling a wave, two chunks per lane;
     split K with ragged K ranges and row tiles; K past the few-token limit."""
