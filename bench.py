@@ -289,7 +289,7 @@ def detail(torch, tp, layer, calls):
     out = {}
     T = torch
     # Llama-3.1-70B MLP rank share, TP=8: rotate through the 8 real rank shards
-    for I in (1, 16, 32, 64, 256):
+    for I in (1, 8, 16, 32, 64, 256):
         X = to_dev(T, datagen.gaussian("X", (I, D), 1.0, "bf16", 1000 + I))
         H = T.empty((I, F // TP), dtype=T.bfloat16, device="cuda")
         P = T.empty((I, D), dtype=T.float32, device="cuda")

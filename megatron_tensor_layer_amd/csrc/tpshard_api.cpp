@@ -3,7 +3,9 @@
 // Host side only: validates arguments without touching the GPU, picks a
 // kernel family by the token count and enqueues it on the caller's stream.
 //   bf16, I <= 8   few-token streaming kernel (VALU dot2), weights read once
-//   bf16, I <= 64  split-K weight streaming on MFMA, workspace for partials
+//                  (from 5 tokens only for small weight matrices)
+//   bf16, I <= 64  split-K or whole-K weight streaming on MFMA (workspace
+//                  for split-K partials)
 //   bf16, I > 64   MFMA tiled kernel (4-stage LDS pipeline, K split when
 //                  the tiles cannot fill the chip)
 //   fp32           few-token streaming kernel, 8 tokens per launch
@@ -43,14 +45,24 @@ Path bf16_path(int64_t I, int64_t K, int64_t N, bool swiglu) {
   // few tokens: weight streaming on VALU; past K = kGemvMaxK16 / 2 the
   // 8-token variant runs out of registers, so 5..8 tokens go to MFMA there
   const int64_t kmax = (I <= 4) ? tpk::kGemvMaxK16 : tpk::kGemvMaxK16 / 2;
-  if (I <= tpk::kGemvMaxTokens && K <= kmax) return Path::Gemv;
+  const bool gemv_ok = I <= tpk::kGemvMaxTokens && K <= kmax;
+  if (gemv_ok && I <= 4) return Path::Gemv;
+  // At 5..8 tokens the VALU kernel's cross-lane sums of 8 token rows limit
+  // it on large matrices, where the MFMA kernels win: measured kernel time
+  // per call on the Llama TP=8 MLP, 33.1 + 17.0 us against 23.9 + 11.6.  On
+  // small ones their fixed costs lose (Qwen2.5-1.5B TP=2 QKV 6.1 us against
+  // 4.4).  Crossovers: about 16 MB of weights for the whole-K kernel
+  // (o_proj, 16.8 MB: 6.0 against 7.2), 32 MB for split K (QKV, 21 MB:
+  // 10.3 against 9.3).
+  const double wbytes = 2.0 * (double)K * (double)N * (swiglu ? 2.0 : 1.0);
   if (I <= tpk::kRowStreamMaxTokens && K <= tpk::kRowStreamMaxK && N <= INT32_MAX &&
-      tpk::rowstream_suits((int)I, (int)K, (int)N, swiglu))
+      (!gemv_ok || wbytes >= 16e6) &&
+      tpk::rowstream_suits((int)std::max<int64_t>(I, 9), (int)K, (int)N, swiglu))
     return Path::RowStream;
-  if (I <= tpk::kSplitKMaxTokens && K <= tpk::kSplitKMaxK &&
+  if (I <= tpk::kSplitKMaxTokens && K <= tpk::kSplitKMaxK && (!gemv_ok || wbytes >= 32e6) &&
       tpk::splitk_suits((int)I, (int)K, (int)N, swiglu))
     return Path::SplitK;
-  return Path::Gemm;
+  return gemv_ok ? Path::Gemv : Path::Gemm;
 }
 
 // Workspace of one projection (split-K partial sums; 0 when not split).

@@ -121,7 +121,7 @@ def sample_rows(I):
     return sorted({0, I // 2, I - 1})
 
 
-@pytest.mark.parametrize("I", [1, 16, 32, 64, 256])
+@pytest.mark.parametrize("I", [1, 6, 16, 32, 64, 256])
 def test_llama_mlp_decode_tp8(orc, llama_mlp, I):
     """Llama-3.1-70B-shaped MLP, all 8 TP=8 rank shares on one GPU, decode I tokens;
     sampled token rows against the oracle (every row depends only on its own
