@@ -21,6 +21,9 @@ The printed JSON line also carries
                 HIP events on its stream inside the timed region (one rank's
                 call per step, rotating over the ranks), against the 8 TB/s
                 HBM peak;
+  read_ceiling: the achievable read rate, tp_stream_read over 2 GiB with the
+                decode kernels' access pattern; roofline and config also give
+                their fraction of it;
   cpu_baseline: the fp64 oracle on the host cores running one whole step
                 (about 55 GFLOP in fp64, a second or so on 16 cores);
   detail:       per-config figures (MLP shard decode I=1/16/64/256 GB/s,
@@ -499,9 +502,43 @@ def cpu_baseline(layer, X, I, S, bytes_per_step):
     orc.reduce(pm)
     step_s = time.perf_counter() - t0
     return dict(value=round(bytes_per_step / step_s / 1e9, 3), unit="GB/s",
-                cores=oracle.num_threads(), kind="oracle",
+                cores=oracle.num_threads(), cpu=cpu_model(), kind="oracle",
                 sample=f"one whole step: 8 ranks x (QKV, attention core, o_proj, MLP) for all "
                        f"{I} tokens plus both reduces, {step_s:.1f} s")
+
+
+def read_ceiling(torch, tp, calls=20):
+    """The achievable read rate: tp_stream_read over 2 GiB (8x the Infinity
+    Cache), the decode kernels' access pattern, median of `calls` reads."""
+    nbytes = 1 << 31
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = tp.stream_read(buf)
+    for _ in range(3):
+        tp.stream_read(buf, sink)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for a, b in ev:
+        a.record()
+        tp.stream_read(buf, sink)
+        b.record()
+    torch.cuda.synchronize()
+    us = statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return dict(GBps=round(nbytes / (us * 1e-6) / 1e9, 1), bytes=nbytes, calls=calls,
+                median_us=round(us, 2), frac_of_peak=round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM, 4),
+                kernel="tp_stream_read: one 16-wave workgroup per CU, 1 KB per wave load, "
+                       "3 loads in flight per wave")
+
+
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ------------------------------------------------------------------ main
@@ -558,6 +595,9 @@ def main():
                 kernel=f"tp_shard_mlp I={I} D={D} F_local={F // TP} "
                        "(gate/up+SwiGLU kernel, then down kernel)",
                 avg_call_us=round(mlp_us, 2), algorithmic_bytes_per_call=mlp_bytes)
+    ceiling = read_ceiling(torch, tp)
+    log(f"read ceiling: {ceiling['GBps']} GB/s over 2 GiB")
+    roof["frac_of_read_ceiling"] = round(achieved / ceiling["GBps"], 4)
     tf = ROOT / "profiles" / "traffic.json"
     if tf.exists():
         tr = json.loads(tf.read_text())
@@ -576,8 +616,9 @@ def main():
                     D=D, F=F, n_q=NQ, n_kv=NKV, head_dim=HD, tp=TP, tokens=I,
                     bytes_per_step=nbytes, flops_per_step=step_flops(I),
                     tokens_per_s_excl_comm=round(I / (ms * 1e-3), 1),
-                    frac_hbm=round(value / PEAK_HBM, 4)),
-        roofline=roof)
+                    frac_hbm=round(value / PEAK_HBM, 4),
+                    frac_read_ceiling=round(value / ceiling["GBps"], 4)),
+        roofline=roof, read_ceiling=ceiling)
 
     if not args.no_detail:
         line["detail"] = detail(torch, tp, layer, args.calls)

@@ -272,6 +272,25 @@ tp_status_t tp_attn_decode(int64_t B, int64_t n_q_local, int64_t n_kv_local, int
 tp_status_t tp_attn_core(int64_t I, int64_t S, int64_t n_q_local, int64_t n_kv_local,
                          int64_t head_dim, const void* qkv, void* A, void* stream);
 
+/*
+ * Measurement aid (not a step of the layer): the achievable read rate.
+ * Decode is bound by reading the rank's weights once ([L4] §1.1, §3.4);
+ * this reads `bytes` of device memory once with the same access pattern as
+ * the decode kernels' weight streams (1 KB contiguous per wave load, three
+ * loads in flight per wave, one 16-wave workgroup per CU), so bytes / time
+ * is the ceiling those kernels are compared with.
+ *   buf   device buffer of `bytes` bytes (a multiple of 1024, at most 2 GiB)
+ *   sink  tp_stream_read_sink_words() uint32 words out: word i is the XOR,
+ *         over the 16-byte chunks thread i read, of each chunk's first and
+ *         last 32-bit words (so the XOR of all of sink is that of the buffer)
+ * Errors: TP_ERR_INVALID (null pointer, bytes 0 or over 2 GiB, sink too
+ * small, no device), TP_ERR_MISALIGNED (bytes not a multiple of 1024, or a
+ * pointer not 16-byte aligned), TP_ERR_LAUNCH.
+ */
+size_t tp_stream_read_sink_words(void);
+tp_status_t tp_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

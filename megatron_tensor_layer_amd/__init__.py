@@ -48,6 +48,8 @@ SIGNATURES = {
     "tp_shard_mlp_fp8": (ctypes.c_int, [_i64, _i64, _i64] + [_vp] * 10 + [_sz, _vp]),
     "tp_residual_rmsnorm": (ctypes.c_int, [_i32, _i64, _i64, _vp, _vp, ctypes.c_int, _vp, _vp,
                                            ctypes.c_int, _vp, ctypes.c_float, _vp]),
+    "tp_stream_read_sink_words": (_sz, []),
+    "tp_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _sz, _vp]),
 }
 
 
@@ -222,6 +224,25 @@ def partial_reduce(partials, Y, stream=None) -> None:
         raise ValueError("Y must hold one partial's elements")
     _check("tp_partial_reduce", lib().tp_partial_reduce(t, n, _ptr(partials), _dt(Y), _ptr(Y),
                                                         _stream(stream, dev)))
+
+
+def stream_read(buf, sink=None, stream=None):
+    """Measurement aid: read the device tensor `buf` (its byte size a multiple
+    of 1024, at most 2 GiB) once with the decode kernels' access pattern.
+    Returns the int32 sink; the XOR of its words equals the XOR, over the
+    buffer's 16-byte chunks, of each chunk's first and last 32-bit words."""
+    torch = _torch()
+    dev = _dev(buf)
+    L = lib()
+    words = L.tp_stream_read_sink_words()
+    if sink is None:
+        sink = torch.empty(words, dtype=torch.int32, device=buf.device)
+    elif sink.dtype != torch.int32 or sink.numel() < words or not sink.is_contiguous():
+        raise ValueError(f"sink must be a contiguous int32 tensor of at least {words} words")
+    nbytes = buf.numel() * buf.element_size()
+    _check("tp_stream_read", L.tp_stream_read(_ptr(buf), nbytes, _ptr(sink), sink.numel(),
+                                              _stream(stream, dev)))
+    return sink
 
 
 def shard_mlp_fp8(X, gate, up, down, H, P, workspace=None, stream=None) -> None:

@@ -18,7 +18,7 @@ CSRC = PKG / "csrc"
 BUILD = PKG.parent / "_build"
 LIB = PKG / "libtpshard.so"
 
-SOURCES = ["gemv.hip", "gemv_fp8.hip", "splitk.hip", "rowstream.hip", "gemm.hip", "reduce.hip", "norm.hip", "attn_core.hip", "attn_decode.hip", "tpshard_api.cpp"]
+SOURCES = ["gemv.hip", "gemv_fp8.hip", "splitk.hip", "rowstream.hip", "gemm.hip", "reduce.hip", "norm.hip", "attn_core.hip", "attn_decode.hip", "probe.hip", "tpshard_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -92,6 +92,12 @@ hipError_t gemm_launch(int M, int N, int K, const uint16_t* A, int64_t lda, cons
                        const uint16_t* W1, void* out, int64_t ldo, void* workspace,
                        hipStream_t stream);
 
+// Read-only stream of `bytes` (a multiple of 1 KB, at most 2 GiB) with the
+// decode kernels' access pattern; one word per thread of the grid
+// (stream_read_sink_words) to `sink`.
+size_t stream_read_sink_words();
+hipError_t stream_read_launch(const void* buf, size_t bytes, unsigned* sink, hipStream_t stream);
+
 hipError_t reduce_launch(int t, int64_t n, const float* P, bool out_bf16, void* Y,
                          hipStream_t stream);
 

@@ -485,4 +485,17 @@ tp_status_t tp_attn_core(int64_t I, int64_t S, int64_t n_q_local, int64_t n_kv_l
                                         static_cast<uint16_t*>(A), s));
 }
 
+size_t tp_stream_read_sink_words(void) { return tpk::stream_read_sink_words(); }
+
+tp_status_t tp_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                           void* stream) {
+  if (!buf || !sink || bytes == 0 || bytes > (size_t(1) << 31)) return TP_ERR_INVALID;
+  if ((bytes % 1024) || !aligned16(buf) || !aligned16(sink)) return TP_ERR_MISALIGNED;
+  const size_t need = tpk::stream_read_sink_words();
+  if (need == 0 || sink_words < need) return TP_ERR_INVALID;
+  if (overlap(rng(buf, (int64_t)bytes), rng(sink, (int64_t)(need * 4)))) return TP_ERR_INVALID;
+  (void)hipGetLastError();
+  return launched(tpk::stream_read_launch(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

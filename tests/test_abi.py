@@ -245,3 +245,16 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(tp, "LIB_PATH", tmp_path / "missing.so")
     with pytest.raises(RuntimeError, match="missing"):
         tp.lib()
+
+
+def test_stream_read_validation(lib):
+    """The read-ceiling probe rejects a null buffer, a size that is not a
+    multiple of 1 KB, and sizes past 2 GiB, before any device query."""
+    sink_words = 1 << 20
+    assert lib.tp_stream_read(None, 1024, fake(1), sink_words, None) == INVALID
+    assert lib.tp_stream_read(fake(0), 1024, None, sink_words, None) == INVALID
+    assert lib.tp_stream_read(fake(0), 0, fake(1), sink_words, None) == INVALID
+    assert lib.tp_stream_read(fake(0), (1 << 31) + 1024, fake(1), sink_words, None) == INVALID
+    assert lib.tp_stream_read(fake(0), 1000, fake(1), sink_words, None) == MISALIGNED
+    assert lib.tp_stream_read(ctypes.c_void_p(FAKE + 8), 1024, fake(1), sink_words,
+                              None) == MISALIGNED
