@@ -207,20 +207,23 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   const int cq = (ncols + 3) / 4;
   const int rs0 = rb * NW * 16;                             // block's first row-space column
   // Sums of the ns split planes at element offsets q[0 .. NQ) (NQ = 2 for
-  // SwiGLU: the gate and the up columns), each in split order.  Eight
-  // splits of every offset are in flight per batch -- gate and up together,
-  // one memory round trip; offsets of splits past ns are out of range and
-  // read zero (x + 0 == x), so the batch needs no branch.
+  // SwiGLU: the gate and the up columns), each in split order.  16 / NQ
+  // splits of every offset are in flight per batch -- gate and up together --
+  // so up to 16 (one offset) or 8 (two) splits cost one memory round trip;
+  // offsets of splits past ns are out of range and read zero (x + 0 == x),
+  // so the batch needs no branch.  (Two items per thread in one batch would
+  // need more than the 128 registers a 1024-thread workgroup allows.)
   auto sum_splits = [&](const auto& q, auto& s) {
     constexpr int NQ = sizeof(s) / sizeof(s[0]);
+    constexpr int B = 16 / NQ;
 #pragma unroll
     for (int i = 0; i < NQ; ++i) s[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < ns; r += 8) {
-      f32x4_t v[NQ][8];
+    for (int r = 0; r < ns; r += B) {
+      f32x4_t v[NQ][B];
 #pragma unroll
       for (int i = 0; i < NQ; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int e = 0; e < B; ++e)
           v[i][e] = __builtin_bit_cast(
               f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                            pr, r + e < ns ? (uint32_t)((q[i] + (r + e) * plane) * 4) : kOob, 0,
@@ -228,7 +231,7 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
 #pragma unroll
       for (int i = 0; i < NQ; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s[i] += v[i][e];
+        for (int e = 0; e < B; ++e) s[i] += v[i][e];
     }
   };
   for (int idx = tid; idx < I * cq; idx += NW * 64) {
