@@ -47,7 +47,7 @@ constexpr uint32_t kOob = 0x80000000u;         // buffer offset past any record:
 constexpr int kAuxSys = 17;                    // sc0 sc1: system coherent
 constexpr int kCUs = 256;
 static_assert(4 * 16 * 64 * 4 <= kStageA, "a wave pair's K-group reduction fits one stage buffer");
-static_assert(4 * kStageA + 4 <= kLds, "the arrival flag follows the reduction area");
+static_assert(2 * BM * BN * 4 + 4 <= kLds, "the arrival flag follows both K groups' tiles");
 
 __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt at their maxima
@@ -70,6 +70,114 @@ __device__ __forceinline__ void store_out(void* out, int64_t ldo, int m, int col
     static_cast<float*>(out)[(int64_t)m * ldo + col] = v;
   else
     static_cast<uint16_t*>(out)[(int64_t)m * ldo + col] = f32_to_bf16_bits(v);
+}
+
+// Columns col .. col + n - 1 (n <= 4) of output row m: one 16-byte (fp32) or
+// 8-byte (bf16) store when all four are in range and aligned.
+template <int EPI>
+__device__ __forceinline__ void store_out4(void* out, int64_t ldo, int m, int col, int n,
+                                           f32x4_t v) {
+  if constexpr (EPI == EPI_F32) {
+    float* o = static_cast<float*>(out) + (int64_t)m * ldo + col;
+    if (n == 4 && (reinterpret_cast<uintptr_t>(o) & 15) == 0) {
+      *reinterpret_cast<f32x4_t*>(o) = v;
+      return;
+    }
+    for (int e = 0; e < n; ++e) o[e] = v[e];
+  } else {
+    uint16_t* o = static_cast<uint16_t*>(out) + (int64_t)m * ldo + col;
+    if (n == 4 && (reinterpret_cast<uintptr_t>(o) & 7) == 0) {
+      *reinterpret_cast<u32x2_t*>(o) =
+          u32x2_t{f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16),
+                  f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16)};
+      return;
+    }
+    for (int e = 0; e < n; ++e) o[e] = f32_to_bf16_bits(v[e]);
+  }
+}
+
+// Split-K finish, run by the last of a tile's ns workgroups: the ns fp32
+// partial tiles (TM x TN, W-tile row order, plane `plane` apart; for SwiGLU
+// the up partial of column c sits at column c + TN / 2) are summed in split
+// order and the epilogue writes out[m0 + r][c0 + c].  An item is 4 columns of
+// one row.  A thread's items are summed together rather than one after
+// another: each round trip loads kB = 4 splits of IQ / kNQ items (and of gate
+// and up), 4 IQ loads in flight, so up to 4 splits cost one memory round trip
+// per IQ / kNQ items instead of one per item and matrix.  The split's plane
+// offset is the same for every lane and travels in the scalar offset, so a
+// load needs no address register of its own.  Rows past M read zero through
+// an out-of-range lane offset, splits past ns are not loaded.  When the
+// finishing workgroup's own partial is still in LDS (own >= 0: the sum of
+// the row-major tiles own0 and own1), that split is taken from there.
+template <int EPI, int TM, int TN, int THREADS, int IQ>
+__device__ __forceinline__ void finish_splits(const __amdgpu_buffer_rsrc_t pr, int64_t tbase,
+                                              int64_t plane, int ns, int m0, int c0, int M,
+                                              int N, void* out, int64_t ldo, int tid, int own,
+                                              const f32x4_t* own0, const f32x4_t* own1) {
+  constexpr int kNQ = (EPI == EPI_SWIGLU) ? 2 : 1;  // gate and up
+  constexpr int kCols = TN / kNQ;                   // output columns of the tile
+  constexpr int kQ = kCols / 4;                     // items per tile row
+  constexpr int kNI = TM * kQ / THREADS;            // items per thread
+  constexpr int kIP = IQ / kNQ;                     // items per pass
+  constexpr int kB = 4;                             // splits per round trip
+  static_assert(TM * kQ % THREADS == 0 && kNI % kIP == 0, "whole passes of items");
+#pragma unroll 1
+  for (int p = 0; p < kNI / kIP; ++p) {
+    f32x4_t s[kIP][kNQ];
+    uint32_t off[kIP][kNQ];  // byte offset of the item in split 0
+    int fi[kIP][kNQ];        // its float4 index within the tile
+    int tr[kIP], tc[kIP];
+#pragma unroll
+    for (int i = 0; i < kIP; ++i) {
+      const int idx = tid + (p * kIP + i) * THREADS;
+      tr[i] = idx / kQ;
+      tc[i] = (idx % kQ) * 4;
+#pragma unroll
+      for (int q = 0; q < kNQ; ++q) {
+        s[i][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        fi[i][q] = (tr[i] * TN + q * kCols + tc[i]) / 4;
+        off[i][q] = m0 + tr[i] < M ? (uint32_t)((tbase + 4 * fi[i][q]) * 4) : kOob;
+      }
+    }
+    for (int s0 = 0; s0 < ns; s0 += kB) {
+      f32x4_t v[kIP][kNQ][kB];
+#pragma unroll
+      for (int e = 0; e < kB; ++e) {
+        const int sp = s0 + e;
+#pragma unroll
+        for (int i = 0; i < kIP; ++i)
+#pragma unroll
+          for (int q = 0; q < kNQ; ++q) {
+            if (sp == own)
+              v[i][q][e] = own0[fi[i][q]] + own1[fi[i][q]];
+            else if (sp < ns)
+              v[i][q][e] = __builtin_bit_cast(
+                  f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                               pr, off[i][q], (uint32_t)(sp * plane * 4), kAuxSys));
+            else
+              v[i][q][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < kIP; ++i)
+#pragma unroll
+        for (int q = 0; q < kNQ; ++q)
+#pragma unroll
+          for (int e = 0; e < kB; ++e) s[i][q] += v[i][q][e];
+    }
+#pragma unroll
+    for (int i = 0; i < kIP; ++i) {
+      const int m = m0 + tr[i];
+      if (m >= M) continue;
+      f32x4_t v = s[i][0];
+      if constexpr (EPI == EPI_SWIGLU) {
+        const f32x4_t u = s[i][1];
+        v = f32x4_t{silu(v.x) * u.x, silu(v.y) * u.y, silu(v.z) * u.z, silu(v.w) * u.w};
+      }
+      const int n = min(4, N - (c0 + tc[i]));
+      store_out4<EPI == EPI_F32 ? EPI_F32 : EPI_DT>(out, ldo, m, c0 + tc[i], n, v);
+    }
+  }
 }
 
 // One launch: grid = tiles * ns workgroups of 512 threads, 128 KB static LDS.
@@ -192,9 +300,50 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
     issue(kt + S - 1, (kt + S - 1) % S);
   }
 
-  // ---- sum the two K groups through LDS (lane-linear, conflict-free)
   wait_vmcnt<0>();  // zero-fill loads of stages past the end have landed
   __syncthreads();
+
+  if (ns > 1) {
+    // ---- split K: partial tile [BM][BN] in W-tile row order, then arrival.
+    // Both K groups write their accumulators to LDS as row-major tiles; every
+    // thread then adds the two groups over 8 runs of 4 columns and stores
+    // them with 16-byte stores: 8 store instructions per thread instead of
+    // 64 single-word ones in each wave of one group.
+    float* tg = reinterpret_cast<float*>(smem) + g * (BM * BN);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          tg[(wm * 64 + i * 32 + acc_row32(r, lane)) * BN + brow[j] + (lane & 31)] = acc[i][j][r];
+    __syncthreads();
+    const int64_t tile_elems = (int64_t)BM * BN;
+    const __amdgpu_buffer_rsrc_t pr =
+        make_rsrc(part, (uint32_t)((int64_t)ns * tiles * tile_elems * 4));
+    const int64_t tbase = (int64_t)tile * tile_elems;  // split 0 of this tile
+    const int64_t plane = (int64_t)tiles * tile_elems;
+    const f32x4_t* t0 = reinterpret_cast<const f32x4_t*>(smem);
+    const f32x4_t* t1 = t0 + BM * BN / 4;
+#pragma unroll
+    for (int k = 0; k < BM * BN / 4 / kThreads; ++k) {
+      const int q = tid + k * kThreads;
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4_t, t0[q] + t1[q]), pr,
+          (uint32_t)((split * plane + tbase + 4 * q) * 4), 0, kAuxSys);
+    }
+    int* is_last = reinterpret_cast<int*>(smem + 2 * BM * BN * 4);  // past both tiles
+    wait_vmcnt<0>();  // partial stores have reached memory
+    __syncthreads();
+    if (tid == 0) *is_last = arrive_last(counters + tile, (unsigned)ns);
+    __syncthreads();
+    if (!*is_last) return;
+    finish_splits<EPI, BM, BN, kThreads, 8>(pr, tbase, plane, ns, m0, c0, M, N, out, ldo, tid,
+                                            split, t0, t1);
+    return;
+  }
+
+  // ---- sum the two K groups through LDS (lane-linear, conflict-free)
   const int pair = wave & 3;  // waves pair and pair + 4 hold the same tile
   float* red = reinterpret_cast<float*>(smem + pair * kStageA);
   if (g == 1) {
@@ -215,97 +364,30 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
         for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * 2 + j) * 16 + r) * 64 + lane];
   }
 
-  if (ns == 1) {
-    if (g != 0) return;
-    // ---- direct epilogue
-    if constexpr (EPI == EPI_SWIGLU) {
-      const int col = c0 + wn * 32 + (lane & 31);
+  if (g != 0) return;
+  // ---- direct epilogue
+  if constexpr (EPI == EPI_SWIGLU) {
+    const int col = c0 + wn * 32 + (lane & 31);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * 64 + i * 32 + acc_row32(r, lane);
-          if (m < M && col < N)
-            store_out<EPI_DT>(out, ldo, m, col, silu(acc[i][0][r]) * acc[i][1][r]);
-        }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = c0 + wn * 64 + j * 32 + (lane & 31);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = m0 + wm * 64 + i * 32 + acc_row32(r, lane);
-            if (m < M && col < N) store_out<EPI>(out, ldo, m, col, acc[i][j][r]);
-          }
-        }
-    }
-    return;
-  }
-
-  // ---- split K: partial tile [BM][BN] in W-tile row order, then arrival
-  const int64_t tile_elems = (int64_t)BM * BN;
-  const __amdgpu_buffer_rsrc_t pr =
-      make_rsrc(part, (uint32_t)((int64_t)ns * tiles * tile_elems * 4));
-  const int64_t tbase = (int64_t)tile * tile_elems;  // split 0 of this tile
-  const int64_t plane = (int64_t)tiles * tile_elems;
-  if (g == 0) {
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 64 + i * 32 + acc_row32(r, lane);
+        if (m < M && col < N)
+          store_out<EPI_DT>(out, ldo, m, col, silu(acc[i][0][r]) * acc[i][1][r]);
+      }
+  } else {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int tc = brow[j] + (lane & 31);
+        const int col = c0 + wn * 64 + j * 32 + (lane & 31);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int tr = wm * 64 + i * 32 + acc_row32(r, lane);
-          const float v = acc[i][j][r];
-          __builtin_amdgcn_raw_buffer_store_b32(
-              __builtin_bit_cast(uint32_t, v), pr,
-              (uint32_t)((split * plane + tbase + tr * BN + tc) * 4), 0, kAuxSys);
+          const int m = m0 + wm * 64 + i * 32 + acc_row32(r, lane);
+          if (m < M && col < N) store_out<EPI>(out, ldo, m, col, acc[i][j][r]);
         }
       }
-  }
-  int* is_last = reinterpret_cast<int*>(smem + 4 * kStageA);  // past the reduction area
-  wait_vmcnt<0>();  // partial stores have reached memory
-  __syncthreads();
-  if (tid == 0) *is_last = arrive_last(counters + tile, (unsigned)ns);
-  __syncthreads();
-  if (!*is_last) return;
-
-  // Sum of the ns split tiles at element offset q (split 0), in split order;
-  // eight loads in flight, offsets past the last split read zero.
-  auto sum_splits = [&](int64_t q) {
-    f32x4_t s4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < ns; s += 8) {
-      f32x4_t v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        v[e] = __builtin_bit_cast(
-            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                         pr, s + e < ns ? (uint32_t)((q + (s + e) * plane) * 4) : kOob, 0,
-                         kAuxSys));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s4 += v[e];
-    }
-    return s4;
-  };
-  constexpr int kQ = kCols / 4;  // float4 items per output row of the tile
-  for (int idx = tid; idx < BM * kQ; idx += kThreads) {
-    const int tr = idx / kQ, tc = (idx % kQ) * 4;
-    const int m = m0 + tr;
-    if (m >= M) continue;
-    const f32x4_t s4 = sum_splits(tbase + tr * BN + tc);
-    f32x4_t v;
-    if constexpr (EPI == EPI_SWIGLU) {
-      const f32x4_t u = sum_splits(tbase + tr * BN + 64 + tc);
-      v = f32x4_t{silu(s4.x) * u.x, silu(s4.y) * u.y, silu(s4.z) * u.z, silu(s4.w) * u.w};
-    } else {
-      v = s4;
-    }
-    const int n = min(4, N - (c0 + tc));
-    for (int e = 0; e < n; ++e)
-      store_out<EPI == EPI_F32 ? EPI_F32 : EPI_DT>(out, ldo, m, c0 + tc + e, v[e]);
   }
 }
 
@@ -566,39 +648,8 @@ gemm_big_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda
   if (tid == 0) *is_last = arrive_last(counters + tile, (unsigned)ns);
   __syncthreads();
   if (!*is_last) return;
-
-  auto sum_splits = [&](int64_t q) {
-    f32x4_t s4 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < ns; s += 8) {
-      f32x4_t v[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        v[e] = __builtin_bit_cast(
-            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                         pr, s + e < ns ? (uint32_t)((q + (s + e) * plane) * 4) : kOob, 0,
-                         kAuxSys));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s4 += v[e];
-    }
-    return s4;
-  };
-  constexpr int kQ = kCols / 4;
-  for (int idx = tid; idx < BB * kQ; idx += kThr) {
-    const int tr = idx / kQ, tc = (idx % kQ) * 4;
-    const int m = m0 + tr;
-    if (m >= M) continue;
-    const f32x4_t s4 = sum_splits(tbase + tr * BB + tc);
-    f32x4_t v;
-    if constexpr (EPI == EPI_SWIGLU) {
-      const f32x4_t u = sum_splits(tbase + tr * BB + 128 + tc);
-      v = f32x4_t{silu(s4.x) * u.x, silu(s4.y) * u.y, silu(s4.z) * u.z, silu(s4.w) * u.w};
-    } else {
-      v = s4;
-    }
-    const int n = min(4, N - (c0 + tc));
-    for (int e = 0; e < n; ++e)
-      store_out<EPI == EPI_F32 ? EPI_F32 : EPI_DT>(out, ldo, m, c0 + tc + e, v[e]);
-  }
+  finish_splits<EPI, BB, BB, kThr, 4>(pr, tbase, plane, ns, m0, c0, M, N, out, ldo, tid, -1,
+                                      nullptr, nullptr);
 }
 
 struct Plan {
