@@ -227,9 +227,21 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
   // is out of range and the slot is zero-filled.
   const int rr = lane >> 3, sl = lane & 7;
   const uint32_t lsm = lds_addr(smem);
+  // Stage order.  Weight rows K * 2 bytes apart, with K a multiple of 2048
+  // (16 KB rows at D = 8192), put every workgroup of a split on the same low
+  // address bits at once while they stream in lockstep, which crowds a few
+  // memory channels.  With one M block (no W tile shared through L2 by
+  // neighbouring workgroups) each W tile therefore starts its K range at
+  // stage tn % NT and wraps around: 64-token gate/up 37.7 -> 30.0 us.  With
+  // several M blocks the common order is kept: rotating it there lost the
+  // L2 reuse of shared tiles (512-token gate/up 77 -> 89 us).
+  const int NT = (ke - kb + BK - 1) / BK;
+  const int rot = (mt_n == 1 && K % 2048 == 0) ? tn % NT : 0;
   auto issue = [&](int st, int buf) {
     const uint32_t la = lsm + buf * kStage, lb = la + kStageA;
-    const int k0 = kb + st * BK;
+    int sr = st + rot;  // stages past NT - 1 start at ke: zero-filled
+    if (sr >= NT) sr = st < NT ? sr - NT : NT;
+    const int k0 = kb + sr * BK;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int q = wave + h * 8;
@@ -269,7 +281,6 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int NT = (ke - kb + BK - 1) / BK;
 #pragma unroll
   for (int st = 0; st < S - 1; ++st) issue(st, st);
 

@@ -39,6 +39,9 @@ SMALL = [
     (64, 136, 72, 2, 1, "bf16"), (65, 264, 200, 1, 0, "bf16"), (130, 520, 136, 2, 1, "bf16"),
     (257, 264, 200, 2, 1, "bf16"), (33, 72, 24, 2, 1, "bf16"), (48, 1000, 1000, 1, 0, "bf16"),
     (16, 2048, 4096, 1, 0, "bf16"),
+    # one M block with K a multiple of 2048: the GEMM starts each W tile's K
+    # range at a different stage (and wraps), split K on both
+    (80, 2048, 200, 2, 1, "bf16"), (100, 4096, 136, 1, 0, "bf16"),
     # whole-K row blocks (9..32 tokens, 128..256 workgroups): gate/up with a
     # ragged last K slice, down with a ragged last row block, a full grid
     (20, 1040, 2064, 1, 0, "bf16"), (9, 4104, 1032, 1, 0, "bf16"), (32, 1024, 4096, 1, 0, "bf16"),
