@@ -18,9 +18,9 @@ exceed the 256 MB Infinity Cache, so every step streams them from HBM.
 
 The printed JSON line also carries
   roofline:     the dominant call (one rank's tp_shard_mlp at I=32) timed with
-                HIP events on its stream inside the timed region (one rank's
-                call per step, rotating over the ranks), against the 8 TB/s
-                HBM peak;
+                HIP events on its stream inside the timed region (one event
+                pair per step around the 8 ranks' back-to-back calls, divided
+                by 8), against the 8 TB/s HBM peak;
   read_ceiling: the achievable read rate, tp_stream_read over 2 GiB with the
                 decode kernels' access pattern; roofline and config also give
                 their fraction of it;
@@ -221,7 +221,7 @@ class Layer:
                     y=T.empty((I, D), dtype=f32, device="cuda"),
                     x=T.empty((I, D), dtype=bf, device="cuda"))
 
-    def step(self, X, B, S, mlp_events=None, timed_rank=0):
+    def step(self, X, B, S, mlp_events=None):
         tp = self.tp
         for r, R in enumerate(self.ranks):
             tp.shard_attn_proj(tp.TP_ATTN_QKV, X, R["qkv"], B["qkv"], self.nql, self.nkl, HD)
@@ -229,15 +229,14 @@ class Layer:
             tp.shard_attn_proj(tp.TP_ATTN_O, B["A"], R["o"], B["po"][r], self.nql, self.nkl, HD)
         tp.partial_reduce(B["po"], B["y1"])
         s = self.torch.cuda.current_stream()
+        if mlp_events is not None:  # one event pair around the 8 back-to-back calls
+            e0, e1 = (self.torch.cuda.Event(enable_timing=True) for _ in range(2))
+            e0.record(s)
         for r, R in enumerate(self.ranks):
-            timed = mlp_events is not None and r == timed_rank
-            if timed:  # one rank's call per step: few event records in the stream
-                e0, e1 = (self.torch.cuda.Event(enable_timing=True) for _ in range(2))
-                e0.record(s)
             tp.shard_mlp(B["y1"], *R["mlp"], B["H"], B["pm"][r])
-            if timed:
-                e1.record(s)
-                mlp_events.append((e0, e1))
+        if mlp_events is not None:
+            e1.record(s)
+            mlp_events.append((e0, e1))
         tp.partial_reduce(B["pm"], B["y"])
 
 
@@ -578,7 +577,7 @@ def main():
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for k in range(args.steps):
-        layer.step(X, B, S, mlp_events=mlp_ev, timed_rank=k % TP)
+        layer.step(X, B, S, mlp_events=mlp_ev)
     e1.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
@@ -587,7 +586,7 @@ def main():
     value = nbytes / (ms * 1e-3) / 1e9
 
     log(f"timed {args.steps} steps: {ms:.3f} ms/step")
-    mlp_us = statistics.mean(a.elapsed_time(b) * 1e3 for a, b in mlp_ev)
+    mlp_us = statistics.mean(a.elapsed_time(b) * 1e3 for a, b in mlp_ev) / TP  # per call
     mlp_bytes = wl.MlpShape(I, D, F // TP).bytes()
     achieved = mlp_bytes / (mlp_us * 1e-6) / 1e9
     roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM, unit="GB/s",
