@@ -42,6 +42,9 @@ SMALL = [
     # one M block with K a multiple of 2048: the GEMM starts each W tile's K
     # range at a different stage (and wraps), split K on both
     (80, 2048, 200, 2, 1, "bf16"), (100, 4096, 136, 1, 0, "bf16"),
+    # one gate/up tile split 16 ways: the finishing workgroup sums its items
+    # over four rounds of 4 splits
+    (70, 8192, 64, 1, 0, "bf16"),
     # whole-K row blocks (9..32 tokens, 128..256 workgroups): gate/up with a
     # ragged last K slice, down with a ragged last row block, a full grid
     (20, 1040, 2064, 1, 0, "bf16"), (9, 4104, 1032, 1, 0, "bf16"), (32, 1024, 4096, 1, 0, "bf16"),
