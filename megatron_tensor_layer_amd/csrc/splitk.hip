@@ -49,8 +49,8 @@ constexpr int kCUs = 256;
 // matrix (N rows): block rb covers rows [16 NW rb, 16 NW (rb + 1)).  SwiGLU
 // (gate W0 and up W1, N rows each): block rb covers F rows f0 = 8 NW rb ..
 // f0 + 8 NW, its first NW/2 tiles from gate, the other NW/2 from up.
-template <int MT, int P, int EPI, bool F8>
-__global__ void __launch_bounds__(1024)
+template <int MT, int P, int EPI, bool F8, int MAXT>
+__global__ void __launch_bounds__(MAXT)
 splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
               const void* __restrict__ W0, const void* __restrict__ W1,
               const float* __restrict__ S0, const float* __restrict__ S1, int KR,
@@ -211,11 +211,12 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   // splits of every offset are in flight per batch -- gate and up together --
   // so up to 16 (one offset) or 8 (two) splits cost one memory round trip;
   // offsets of splits past ns are out of range and read zero (x + 0 == x),
-  // so the batch needs no branch.  (Two items per thread in one batch would
-  // need more than the 128 registers a 1024-thread workgroup allows.)
+  // so the batch needs no branch.  A workgroup of at most 4 waves (launch
+  // bound 256) has the registers for 32 loads in flight: its threads sum two
+  // items per batch (a 1024-thread bound leaves 128 registers, too few).
   auto sum_splits = [&](const auto& q, auto& s) {
     constexpr int NQ = sizeof(s) / sizeof(s[0]);
-    constexpr int B = 16 / NQ;
+    constexpr int B = (MAXT <= 256 ? 32 : 16) / NQ;
 #pragma unroll
     for (int i = 0; i < NQ; ++i) s[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int r = 0; r < ns; r += B) {
@@ -234,6 +235,35 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
         for (int e = 0; e < B; ++e) s[i] += v[i][e];
     }
   };
+  auto store_item = [&](int m, int c, int n, const f32x4_t& v) {
+    if constexpr (EPI == EPI_F32) {
+      float* o = static_cast<float*>(out) + (int64_t)m * ldo + cbase + c;
+      if (n == 4 && ((reinterpret_cast<uintptr_t>(o) & 15) == 0)) {
+        *reinterpret_cast<f32x4_t*>(o) = v;
+      } else {
+        for (int e = 0; e < n; ++e) o[e] = v[e];
+      }
+    } else {
+      uint16_t* o = static_cast<uint16_t*>(out) + (int64_t)m * ldo + cbase + c;
+      for (int e = 0; e < n; ++e) o[e] = f32_to_bf16_bits(v[e]);
+    }
+  };
+  if constexpr (MAXT <= 256 && EPI != EPI_SWIGLU && !F8) {
+    // items idx and idx + NW * 64 of a thread summed in one batch
+    const int step = NW * 64;
+    for (int idx = tid; idx < I * cq; idx += 2 * step) {
+      const int idx2 = idx + step;
+      const bool has2 = idx2 < I * cq;
+      const int m = idx / cq, c = (idx % cq) * 4;
+      const int m2 = has2 ? idx2 / cq : m, c2 = has2 ? (idx2 % cq) * 4 : c;
+      const int64_t qq[2] = {(int64_t)m * NR + rs0 + c, (int64_t)m2 * NR + rs0 + c2};
+      f32x4_t sv[2];
+      sum_splits(qq, sv);
+      store_item(m, c, min(4, ncols - c), sv[0]);
+      if (has2) store_item(m2, c2, min(4, ncols - c2), sv[1]);
+    }
+    return;
+  }
   for (int idx = tid; idx < I * cq; idx += NW * 64) {
     const int m = idx / cq, c = (idx % cq) * 4;
     const int64_t q = (int64_t)m * NR + rs0 + c;
@@ -272,17 +302,7 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
       }
       v = s4;
     }
-    if constexpr (EPI == EPI_F32) {
-      float* o = static_cast<float*>(out) + (int64_t)m * ldo + cbase + c;
-      if (n == 4 && ((reinterpret_cast<uintptr_t>(o) & 15) == 0)) {
-        *reinterpret_cast<f32x4_t*>(o) = v;
-      } else {
-        for (int e = 0; e < n; ++e) o[e] = v[e];
-      }
-    } else {
-      uint16_t* o = static_cast<uint16_t*>(out) + (int64_t)m * ldo + cbase + c;
-      for (int e = 0; e < n; ++e) o[e] = f32_to_bf16_bits(v[e]);
-    }
+    store_item(m, c, n, v);
   }
 }
 
@@ -356,13 +376,17 @@ template <int MT, int EPI, bool F8 = false>
 hipError_t launch_plan(const Plan& pl, int I, int K, int N, const uint16_t* X, const void* W0,
                        const void* W1, void* out, int64_t ldo, void* workspace,
                        hipStream_t stream, const float* S0 = nullptr, const float* S1 = nullptr) {
-  auto kern = splitk_kernel<MT, F8 ? 4 : 2, EPI, F8>;
-  static bool attr_set = false;  // raising the dynamic-LDS limit once per process is enough
-  if (!attr_set) {
+  // plans of at most 4 waves run the variant bounded to 256 threads (more
+  // registers per wave: the finish sums two items per batch)
+  const bool small = pl.nw <= 4;
+  auto kern = small ? splitk_kernel<MT, F8 ? 4 : 2, EPI, F8, 256>
+                    : splitk_kernel<MT, F8 ? 4 : 2, EPI, F8, 1024>;
+  static bool attr_set[2] = {false, false};  // raising the dynamic-LDS limit once is enough
+  if (!attr_set[small]) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set[small] = true;
   }
   if (pl.rbs > kWsMaxCounters) return hipErrorInvalidValue;
   auto* counters = static_cast<unsigned*>(workspace);
