@@ -32,7 +32,9 @@ The printed JSON line also carries
                 update + RMSNorm after a block, the layer as a pre-norm block
                 with those at decode 32, the MLP with weight-only FP8
                 storage at decode 1, 8 and 32, and decode attention over a
-                rank's KV cache).
+                rank's KV cache); calls rotating over weight sets are timed
+                in groups of back-to-back calls, one per set, with one event
+                pair per group, queued behind a spin kernel.
 """
 from __future__ import annotations
 
@@ -82,20 +84,50 @@ def to_dev(torch, a, dtype="bf16"):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
+_SPIN_US_PER_MCYCLE = None
+
+
+def _spin_cycles(torch, us):
+    """Cycles of torch's spin kernel that keep the GPU busy for about `us`
+    microseconds (calibrated once)."""
+    global _SPIN_US_PER_MCYCLE
+    if not hasattr(torch.cuda, "_sleep"):
+        return 0
+    if _SPIN_US_PER_MCYCLE is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1_000_000)
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SPIN_US_PER_MCYCLE = max(a.elapsed_time(b) * 1e3, 1.0)
+    return int(us / _SPIN_US_PER_MCYCLE * 1e6)
+
+
 def time_calls(torch, fns, n, warm=10):
-    """Event-time n calls, cycling through fns (one per weight set); returns
-    per-call microseconds."""
+    """Event-time about n calls, cycling through fns (one per weight set) in
+    groups of len(fns) back-to-back calls with one event pair per group (an
+    event pair around every call adds about 3 us to a decode call).  A spin
+    kernel ahead of each group keeps the GPU busy while the host queues the
+    group, so calls shorter than the binding's host overhead (about 10 us)
+    are timed on the device, not on the host.  Returns per-call
+    microseconds, one figure per group."""
     for i in range(warm):
         fns[i % len(fns)]()
+    groups = max(1, n // len(fns))
+    spin = _spin_cycles(torch, 15.0 * len(fns) + 50.0)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n)]
+          for _ in range(groups)]
     s = torch.cuda.current_stream()
-    for i in range(n):
-        ev[i][0].record(s)
-        fns[i % len(fns)]()
-        ev[i][1].record(s)
+    for g in range(groups):
+        if spin:
+            torch.cuda._sleep(spin)
+        ev[g][0].record(s)
+        for f in fns:
+            f()
+        ev[g][1].record(s)
     torch.cuda.synchronize()
-    return [a.elapsed_time(b) * 1e3 for a, b in ev]
+    return [a.elapsed_time(b) * 1e3 / len(fns) for a, b in ev]
 
 
 def log(msg):
