@@ -314,28 +314,31 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
   wait_vmcnt<0>();  // zero-fill loads of stages past the end have landed
   __syncthreads();
 
+  // ---- both K groups write their accumulators to LDS as row-major [BM][BN]
+  // tiles (W-tile row order; for SwiGLU the up column of gate column c sits
+  // at c + 64); every thread then adds the two groups over runs of 4 columns
+  // and stores 16-byte (fp32) or 8-byte (bf16) runs -- a few store
+  // instructions per thread instead of 32..64 single-element stores in each
+  // wave of one group
+  float* tg = reinterpret_cast<float*>(smem) + g * (BM * BN);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        tg[(wm * 64 + i * 32 + acc_row32(r, lane)) * BN + brow[j] + (lane & 31)] = acc[i][j][r];
+  __syncthreads();
+  const f32x4_t* t0 = reinterpret_cast<const f32x4_t*>(smem);
+  const f32x4_t* t1 = t0 + BM * BN / 4;
+
   if (ns > 1) {
-    // ---- split K: partial tile [BM][BN] in W-tile row order, then arrival.
-    // Both K groups write their accumulators to LDS as row-major tiles; every
-    // thread then adds the two groups over 8 runs of 4 columns and stores
-    // them with 16-byte stores: 8 store instructions per thread instead of
-    // 64 single-word ones in each wave of one group.
-    float* tg = reinterpret_cast<float*>(smem) + g * (BM * BN);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          tg[(wm * 64 + i * 32 + acc_row32(r, lane)) * BN + brow[j] + (lane & 31)] = acc[i][j][r];
-    __syncthreads();
+    // ---- split K: partial tile [BM][BN], then arrival
     const int64_t tile_elems = (int64_t)BM * BN;
     const __amdgpu_buffer_rsrc_t pr =
         make_rsrc(part, (uint32_t)((int64_t)ns * tiles * tile_elems * 4));
     const int64_t tbase = (int64_t)tile * tile_elems;  // split 0 of this tile
     const int64_t plane = (int64_t)tiles * tile_elems;
-    const f32x4_t* t0 = reinterpret_cast<const f32x4_t*>(smem);
-    const f32x4_t* t1 = t0 + BM * BN / 4;
 #pragma unroll
     for (int k = 0; k < BM * BN / 4 / kThreads; ++k) {
       const int q = tid + k * kThreads;
@@ -354,51 +357,21 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
     return;
   }
 
-  // ---- sum the two K groups through LDS (lane-linear, conflict-free)
-  const int pair = wave & 3;  // waves pair and pair + 4 hold the same tile
-  float* red = reinterpret_cast<float*>(smem + pair * kStageA);
-  if (g == 1) {
+  // ---- direct epilogue: item = 4 output columns of one row
+  constexpr int kQ = kCols / 4;  // items per tile row
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) red[((i * 2 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
-  }
-  __syncthreads();
-  if (g == 0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * 2 + j) * 16 + r) * 64 + lane];
-  }
-
-  if (g != 0) return;
-  // ---- direct epilogue
-  if constexpr (EPI == EPI_SWIGLU) {
-    const int col = c0 + wn * 32 + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * 64 + i * 32 + acc_row32(r, lane);
-        if (m < M && col < N)
-          store_out<EPI_DT>(out, ldo, m, col, silu(acc[i][0][r]) * acc[i][1][r]);
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = c0 + wn * 64 + j * 32 + (lane & 31);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * 64 + i * 32 + acc_row32(r, lane);
-          if (m < M && col < N) store_out<EPI>(out, ldo, m, col, acc[i][j][r]);
-        }
-      }
+  for (int k = 0; k < BM * kQ / kThreads; ++k) {
+    const int idx = tid + k * kThreads;
+    const int tr = idx / kQ, tc = (idx % kQ) * 4;
+    const int m = m0 + tr;
+    if (m >= M || c0 + tc >= N) continue;
+    const int fi = (tr * BN + tc) / 4;
+    f32x4_t v = t0[fi] + t1[fi];
+    if constexpr (EPI == EPI_SWIGLU) {
+      const f32x4_t u = t0[fi + 16] + t1[fi + 16];  // up: 64 columns on
+      v = f32x4_t{silu(v.x) * u.x, silu(v.y) * u.y, silu(v.z) * u.z, silu(v.w) * u.w};
+    }
+    store_out4<EPI == EPI_F32 ? EPI_F32 : EPI_DT>(out, ldo, m, c0 + tc, min(4, N - (c0 + tc)), v);
   }
 }
 
