@@ -42,6 +42,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 
+// The same resource from values the compiler cannot prove wave-uniform (a
+// pointer or size derived from the wave index): every word is taken from the
+// first active lane, so the descriptor lives in scalar registers and the
+// loads that use it need no per-lane waterfall loop.  The caller guarantees
+// that the values are uniform across the wave.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_uniform(const void* base,
+                                                                     uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint64_t au = ((uint64_t)hi << 32) | lo;
+  return make_rsrc(reinterpret_cast<const void*>(au), __builtin_amdgcn_readfirstlane(bytes));
+}
+
+// The value unchanged, but opaque to the optimizer.  A buffer load whose
+// offset is a select (an in-range offset or an out-of-range one that reads
+// zero) is otherwise split into two exec-masked loads, one per arm, and the
+// second arm then waits for every load in flight (vmcnt(0)) before it may
+// reuse the destination registers.  With the select materialised first
+// there is one load and no branch.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 constexpr int kAuxNT = 2;  // non-temporal hint: streamed once, do not keep in cache
 
 // 16-byte load at byte offset `off` of a buffer resource.

@@ -86,7 +86,7 @@ rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   }
   const int rows = max(0, min(RPT, N - wrow0));
   const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(static_cast<const unsigned char*>(wmat) + (rows ? (int64_t)wrow0 * K * ES : 0),
+      make_rsrc_uniform(static_cast<const unsigned char*>(wmat) + (rows ? (int64_t)wrow0 * K * ES : 0),
                 (uint32_t)rows * (uint32_t)K * (uint32_t)ES);
   const int kb = sl * KS, ke = min(K, kb + KS);  // this wave's K slice
   const int NC = KS / kKC;                       // chunks per slice (same for all)
@@ -104,7 +104,7 @@ rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
 #pragma unroll
     for (int p = 0; p < LPG; ++p) {
       const uint32_t r = RPI * p + lane / CPR;
-      v[p] = buf_load16<kAuxNT>(wr, ok ? (r * (uint32_t)K + (uint32_t)k) * (uint32_t)ES : kOob);
+      v[p] = buf_load16<kAuxNT>(wr, opaque(ok ? (r * (uint32_t)K + (uint32_t)k) * (uint32_t)ES : kOob));
     }
   };
 

@@ -99,7 +99,7 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   }
   const int rows = max(0, min(16, N - wrow0));
   const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(static_cast<const unsigned char*>(wmat) + (int64_t)wrow0 * K * ES,
+      make_rsrc_uniform(static_cast<const unsigned char*>(wmat) + (int64_t)wrow0 * K * ES,
                 (uint32_t)rows * (uint32_t)K * (uint32_t)ES);
   const int NG = (kend - k0 + kGK - 1) / kGK;
 
@@ -115,7 +115,7 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
 #pragma unroll
     for (int p = 0; p < LPG; ++p) {
       const uint32_t r = RPI * p + lane / CPR;
-      v[p] = buf_load16<kAuxNT>(wr, ok ? (r * (uint32_t)K + (uint32_t)k) * (uint32_t)ES : kOob);
+      v[p] = buf_load16<kAuxNT>(wr, opaque(ok ? (r * (uint32_t)K + (uint32_t)k) * (uint32_t)ES : kOob));
     }
   };
 
@@ -127,14 +127,14 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // the activation loads are older than every weight load: once group 0 has
   // landed, so has this wave's share of X; the barrier publishes all shares
-  wait_vmcnt<(P - 1) * 4>();
+  wait_vmcnt<(P - 1) * LPG>();
   __syncthreads();
 
   for (int g0 = 0; g0 < NG; g0 += P) {
 #pragma unroll
     for (int b = 0; b < P; ++b) {
       const int g = g0 + b;
-      wait_vmcnt<(P - 1) * 4>();
+      wait_vmcnt<(P - 1) * LPG>();
       // transpose through the tile: row r, bf16 chunk c at slot c ^ r
       if constexpr (F8) {
 #pragma unroll
