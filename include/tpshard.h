@@ -94,11 +94,14 @@ size_t tp_shard_mlp_workspace_size(int64_t I, int64_t D, int64_t F_local, tp_dty
  *           bf16 calls that split K over workgroups (9..256 tokens, by
  *           shape) keep arrival counters and fp32 partial sums there.  The
  *           first 8 KiB (the counters) must be zero before the workspace's
- *           first use (one hipMemset after allocating it); every completed
- *           call leaves them zero again, so one workspace serves any sequence
- *           of calls on one stream.  The rest is scratch: contents on entry
- *           ignored, on return undefined.  Two calls in flight at once
- *           (other streams) need separate workspaces.
+ *           first use (tp_workspace_reset, once after allocating it); every
+ *           completed call leaves them zero again, so one workspace serves
+ *           any sequence of calls on one stream.  Counters left non-zero (a
+ *           workspace never reset, or a call that did not complete) make
+ *           later calls produce wrong output without an error: reset then.
+ *           The rest is scratch: contents on entry ignored, on return
+ *           undefined.  Two calls in flight at once (other streams) need
+ *           separate workspaces.
  * Errors: TP_ERR_INVALID, TP_ERR_MISALIGNED (D or F_local not a multiple of 8,
  * a pointer not 16-byte aligned), TP_ERR_WORKSPACE, TP_ERR_LAUNCH.
  */
@@ -271,6 +274,21 @@ tp_status_t tp_attn_decode(int64_t B, int64_t n_q_local, int64_t n_kv_local, int
  */
 tp_status_t tp_attn_core(int64_t I, int64_t S, int64_t n_q_local, int64_t n_kv_local,
                          int64_t head_dim, const void* qkv, void* A, void* stream);
+
+/*
+ * Prepare a workspace for the calls above that take one: enqueue on `stream`
+ * a fill kernel that zeroes its leading counter area (the first
+ * min(workspace_bytes, 8 KiB) bytes; the rest is scratch and left alone).
+ * Split sums keep one 32-bit arrival counter per output block there; every
+ * completed call leaves them zero again, so one reset after allocating a
+ * workspace serves any sequence of calls on one stream.  Reset again after a
+ * call that did not run to completion, or when handing a workspace that was
+ * used for anything else to these calls.  It is a kernel, not a memset, so it
+ * may be recorded into a HIP graph.
+ * Errors: TP_ERR_INVALID (NULL, zero bytes), TP_ERR_MISALIGNED (not 16-byte
+ * aligned), TP_ERR_LAUNCH.
+ */
+tp_status_t tp_workspace_reset(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Measurement aid (not a step of the layer): the achievable read rate.

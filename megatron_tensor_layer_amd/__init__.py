@@ -48,6 +48,7 @@ SIGNATURES = {
     "tp_shard_mlp_fp8": (ctypes.c_int, [_i64, _i64, _i64] + [_vp] * 10 + [_sz, _vp]),
     "tp_residual_rmsnorm": (ctypes.c_int, [_i32, _i64, _i64, _vp, _vp, ctypes.c_int, _vp, _vp,
                                            ctypes.c_int, _vp, ctypes.c_float, _vp]),
+    "tp_workspace_reset": (ctypes.c_int, [_vp, _sz, _vp]),
     "tp_stream_read_sink_words": (_sz, []),
     "tp_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _sz, _vp]),
 }
@@ -129,23 +130,40 @@ def attn_workspace_bytes(phase: int, I: int, D: int, n_q_local: int, n_kv_local:
                                                    head_dim, dtype)
 
 
-# One scratch buffer per device, grown on demand, used when a caller passes no
-# workspace.  It is allocated zero-filled: its leading counter area must be
-# zero before first use, and every completed call leaves it zero.  Calls that
-# may run concurrently on different streams of one device must pass their own
-# workspace instead (zero-filled the same way).
+# One scratch buffer per (device, stream), grown on demand, used when a caller
+# passes no workspace.  A new buffer's leading counter area is zeroed with
+# tp_workspace_reset on the call's stream before its first use; every
+# completed call leaves it zero.  Keying by stream keeps calls that run
+# concurrently on different streams off each other's counters.  A buffer
+# that is outgrown is kept alive (not freed), since a call still in flight on
+# its stream may be using it.
 _ws_cache: dict = {}
+_ws_retired: list = []
 
 
-def _workspace(dev, nbytes: int):
+def _workspace(dev, nbytes: int, stream=None):
     if nbytes <= 0:
         return None, 0
     torch = _torch()
-    buf = _ws_cache.get(dev)
+    s = _stream(stream, dev)
+    key = (dev, s.value)
+    buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
-        _ws_cache[dev] = buf
+        if buf is not None:
+            _ws_retired.append(buf)
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _check("tp_workspace_reset", lib().tp_workspace_reset(_ptr(buf), buf.numel(), s))
+        _ws_cache[key] = buf
     return _ptr(buf), buf.numel()
+
+
+def workspace_reset(workspace, stream=None) -> None:
+    """Zero the counter area of a caller-owned workspace (once after
+    allocating it, or after a call that did not complete)."""
+    dev = _dev(workspace)
+    _check("tp_workspace_reset",
+           lib().tp_workspace_reset(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _stream(stream, dev)))
 
 
 def _user_workspace(workspace):
@@ -173,7 +191,7 @@ def shard_mlp(X, W_gate, W_up, W_down, H, P, workspace=None, stream=None) -> Non
     if workspace is not None:
         ws_ptr, ws_bytes = _user_workspace(workspace)
     else:
-        ws_ptr, ws_bytes = _workspace(dev, mlp_workspace_bytes(I, D, F_local, dt))
+        ws_ptr, ws_bytes = _workspace(dev, mlp_workspace_bytes(I, D, F_local, dt), stream)
     _check("tp_shard_mlp", lib().tp_shard_mlp(I, D, F_local, dt, _ptr(X), _ptr(W_gate),
                                               _ptr(W_up), _ptr(W_down), _ptr(H), _ptr(P),
                                               ws_ptr, ws_bytes, _stream(stream, dev)))
@@ -206,7 +224,7 @@ def shard_attn_proj(phase: int, inp, W, out, n_q_local: int, n_kv_local: int, he
         ws_ptr, ws_bytes = _user_workspace(workspace)
     else:
         ws_ptr, ws_bytes = _workspace(dev, attn_workspace_bytes(phase, I, D, n_q_local,
-                                                                n_kv_local, head_dim, dt))
+                                                                n_kv_local, head_dim, dt), stream)
     _check("tp_shard_attn_proj",
            lib().tp_shard_attn_proj(phase, I, D, n_q_local, n_kv_local, head_dim, dt, _ptr(inp),
                                     _ptr(W), _ptr(out), ws_ptr, ws_bytes, _stream(stream, dev)))
@@ -268,7 +286,8 @@ def shard_mlp_fp8(X, gate, up, down, H, P, workspace=None, stream=None) -> None:
     if workspace is not None:
         ws_ptr, ws_bytes = _user_workspace(workspace)
     else:
-        ws_ptr, ws_bytes = _workspace(dev, lib().tp_shard_mlp_fp8_workspace_size(I, D, F_local))
+        ws_ptr, ws_bytes = _workspace(dev, lib().tp_shard_mlp_fp8_workspace_size(I, D, F_local),
+                                      stream)
     _check("tp_shard_mlp_fp8", lib().tp_shard_mlp_fp8(
         I, D, F_local, _ptr(X), _ptr(Wg), _ptr(sg), _ptr(Wu), _ptr(su), _ptr(Wd), _ptr(sd),
         _ptr(H), _ptr(P), ws_ptr, ws_bytes, _stream(stream, dev)))
@@ -358,7 +377,7 @@ def attn_decode(lens, qkv, K_cache, V_cache, A, n_q_local: int, n_kv_local: int,
         ws_ptr, ws_bytes = _user_workspace(workspace)
     else:
         ws_ptr, ws_bytes = _workspace(dev, lib().tp_attn_decode_workspace_size(
-            B, n_q_local, n_kv_local, head_dim, L_max))
+            B, n_q_local, n_kv_local, head_dim, L_max), stream)
     _check("tp_attn_decode", lib().tp_attn_decode(
         B, n_q_local, n_kv_local, head_dim, L_max, _ptr(lens), _ptr(qkv), _ptr(K_cache),
         _ptr(V_cache), _ptr(A), ws_ptr, ws_bytes, _stream(stream, dev)))

@@ -16,6 +16,9 @@ namespace tpk {
 // calls of any shape share one workspace.
 constexpr size_t kWsCounterBytes = 8192;
 constexpr int kWsMaxCounters = int(kWsCounterBytes / 4);
+// Zero the counter area (the first min(bytes, kWsCounterBytes) bytes) of a
+// workspace with a fill kernel on `stream`.
+hipError_t counters_reset_launch(void* workspace, size_t bytes, hipStream_t stream);
 
 // Largest contraction length (elements) the few-token kernel handles:
 // 8 chunks of 16 bytes per lane, 512 lanes.

@@ -142,9 +142,14 @@ size_t tp_shard_mlp_workspace_size(int64_t I, int64_t D, int64_t F_local, tp_dty
                   proj_workspace(I, F_local, D, false, dt));
 }
 
-tp_status_t tp_shard_mlp(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt, const void* X,
-                         const void* W_gate, const void* W_up, const void* W_down, void* H,
-                         float* P, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// Every check of tp_shard_mlp except those on the workspace; TP_OK when the
+// call may go ahead (I == 0 included).
+tp_status_t mlp_args_status(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt, const void* X,
+                            const void* W_gate, const void* W_up, const void* W_down,
+                            const void* H, const float* P) {
   if (!dtype_ok(dt) || I < 0 || I > kMaxDim || !dims_ok(D) || !dims_ok(F_local))
     return TP_ERR_INVALID;
   if (I == 0) return TP_OK;
@@ -160,16 +165,30 @@ tp_status_t tp_shard_mlp(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt, c
   for (Range in : {rX, rG, rU, rD})
     if (overlap(rH, in) || overlap(rP, in)) return TP_ERR_INVALID;
   if (overlap(rH, rP)) return TP_ERR_INVALID;
+  if (dt == TP_F32 && (D > tpk::kGemvMaxK32 || F_local > tpk::kGemvMaxK32))
+    return TP_ERR_UNSUPPORTED;
+  return TP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+tp_status_t tp_shard_mlp(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt, const void* X,
+                         const void* W_gate, const void* W_up, const void* W_down, void* H,
+                         float* P, void* workspace, size_t workspace_bytes, void* stream) {
+  const tp_status_t st = mlp_args_status(I, D, F_local, dt, X, W_gate, W_up, W_down, H, P);
+  if (st != TP_OK || I == 0) return st;
   const size_t need = tp_shard_mlp_workspace_size(I, D, F_local, dt);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return TP_ERR_WORKSPACE;
     if (!aligned16(workspace)) return TP_ERR_MISALIGNED;
+    const int64_t es = esize(dt);
     const Range rW = rng(workspace, (int64_t)need);
-    for (Range o : {rX, rG, rU, rD, rH, rP})
+    for (Range o : {rng(X, I * D * es), rng(W_gate, F_local * D * es),
+                    rng(W_up, F_local * D * es), rng(W_down, D * F_local * es),
+                    rng(H, I * F_local * es), rng(P, I * D * 4)})
       if (overlap(rW, o)) return TP_ERR_INVALID;
   }
-  if (dt == TP_F32 && (D > tpk::kGemvMaxK32 || F_local > tpk::kGemvMaxK32))
-    return TP_ERR_UNSUPPORTED;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so the checks below are ours
@@ -483,6 +502,14 @@ tp_status_t tp_attn_core(int64_t I, int64_t S, int64_t n_q_local, int64_t n_kv_l
   return launched(tpk::attn_core_launch((int)I, (int)S, (int)n_q_local, (int)n_kv_local,
                                         (int)head_dim, static_cast<const uint16_t*>(qkv),
                                         static_cast<uint16_t*>(A), s));
+}
+
+tp_status_t tp_workspace_reset(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes == 0) return TP_ERR_INVALID;
+  if (!aligned16(workspace)) return TP_ERR_MISALIGNED;
+  (void)hipGetLastError();
+  return launched(
+      tpk::counters_reset_launch(workspace, workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
 size_t tp_stream_read_sink_words(void) { return tpk::stream_read_sink_words(); }

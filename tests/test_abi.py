@@ -258,3 +258,11 @@ def test_stream_read_validation(lib):
     assert lib.tp_stream_read(fake(0), 1000, fake(1), sink_words, None) == MISALIGNED
     assert lib.tp_stream_read(ctypes.c_void_p(FAKE + 8), 1024, fake(1), sink_words,
                               None) == MISALIGNED
+
+
+def test_workspace_reset_validation(lib):
+    """tp_workspace_reset rejects a null or empty workspace and a misaligned
+    pointer before launching anything."""
+    assert lib.tp_workspace_reset(None, 8192, None) == INVALID
+    assert lib.tp_workspace_reset(fake(0), 0, None) == INVALID
+    assert lib.tp_workspace_reset(ctypes.c_void_p(FAKE + 4), 8192, None) == MISALIGNED

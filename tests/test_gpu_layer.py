@@ -16,31 +16,39 @@ TOL = 2e-2
 D, F, NQ, NKV, HD, T_ = 8192, 28672, 64, 8, 128, 8
 
 
+def shard_set(Wq, Wk, Wv, Wo, Wg, Wu, Wd, t, r):
+    return dict(
+        qkv=to_dev(datagen.qkv_rank_shard(Wq, Wk, Wv, NQ, NKV, HD, t, r), "bf16"),
+        o=to_dev(datagen.oproj_rank_shard(Wo, NQ, HD, t, r), "bf16"),
+        mlp=tuple(to_dev(a, "bf16") for a in datagen.mlp_rank_shards(Wg, Wu, Wd, t, r)))
+
+
 @pytest.fixture(scope="module")
 def layer():
+    """The layer's weights on the host, its 8 TP rank shares on the GPU, and
+    the unsharded layer on the GPU (the TP=1 run)."""
     Wq, Wk, Wv, Wo = datagen.attn_weights(D, NQ, NKV, HD, "bf16", 11)
     Wg, Wu, Wd = datagen.mlp_weights(D, F, "bf16", 11)
-    ranks = []
-    for r in range(T_):
-        ranks.append(dict(
-            qkv=to_dev(datagen.qkv_rank_shard(Wq, Wk, Wv, NQ, NKV, HD, T_, r), "bf16"),
-            o=to_dev(datagen.oproj_rank_shard(Wo, NQ, HD, T_, r), "bf16"),
-            mlp=tuple(to_dev(a, "bf16") for a in datagen.mlp_rank_shards(Wg, Wu, Wd, T_, r))))
-    yield dict(attn=(Wq, Wk, Wv, Wo), mlp=(Wg, Wu, Wd), ranks=ranks)
-    del ranks
+    W = (Wq, Wk, Wv, Wo, Wg, Wu, Wd)
+    ranks = [shard_set(*W, T_, r) for r in range(T_)]
+    full = [shard_set(*W, 1, 0)]
+    yield dict(attn=(Wq, Wk, Wv, Wo), mlp=(Wg, Wu, Wd), ranks=ranks, full=full)
+    del ranks, full
     torch().cuda.empty_cache()
 
 
-def gpu_layer(L, X, S):
-    """Returns (QKV of rank 0, A of rank 0, o-partial of rank 0, attention
-    block output y1 in bf16, layer output y)."""
+def gpu_layer(L, X, S, t=T_):
+    """t rank shares of the layer in turn (t = 8: L["ranks"], t = 1:
+    L["full"]).  Returns (QKV of rank 0, A of rank 0, o-partial of rank 0,
+    attention block output y1 in bf16, layer output y).  Partial buffers are
+    pre-filled with NaN, so a row no kernel writes shows."""
     T = torch()
     I = X.shape[0]
-    nql, nkl = NQ // T_, NKV // T_
+    nql, nkl = NQ // t, NKV // t
     Xd = to_dev(X, "bf16")
-    po = T.empty((T_, I, D), dtype=T.float32, device="cuda")
+    po = T.full((t, I, D), float("nan"), dtype=T.float32, device="cuda")
     keep = {}
-    for r, R in enumerate(L["ranks"]):
+    for r, R in enumerate(L["ranks"] if t == T_ else L["full"]):
         qkv = empty((I, (nql + 2 * nkl) * HD), "bf16")
         tp.shard_attn_proj(tp.TP_ATTN_QKV, Xd, R["qkv"], qkv, nql, nkl, HD)
         A = empty((I, nql * HD), "bf16")
@@ -50,9 +58,9 @@ def gpu_layer(L, X, S):
             keep = dict(qkv=qkv, A=A)
     y1 = empty((I, D), "bf16")
     tp.partial_reduce(po, y1)
-    pm = T.empty((T_, I, D), dtype=T.float32, device="cuda")
-    for r, R in enumerate(L["ranks"]):
-        H = empty((I, F // T_), "bf16")
+    pm = T.full((t, I, D), float("nan"), dtype=T.float32, device="cuda")
+    for r, R in enumerate(L["ranks"] if t == T_ else L["full"]):
+        H = empty((I, F // t), "bf16")
         tp.shard_mlp(y1, *R["mlp"], H, pm[r])
     y = empty((I, D), "f32")
     tp.partial_reduce(pm, y)
@@ -61,39 +69,65 @@ def gpu_layer(L, X, S):
 
 
 def test_layer_decode32(orc, layer):
-    """Decode batch 32: 32 independent sequences of one token each."""
+    """Decode batch 32: 32 independent sequences of one token each.  Rank 0's
+    stages, the attention block output y1 (all rows) and the layer output y
+    (all rows) against the unsharded oracle; the 8-rank result against the
+    GPU's own TP=1 run of the same layer, every element."""
     I, S = 32, 1
     X = datagen.gaussian("X", (I, D), 1.0, "bf16", 32)
     qkv0, A0, po0, y1, y = gpu_layer(layer, X, S)
+    _, _, _, y1_t1, y_t1 = gpu_layer(layer, X, S, t=1)
     Wq, Wk, Wv, Wo = layer["attn"]
     # rank 0 stages
     q_ref, A_ref, po_ref = orc.attn_block_rank(X, Wq, Wk, Wv, Wo, NQ, NKV, HD, S, T_, 0)
     assert normwise_err(to_host(qkv0), q_ref) <= TOL
     assert normwise_err(to_host(A0), A_ref) <= TOL
     assert normwise_err(to_host(po0), po_ref) <= TOL
-    # unsharded attention block, then the unsharded MLP on sampled rows
+    # unsharded attention block, then the unsharded MLP
     _, _, y1_ref = orc.attn_block_rank(X, Wq, Wk, Wv, Wo, NQ, NKV, HD, S)
     assert normwise_err(to_host(y1), y1_ref) <= TOL
-    rows = [0, 13, 31]
-    _, y_ref = orc.mlp_full(y1_ref, *layer["mlp"], rows=rows)
-    assert normwise_err(to_host(y)[rows], y_ref) <= TOL
+    _, y_ref = orc.mlp_full(y1_ref, *layer["mlp"])
+    yh = to_host(y)
+    assert normwise_err(yh, y_ref) <= TOL
+    # sum of the 8 ranks' partials against the GPU's TP=1 layer
+    assert normwise_err(to_host(y1), to_host(y1_t1)) <= TOL
+    assert normwise_err(yh, to_host(y_t1)) <= TOL
 
 
-def test_layer_prefill512_rank0(orc, layer):
-    """Prefill of one causal sequence of 512 tokens: rank 0's QKV, attention and
-    o_proj partial against the oracle (sampled rows), and the layer output is
-    finite everywhere."""
+def test_layer_prefill512(orc, layer):
+    """Prefill of one causal sequence of 512 tokens.  Rank 0's QKV (all rows),
+    attention output and o_proj partial (a seeded 32-row sample) against the
+    oracle; the attention block output y1 against the unsharded oracle block
+    on every row; the layer output y against the unsharded oracle MLP (of the
+    oracle's y1) on a seeded 32-row sample holding rows 0 and 511; and the
+    8-rank result against the GPU's own TP=1 run, every element."""
     I, S = 512, 512
     X = datagen.gaussian("X", (I, D), 1.0, "bf16", 512)
     qkv0, A0, po0, y1, y = gpu_layer(layer, X, S)
+    _, _, _, y1_t1, y_t1 = gpu_layer(layer, X, S, t=1)
     Wq, Wk, Wv, Wo = layer["attn"]
     q_ref, A_ref, po_ref = orc.attn_block_rank(X, Wq, Wk, Wv, Wo, NQ, NKV, HD, S, T_, 0)
-    rows = [0, 1, 100, 311, 511]
+    rows = sample_rows(I)
     assert normwise_err(to_host(qkv0), q_ref) <= TOL
     assert normwise_err(to_host(A0)[rows], A_ref[rows]) <= TOL
     assert normwise_err(to_host(po0)[rows], po_ref[rows]) <= TOL
-    T = torch()
-    assert T.isfinite(y).all() and T.isfinite(y1.float()).all()
+    _, _, y1_ref = orc.attn_block_rank(X, Wq, Wk, Wv, Wo, NQ, NKV, HD, S)
+    y1h = to_host(y1)
+    assert normwise_err(y1h, y1_ref) <= TOL
+    _, y_ref = orc.mlp_full(y1_ref, *layer["mlp"], rows=rows)
+    yh = to_host(y)
+    assert normwise_err(yh[rows], y_ref) <= TOL
+    assert normwise_err(y1h, to_host(y1_t1)) <= TOL
+    assert normwise_err(yh, to_host(y_t1)) <= TOL
+
+
+def sample_rows(I, n=32, seed=0):
+    """Seeded sample of n token rows that always holds rows 0 and I - 1."""
+    if I <= n:
+        return list(range(I))
+    rng = np.random.default_rng(seed + I)
+    mid = rng.choice(np.arange(1, I - 1), size=n - 2, replace=False)
+    return sorted({0, I - 1, *map(int, mid)})
 
 
 def test_prenorm_block_decode32(orc, layer):

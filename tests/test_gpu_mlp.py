@@ -88,108 +88,126 @@ def test_tiny_f32_tp2_sum_of_partials(orc):
 
 @pytest.mark.parametrize("I", [1, 8, 64])
 def test_qwen_mlp_tp2(orc, I):
-    """Qwen2.5-1.5B-shaped MLP at TP=2 (D=1536, F=8960): both ranks, reduce."""
+    """Qwen2.5-1.5B-shaped MLP at TP=2 (D=1536, F=8960): both ranks (H and P
+    of each against the oracle), the reduce against the unsharded oracle, and
+    the GPU's sum of partials against its own TP=1 run, every element."""
     D, F, t = 1536, 8960, 2
     X = datagen.gaussian("X", (I, D), 1.0, "bf16", 100 + I)
     Wg, Wu, Wd = datagen.mlp_weights(D, F, "bf16", 100)
     T = torch()
-    parts = T.empty((t, I, D), dtype=T.float32, device="cuda")
+    parts = T.full((t, I, D), float("nan"), dtype=T.float32, device="cuda")
     for r in range(t):
         H, P = gpu_mlp(X, *datagen.mlp_rank_shards(Wg, Wu, Wd, t, r), "bf16")
         parts[r].copy_(P)
-        if r == 1:
-            Href, Pref = orc.mlp_rank(X, Wg, Wu, Wd, t, r)
-            assert normwise_err(to_host(H), Href) <= TOL["bf16"]
-            assert normwise_err(to_host(P), Pref) <= TOL["bf16"]
+        Href, Pref = orc.mlp_rank(X, Wg, Wu, Wd, t, r)
+        assert normwise_err(to_host(H), Href) <= TOL["bf16"], r
+        assert normwise_err(to_host(P), Pref) <= TOL["bf16"], r
     Y = empty((I, D), "f32")
     tp.partial_reduce(parts, Y)
+    _, Y1 = gpu_mlp(X, Wg, Wu, Wd, "bf16")
     T.cuda.synchronize()
     _, Yref = orc.mlp_full(X, Wg, Wu, Wd)
     assert normwise_err(to_host(Y), Yref) <= TOL["bf16"]
+    assert normwise_err(to_host(Y1), Yref) <= TOL["bf16"]
+    assert normwise_err(to_host(Y), to_host(Y1)) <= TOL["bf16"]
 
 
 # ---------------------------------------------------------------- Llama-70B
 @pytest.fixture(scope="module")
 def llama_mlp():
     """Full Llama-3.1-70B-shaped MLP weights (D=8192, F=28672), host fp32 and
-    fp64 copies, and the 8 TP rank shards resident on the GPU."""
+    fp64 copies, the 8 TP rank shards resident on the GPU, and the unsharded
+    weights on the GPU (the TP=1 run)."""
     D, F, t = 8192, 28672, 8
     Wg, Wu, Wd = datagen.mlp_weights(D, F, "bf16", 7)
     shards = [tuple(to_dev(a, "bf16") for a in datagen.mlp_rank_shards(Wg, Wu, Wd, t, r))
               for r in range(t)]
+    full = tuple(to_dev(a, "bf16") for a in (Wg, Wu, Wd))
     W64 = tuple(a.astype(np.float64) for a in (Wg, Wu, Wd))
-    yield dict(D=D, F=F, t=t, W=(Wg, Wu, Wd), W64=W64, shards=shards)
-    del shards
+    yield dict(D=D, F=F, t=t, W=(Wg, Wu, Wd), W64=W64, shards=shards, full=full)
+    del shards, full
     torch().cuda.empty_cache()
 
 
-def sample_rows(I):
-    return sorted({0, I // 2, I - 1})
+def sample_rows(I, n=32, seed=0):
+    """Seeded sample of n token rows that always holds rows 0 and I - 1."""
+    if I <= n:
+        return list(range(I))
+    rng = np.random.default_rng(seed + I)
+    mid = rng.choice(np.arange(1, I - 1), size=n - 2, replace=False)
+    return sorted({0, I - 1, *map(int, mid)})
+
+
+def sharded_mlp(L, Xd, I, keep_h=True):
+    """All t rank shares on the GPU (partials pre-filled with NaN, so a row
+    a kernel never writes shows), then the on-device reduce; plus the GPU's
+    own TP=1 run of the unsharded weights."""
+    T = torch()
+    D, F, t = L["D"], L["F"], L["t"]
+    parts = T.full((t, I, D), float("nan"), dtype=T.float32, device="cuda")
+    Hs = []
+    for r in range(t):
+        H = empty((I, F // t), "bf16")
+        tp.shard_mlp(Xd, *L["shards"][r], H, parts[r])
+        Hs.append(H if keep_h else None)
+    Y = empty((I, D), "f32")
+    tp.partial_reduce(parts, Y)
+    H1 = empty((I, F), "bf16")
+    Y1 = empty((I, D), "f32")
+    tp.shard_mlp(Xd, *L["full"], H1, Y1)
+    T.cuda.synchronize()
+    del H1
+    return Hs, parts, Y, Y1
 
 
 @pytest.mark.parametrize("I", [1, 6, 16, 32, 64, 256])
 def test_llama_mlp_decode_tp8(orc, llama_mlp, I):
-    """Llama-3.1-70B-shaped MLP, all 8 TP=8 rank shares on one GPU, decode I tokens;
-    sampled token rows against the oracle (every row depends only on its own
-    input row)."""
+    """Llama-3.1-70B-shaped MLP, all 8 TP=8 rank shares on one GPU, decode I
+    tokens.  Every row of every rank's H and P and of the reduced Y against
+    the oracle; Y against the unsharded oracle layer on a seeded row sample
+    (lecture §4.3: the sharded output equals the single-device output); the
+    GPU's sum of partials against the GPU's own TP=1 run, every element."""
     L = llama_mlp
-    D, F_local, t = L["D"], L["F"] // L["t"], L["t"]
-    X = datagen.gaussian("X", (I, D), 1.0, "bf16", 200 + I)
-    Xd = to_dev(X, "bf16")
-    T = torch()
-    parts = T.empty((t, I, D), dtype=T.float32, device="cuda")
-    Hs = []
+    t = L["t"]
+    X = datagen.gaussian("X", (I, L["D"]), 1.0, "bf16", 200 + I)
+    Hs, parts, Y, Y1 = sharded_mlp(L, to_dev(X, "bf16"), I)
+    Prefs = []
     for r in range(t):
-        H = empty((I, F_local), "bf16")
-        tp.shard_mlp(Xd, *L["shards"][r], H, parts[r])
-        Hs.append(H)
-    Y = empty((I, D), "f32")
-    tp.partial_reduce(parts, Y)
-    T.cuda.synchronize()
+        Href, Pref = orc.mlp_rank(X, *L["W64"], t, r)
+        assert normwise_err(to_host(Hs[r]), Href) <= TOL["bf16"], r
+        assert normwise_err(to_host(parts[r]), Pref) <= TOL["bf16"], r
+        Prefs.append(Pref)
+    Yref = orc.reduce(np.stack(Prefs))
+    Yh = to_host(Y)
+    assert normwise_err(Yh, Yref) <= TOL["bf16"]
     rows = sample_rows(I)
-    _, Yref = orc.mlp_full(X, *L["W64"], rows=rows)
-    assert normwise_err(to_host(Y)[rows], Yref) <= TOL["bf16"]
-    for r in (0, t - 1):
-        Href, Pref = orc.mlp_rank(X, *L["W64"], t, r, rows=rows)
-        assert normwise_err(to_host(Hs[r])[rows], Href) <= TOL["bf16"]
-        assert normwise_err(to_host(parts[r])[rows], Pref) <= TOL["bf16"]
-    # no canary survives anywhere in the outputs
-    assert not T.isnan(Y).any() and all(not T.isnan(h).any() for h in Hs)
+    _, Yfull = orc.mlp_full(X, *L["W64"], rows=rows)
+    assert normwise_err(Yh[rows], Yfull) <= TOL["bf16"]
+    assert normwise_err(Yh, to_host(Y1)) <= TOL["bf16"]
 
 
 def test_llama_mlp_prefill(orc, llama_mlp):
-    """512-token prefill: TP=8 rank shares (sampled rows vs oracle; their sum
-    vs the GPU's own TP=1 run, all elements) and the TP=1 unsharded MLP."""
+    """512-token prefill.  TP=8: every row of every rank's H and P and of the
+    reduced Y against the oracle.  TP=1 (the unsharded 8192 x 28672 MLP): a
+    seeded 32-row sample holding rows 0 and 511 against the unsharded oracle.
+    The GPU's sum of partials against its TP=1 run, every element."""
     L = llama_mlp
-    D, F, t, I = L["D"], L["F"], L["t"], 512
-    X = datagen.gaussian("X", (I, D), 1.0, "bf16", 512)
-    Xd = to_dev(X, "bf16")
-    T = torch()
-    parts = T.empty((t, I, D), dtype=T.float32, device="cuda")
-    H0 = None
+    t, I = L["t"], 512
+    X = datagen.gaussian("X", (I, L["D"]), 1.0, "bf16", 512)
+    Hs, parts, Y, Y1 = sharded_mlp(L, to_dev(X, "bf16"), I)
+    Prefs = []
     for r in range(t):
-        H = empty((I, F // t), "bf16")
-        tp.shard_mlp(Xd, *L["shards"][r], H, parts[r])
-        if r == 0:
-            H0 = H
-    Y = empty((I, D), "f32")
-    tp.partial_reduce(parts, Y)
-    rows = [0, 1, 255, 256, 511]
-    Href, Pref = orc.mlp_rank(X, *L["W64"], t, 0, rows=rows)
-    T.cuda.synchronize()
-    assert normwise_err(to_host(H0)[rows], Href) <= TOL["bf16"]
-    assert normwise_err(to_host(parts[0])[rows], Pref) <= TOL["bf16"]
-    # TP=1: the whole 8192 x 28672 MLP as one rank
-    full = tuple(to_dev(a, "bf16") for a in L["W"])
-    H1 = empty((I, F), "bf16")
-    Y1 = empty((I, D), "f32")
-    tp.shard_mlp(Xd, *full, H1, Y1)
-    T.cuda.synchronize()
-    _, Yref = orc.mlp_full(X, *L["W64"], rows=rows)
-    assert normwise_err(to_host(Y1)[rows], Yref) <= TOL["bf16"]
-    assert normwise_err(to_host(Y)[rows], Yref) <= TOL["bf16"]
-    assert normwise_err(to_host(Y), to_host(Y1)) <= TOL["bf16"]
-    del full, H1
+        Href, Pref = orc.mlp_rank(X, *L["W64"], t, r)
+        assert normwise_err(to_host(Hs[r]), Href) <= TOL["bf16"], r
+        assert normwise_err(to_host(parts[r]), Pref) <= TOL["bf16"], r
+        Prefs.append(Pref)
+    Yh, Y1h = to_host(Y), to_host(Y1)
+    assert normwise_err(Yh, orc.reduce(np.stack(Prefs))) <= TOL["bf16"]
+    rows = sample_rows(I)
+    _, Yfull = orc.mlp_full(X, *L["W64"], rows=rows)
+    assert normwise_err(Y1h[rows], Yfull) <= TOL["bf16"]
+    assert normwise_err(Yh[rows], Yfull) <= TOL["bf16"]
+    assert normwise_err(Yh, Y1h) <= TOL["bf16"]
 
 
 def test_mlp_deterministic(llama_mlp):
@@ -238,18 +256,23 @@ COUNTER_BYTES = 8192  # leading arrival-counter area of a split-K workspace
 
 def test_explicit_workspace_scratch_contents_do_not_matter(llama_mlp):
     """Split-K calls (9..64 tokens on the streaming kernel, 65..256 on the
-    tiled one) keep arrival counters and fp32 partials in the workspace: a
-    caller buffer whose counter area is zero and whose partial area is NaN
-    gives the same bits as the binding's own, twice in a row, and leaves the
-    counter area zero."""
+    tiled one) keep arrival counters and fp32 partials in the workspace.  A
+    caller buffer filled with arbitrary bits -- counter area included -- and
+    then prepared with tp_workspace_reset gives the same bits as the
+    binding's own workspace, twice in a row, and is left with a zero counter
+    area."""
     L = llama_mlp
     T = torch()
+    gen = T.Generator(device="cuda")
+    gen.manual_seed(1234)
     for I in (9, 32, 64, 128, 256):
         X = to_dev(datagen.gaussian("X", (I, L["D"]), 1.0, "bf16", 77), "bf16")
         need = tp.mlp_workspace_bytes(I, L["D"], L["F"] // L["t"])
         assert need > COUNTER_BYTES, I
-        ws = T.full((need // 4 + 4,), float("nan"), dtype=T.float32, device="cuda")
-        ws[:COUNTER_BYTES // 4].view(T.int32).zero_()
+        ws = T.randint(-2**31, 2**31 - 1, (need // 4 + 4,), dtype=T.int32, device="cuda",
+                       generator=gen)
+        assert int((ws[:COUNTER_BYTES // 4] != 0).sum()) > 0
+        tp.workspace_reset(ws)
         outs = []
         for w in (None, ws, ws):
             H = empty((I, L["F"] // L["t"]), "bf16")
@@ -259,6 +282,36 @@ def test_explicit_workspace_scratch_contents_do_not_matter(llama_mlp):
         T.cuda.synchronize()
         for o in outs[1:]:
             assert T.equal(outs[0][0], o[0]) and T.equal(outs[0][1], o[1]), I
-        assert int(ws[:COUNTER_BYTES // 4].view(T.int32).abs().sum()) == 0, I
+        assert int(ws[:COUNTER_BYTES // 4].abs().sum()) == 0, I
         with pytest.raises(tp.TPError, match="WORKSPACE"):
             tp.shard_mlp(X, *L["shards"][5], outs[0][0], outs[0][1], workspace=ws[:8])
+
+
+def test_binding_workspace_per_stream(llama_mlp):
+    """The binding keeps one workspace per (device, stream): calls on two
+    streams, each waiting only for its own inputs, give the bits of the
+    same calls on the default stream."""
+    L = llama_mlp
+    T = torch()
+    I = 32
+    X = to_dev(datagen.gaussian("X", (I, L["D"]), 1.0, "bf16", 78), "bf16")
+    ref = []
+    for r in (2, 6):
+        H = empty((I, L["F"] // L["t"]), "bf16")
+        P = empty((I, L["D"]), "f32")
+        tp.shard_mlp(X, *L["shards"][r], H, P)
+        ref.append((H, P))
+    T.cuda.synchronize()
+    streams = [T.cuda.Stream(), T.cuda.Stream()]
+    got = []
+    for s, r in zip(streams, (2, 6)):
+        H = empty((I, L["F"] // L["t"]), "bf16")
+        P = empty((I, L["D"]), "f32")
+        s.wait_stream(T.cuda.current_stream())
+        with T.cuda.stream(s):
+            for _ in range(3):
+                tp.shard_mlp(X, *L["shards"][r], H, P)
+        got.append((H, P))
+    T.cuda.synchronize()
+    for (h0, p0), (h1, p1) in zip(ref, got):
+        assert T.equal(h0, h1) and T.equal(p0, p1)
