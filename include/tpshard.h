@@ -142,6 +142,28 @@ tp_status_t tp_shard_mlp_fp8(int64_t I, int64_t D, int64_t F_local, const void* 
                              void* H, float* P, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * tp_shard_mlp for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and kernels, with the split-K scratch taken from an array
+ * the library holds in device memory instead of a caller workspace.  The
+ * array, tp_shard_mlp_noalloc_max_workspace() bytes (32 MiB), is part of the
+ * library's code object, so each GPU the library runs on holds its own copy
+ * until the process ends; the call allocates nothing.  Every call clears the
+ * array's counter area (a small fill kernel on `stream`) before its kernels.
+ * All calls on one GPU share that GPU's array: calls that may overlap on one
+ * GPU (other streams, other threads) race and give wrong results -- keep
+ * them on one stream, or use tp_shard_mlp with a workspace each.
+ * Arguments and results as tp_shard_mlp, without the workspace.
+ * Errors as tp_shard_mlp; TP_ERR_WORKSPACE when the call needs more scratch
+ * than the array holds (tp_shard_mlp_workspace_size(...) above the maximum),
+ * TP_ERR_LAUNCH also when the array's device address cannot be looked up.
+ */
+size_t tp_shard_mlp_noalloc_max_workspace(void);
+tp_status_t tp_shard_mlp_noalloc(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt,
+                                 const void* X, const void* W_gate, const void* W_up,
+                                 const void* W_down, void* H, float* P, void* stream);
+
 /* Workspace bytes tp_shard_attn_proj needs (0 if none); host-only. */
 size_t tp_shard_attn_proj_workspace_size(tp_attn_phase_t phase, int64_t I, int64_t D,
                                          int64_t n_q_local, int64_t n_kv_local,

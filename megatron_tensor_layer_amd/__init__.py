@@ -49,6 +49,8 @@ SIGNATURES = {
     "tp_residual_rmsnorm": (ctypes.c_int, [_i32, _i64, _i64, _vp, _vp, ctypes.c_int, _vp, _vp,
                                            ctypes.c_int, _vp, ctypes.c_float, _vp]),
     "tp_workspace_reset": (ctypes.c_int, [_vp, _sz, _vp]),
+    "tp_shard_mlp_noalloc_max_workspace": (_sz, []),
+    "tp_shard_mlp_noalloc": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int] + [_vp] * 7),
     "tp_stream_read_sink_words": (_sz, []),
     "tp_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _sz, _vp]),
 }
@@ -195,6 +197,27 @@ def shard_mlp(X, W_gate, W_up, W_down, H, P, workspace=None, stream=None) -> Non
     _check("tp_shard_mlp", lib().tp_shard_mlp(I, D, F_local, dt, _ptr(X), _ptr(W_gate),
                                               _ptr(W_up), _ptr(W_down), _ptr(H), _ptr(P),
                                               ws_ptr, ws_bytes, _stream(stream, dev)))
+
+
+def shard_mlp_noalloc(X, W_gate, W_up, W_down, H, P, stream=None) -> None:
+    """shard_mlp without a workspace: the library's own static scratch array
+    (calls that overlap on one GPU race on it; see tp_shard_mlp_noalloc)."""
+    torch = _torch()
+    dev = _dev(X, W_gate, W_up, W_down, H, P)
+    I, D = X.shape
+    F_local = W_gate.shape[0]
+    dt = _dt(X)
+    for t in (W_gate, W_up, W_down, H):
+        if _dt(t) != dt:
+            raise TypeError("X, weights and H must share one dtype")
+    if P.dtype != torch.float32:
+        raise TypeError("P must be float32")
+    if (W_gate.shape != (F_local, D) or W_up.shape != (F_local, D)
+            or W_down.shape != (D, F_local) or H.shape != (I, F_local) or P.shape != (I, D)):
+        raise ValueError("shape mismatch")
+    _check("tp_shard_mlp_noalloc",
+           lib().tp_shard_mlp_noalloc(I, D, F_local, dt, _ptr(X), _ptr(W_gate), _ptr(W_up),
+                                      _ptr(W_down), _ptr(H), _ptr(P), _stream(stream, dev)))
 
 
 def shard_attn_proj(phase: int, inp, W, out, n_q_local: int, n_kv_local: int, head_dim: int,

@@ -20,6 +20,13 @@ constexpr int kWsMaxCounters = int(kWsCounterBytes / 4);
 // workspace with a fill kernel on `stream`.
 hipError_t counters_reset_launch(void* workspace, size_t bytes, hipStream_t stream);
 
+// Size of the library's static scratch array (one per device, held until
+// the process ends), and its device address on the current device, looked
+// up once per device.  Used only by the entry point for callers that cannot
+// allocate.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+hipError_t static_scratch(void** ptr);
+
 // Largest contraction length (elements) the few-token kernel handles:
 // 8 chunks of 16 bytes per lane, 512 lanes.
 constexpr int64_t kGemvMaxK16 = 8 * 512 * 8;   // bf16

@@ -198,6 +198,27 @@ tp_status_t tp_shard_mlp(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt, c
   return launched(e);
 }
 
+size_t tp_shard_mlp_noalloc_max_workspace(void) { return tpk::kStaticScratchBytes; }
+
+tp_status_t tp_shard_mlp_noalloc(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt,
+                                 const void* X, const void* W_gate, const void* W_up,
+                                 const void* W_down, void* H, float* P, void* stream) {
+  const tp_status_t st = mlp_args_status(I, D, F_local, dt, X, W_gate, W_up, W_down, H, P);
+  if (st != TP_OK || I == 0) return st;
+  const size_t need = tp_shard_mlp_workspace_size(I, D, F_local, dt);
+  if (need > tpk::kStaticScratchBytes) return TP_ERR_WORKSPACE;
+  if (need == 0) return tp_shard_mlp(I, D, F_local, dt, X, W_gate, W_up, W_down, H, P, nullptr,
+                                     0, stream);
+  void* scratch = nullptr;
+  (void)hipGetLastError();
+  if (tpk::static_scratch(&scratch) != hipSuccess) return TP_ERR_LAUNCH;
+  // the array keeps the last call's contents: clear the counters first
+  if (tpk::counters_reset_launch(scratch, need, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return TP_ERR_LAUNCH;
+  return tp_shard_mlp(I, D, F_local, dt, X, W_gate, W_up, W_down, H, P, scratch,
+                      tpk::kStaticScratchBytes, stream);
+}
+
 size_t tp_shard_attn_proj_workspace_size(tp_attn_phase_t phase, int64_t I, int64_t D,
                                          int64_t n_q_local, int64_t n_kv_local,
                                          int64_t head_dim, tp_dtype_t dt) {
