@@ -21,6 +21,12 @@ The printed JSON line also carries
                 HIP events on its stream inside the timed region (one event
                 pair per step around the 8 ranks' back-to-back calls, divided
                 by 8), against the 8 TB/s HBM peak;
+  roofline_prefill: the prefill side of the metric, one rank's tp_shard_mlp
+                at 512 tokens (TP=8 shapes), event-timed on its stream in
+                groups of 8 back-to-back calls (one per rank share), against
+                the dense bf16 MFMA peak;
+  clocks:       SCLK and MCLK sampled with amd-smi while those prefill calls
+                run back to back;
   read_ceiling: the achievable read rate, tp_stream_read over 2 GiB with the
                 decode kernels' access pattern; roofline and config also give
                 their fraction of it;
@@ -71,6 +77,12 @@ def parse():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for rocprofv3 --pmc: one calibration copy of COPY_MIB MiB, then one "
                          "tp_shard_mlp call per rank at the bench batch; no timing")
+    ap.add_argument("--prefill-profile", action="store_true",
+                    help="for rocprofv3: each 512-token prefill projection of a TP=8 rank "
+                         "(MLP, QKV, o_proj) and the TP=1 MLP in phases of its own, no timing")
+    ap.add_argument("--ingest-prefill-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn the FETCH_SIZE and WRITE_SIZE passes over --prefill-profile "
+                         "into the 512-token MLP entry of profiles/traffic.json")
     ap.add_argument("--ingest-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the counter_collection.csv files of the FETCH_SIZE and "
                          "WRITE_SIZE passes over --traffic-probe into profiles/traffic.json")
@@ -134,6 +146,123 @@ def log(msg):
     print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
+PREFILL_I = 512
+
+
+def prefill_mlp_fns(torch, tp, layer, I=PREFILL_I):
+    """One TP=8 rank's 512-token MLP call per rank share (rotating the 8
+    shares keeps the 176 MB per call coming from HBM)."""
+    X = to_dev(torch, datagen.gaussian("X", (I, D), 1.0, "bf16", 3000 + I))
+    H = torch.empty((I, F // TP), dtype=torch.bfloat16, device="cuda")
+    P = torch.empty((I, D), dtype=torch.float32, device="cuda")
+    return [(lambda R=R: tp.shard_mlp(X, *R["mlp"], H, P)) for R in layer.ranks]
+
+
+def prefill_roofline(torch, tp, layer, calls):
+    """The prefill side of the metric: one TP=8 rank's tp_shard_mlp at 512
+    tokens (gate/up + SwiGLU GEMM, then the down GEMM), timed with HIP events
+    on its launch stream, one event pair per group of 8 back-to-back calls
+    (one per rank share), against the dense bf16 MFMA peak."""
+    fns = prefill_mlp_fns(torch, tp, layer)
+    us = time_calls(torch, fns, calls)
+    avg = statistics.mean(us)
+    m = wl.MlpShape(PREFILL_I, D, F // TP)
+    tf = m.flops() / (avg * 1e-6) / 1e12
+    return dict(bound="mfma", achieved=round(tf, 1), peak=PEAK_BF16, unit="TFLOP/s",
+                frac=round(tf / PEAK_BF16, 4), traffic=None,
+                kernel=f"tp_shard_mlp I={PREFILL_I} D={D} F_local={F // TP} "
+                       "(gemm_kernel SwiGLU epilogue for gate/up, then gemm_kernel fp32 "
+                       "epilogue for down, 128 x 128 tiles)",
+                avg_call_us=round(avg, 2), median_call_us=stats(us)["median_us"],
+                algorithmic_flops_per_call=m.flops())
+
+
+def sample_clocks(torch, fns, samples=3):
+    """SCLK (per XCD) and MCLK while the GPU runs `fns` back to back: each
+    sample is one `amd-smi metric -c --json` child process, queried while
+    the calls keep the GPU busy.  None when amd-smi is unavailable."""
+    import shutil
+    import subprocess
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(exe):
+        return None
+    sclk, mclk = [], []
+    t0 = time.perf_counter()  # bring the clocks up from idle before the first sample
+    while time.perf_counter() - t0 < 0.5:
+        for _ in range(8):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+    for _ in range(samples):
+        proc = subprocess.Popen([exe, "metric", "-c", "--json"], stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True)
+        t0 = time.perf_counter()
+        inflight = []
+        while proc.poll() is None and time.perf_counter() - t0 < 20.0:
+            # keep two bursts queued so the GPU never idles while polling
+            for _ in range(8):
+                for f in fns:
+                    f()
+            ev = torch.cuda.Event()
+            ev.record()
+            inflight.append(ev)
+            if len(inflight) > 2:
+                inflight.pop(0).synchronize()
+        torch.cuda.synchronize()
+        try:
+            out, _ = proc.communicate(timeout=10)
+            clk = json.loads(out)["gpu_data"][0]["clock"]
+        except Exception:  # noqa: BLE001 - a missing field only loses the sample
+            continue
+        g = [v["clk"]["value"] for k, v in clk.items()
+             if k.startswith("gfx_") and isinstance(v.get("clk"), dict)]
+        if g:
+            sclk.append(g)
+        m = clk.get("mem_0", {}).get("clk")
+        if isinstance(m, dict):
+            mclk.append(m["value"])
+    if not sclk:
+        return None
+    return dict(sclk_mhz_per_xcd=sclk, mclk_mhz=mclk, sclk_spec_mhz=2400,
+                how="amd-smi metric -c --json (each sample: the 8 XCDs' current GFX "
+                    "clocks) while the 512-token TP=8 MLP calls run back to back")
+
+
+def prefill_profile(torch, tp, layer, reps=20):
+    """For rocprofv3 --kernel-trace: every 512-token prefill projection of a
+    TP=8 rank in a phase of its own (reps calls each, rotating the rank
+    shares), then the TP=1 MLP, so each kernel's dispatches can be told
+    apart by grid and order."""
+    T = torch
+    I = PREFILL_I
+    fns = prefill_mlp_fns(T, tp, layer)
+    log("profile phase 1: TP=8 MLP 512 (gate/up + SwiGLU, down)")
+    for k in range(reps):
+        fns[k % TP]()
+    T.cuda.synchronize()
+    X = to_dev(T, datagen.gaussian("X", (I, D), 1.0, "bf16", 3600))
+    nql, nkl = NQ // TP, NKV // TP
+    qkv = T.empty((I, (nql + 2 * nkl) * HD), dtype=T.bfloat16, device="cuda")
+    log("profile phase 2: TP=8 QKV 512")
+    for k in range(reps):
+        tp.shard_attn_proj(tp.TP_ATTN_QKV, X, layer.ranks[k % TP]["qkv"], qkv, nql, nkl, HD)
+    T.cuda.synchronize()
+    A = to_dev(T, datagen.gaussian("A", (I, nql * HD), 1.0, "bf16", 3601))
+    Po = T.empty((I, D), dtype=T.float32, device="cuda")
+    log("profile phase 3: TP=8 o_proj 512")
+    for k in range(reps):
+        tp.shard_attn_proj(tp.TP_ATTN_O, A, layer.ranks[k % TP]["o"], Po, nql, nkl, HD)
+    T.cuda.synchronize()
+    log("profile phase 4: TP=1 MLP 512")
+    full = tuple(to_dev(T, a) for a in layer.host["mlp"])
+    H1 = T.empty((I, F), dtype=T.bfloat16, device="cuda")
+    Y1 = T.empty((I, D), dtype=T.float32, device="cuda")
+    for _ in range(max(2, reps // 4)):
+        tp.shard_mlp(X, *full, H1, Y1)
+    T.cuda.synchronize()
+    log("profile phases done")
+
+
 def stats(us):
     us = sorted(us)
     q = lambda p: us[min(len(us) - 1, int(p * len(us)))]
@@ -145,6 +274,10 @@ def stats(us):
 # split-K gate/up kernel, the whole-K row-stream down kernel and their headers.
 MLP_DECODE_SOURCES = tuple(f"megatron_tensor_layer_amd/csrc/{f}" for f in (
     "tpshard_api.cpp", "kernels.h", "common.h", "splitk.hip", "rowstream.hip"))
+
+
+MLP_PREFILL_SOURCES = tuple(f"megatron_tensor_layer_amd/csrc/{f}" for f in (
+    "tpshard_api.cpp", "kernels.h", "common.h", "gemm.hip"))
 
 
 def src_hash(files=MLP_DECODE_SOURCES):
@@ -176,6 +309,43 @@ def traffic_probe(torch, tp, layer, I):
     log(f"traffic probe: copy of {COPY_MIB} MiB, then {len(layer.ranks)} tp_shard_mlp calls at I={I}")
 
 
+def ingest_prefill_traffic(fetch_csv, write_csv):
+    """FETCH_SIZE / WRITE_SIZE of one TP=8 rank's 512-token tp_shard_mlp call
+    from the --prefill-profile counter runs: the first phase's gate/up and
+    down GEMM dispatches, scaled by the copy calibration stored with the
+    decode figures (the same counters on the same chip)."""
+    import csv
+    tf = ROOT / "profiles" / "traffic.json"
+    tr = json.loads(tf.read_text())
+    cal = tr[next(k for k in tr if k.startswith("mlp_I"))]["copy_calibration"]
+
+    def read(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter
+                and "tpk::" in r["Kernel_Name"] and "zero_words_kernel" not in r["Kernel_Name"]]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        phase = []
+        for r in rows:  # phase 1 ends at the first QKV GEMM (bf16 epilogue)
+            if "gemm_kernel<1>" in r["Kernel_Name"]:
+                break
+            phase.append(float(r["Counter_Value"]))
+        if len(phase) % 2:
+            raise SystemExit(f"{path}: odd number of MLP GEMM dispatches in phase 1")
+        return phase
+
+    fetch = read(fetch_csv, "FETCH_SIZE")
+    write = read(write_csv, "WRITE_SIZE")
+    calls = len(fetch) // 2
+    fb = sum(fetch) * 1024 * cal["fetch_factor"] / calls
+    wb = sum(write) * 1024 * cal["write_factor"] / calls
+    tr["mlp_prefill_I512"] = dict(
+        bytes_per_call=round(fb + wb), fetch_bytes_per_call=round(fb),
+        write_bytes_per_call=round(wb), calls=calls, src_hash=src_hash(MLP_PREFILL_SOURCES),
+        command="rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -- "
+                "python3 bench.py --prefill-profile")
+    tf.write_text(json.dumps(tr, indent=1) + "\n")
+    log(f"mlp_prefill_I512: {fb / 1e6:.1f} MB fetched + {wb / 1e6:.1f} MB written per call")
+
+
 def ingest_traffic(fetch_csv, write_csv, I):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one tp_shard_mlp call,
     each scaled by what the counter reads for the calibration copy."""
@@ -187,8 +357,9 @@ def ingest_traffic(fetch_csv, write_csv, I):
         copy = [r for r in rows if "MulFunctor" in r["Kernel_Name"]]
         if len(copy) != 1:
             raise SystemExit(f"{path}: expected one calibration copy dispatch, found {len(copy)}")
+        # the MLP call's kernels; the binding's one-off workspace reset is not part of a call
         after = [r for r in rows if int(r["Dispatch_Id"]) > int(copy[0]["Dispatch_Id"])
-                 and "tpk::" in r["Kernel_Name"]]
+                 and "tpk::" in r["Kernel_Name"] and "zero_words_kernel" not in r["Kernel_Name"]]
         per_kernel = {}
         for r in after:
             per_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
@@ -198,7 +369,7 @@ def ingest_traffic(fetch_csv, write_csv, I):
     cf, kf = read(fetch_csv, "FETCH_SIZE")
     cw, kw = read(write_csv, "WRITE_SIZE")
     f_fetch, f_write = true_bytes / (cf * 1024), true_bytes / (cw * 1024)
-    calls = len(next(iter(kf.values())))
+    calls = max(len(v) for v in kf.values())
     fetch = sum(sum(v) for v in kf.values()) * 1024 * f_fetch / calls
     write = sum(sum(v) for v in kw.values()) * 1024 * f_write / calls
     key = f"mlp_I{I}"
@@ -393,6 +564,18 @@ def detail(torch, tp, layer, calls):
     out["llama70b_mlp_tp8_prefill_I512"] = dict(**st, TFLOPs=round(tf, 1),
                                                 frac_mfma=round(tf / PEAK_BF16, 3),
                                                 tokens_per_s=round(I / (st["median_us"] * 1e-6)))
+    # the attention projections of the rank shares at prefill 512
+    A = to_dev(T, datagen.gaussian("A", (I, nql * HD), 1.0, "bf16", 1512))
+    Q = T.empty((I, (nql + 2 * nkl) * HD), dtype=T.bfloat16, device="cuda")
+    for name, fns, shape in (
+            ("qkv", [(lambda R=R: tp.shard_attn_proj(tp.TP_ATTN_QKV, X, R["qkv"], Q, nql, nkl, HD))
+                     for R in layer.ranks], wl.QkvShape(I, D, nql, nkl, HD)),
+            ("o_proj", [(lambda R=R: tp.shard_attn_proj(tp.TP_ATTN_O, A, R["o"], P, nql, nkl, HD))
+                        for R in layer.ranks], wl.OprojShape(I, D, nql, HD))):
+        st = stats(time_calls(T, fns, calls // 2))
+        tf = shape.flops() / (st["median_us"] * 1e-6) / 1e12
+        out[f"llama70b_{name}_tp8_prefill_I512"] = dict(**st, TFLOPs=round(tf, 1),
+                                                        frac_mfma=round(tf / PEAK_BF16, 3))
     full = tuple(to_dev(T, a) for a in layer.host["mlp"])
     H1 = T.empty((I, F), dtype=T.bfloat16, device="cuda")
     st = stats(time_calls(T, [lambda: tp.shard_mlp(X, *full, H1, P)], max(10, calls // 10), 3))
@@ -586,6 +769,9 @@ def main():
     if args.ingest_traffic:
         ingest_traffic(*args.ingest_traffic, I)
         return
+    if args.ingest_prefill_traffic:
+        ingest_prefill_traffic(*args.ingest_prefill_traffic)
+        return
 
     import torch
     import megatron_tensor_layer_amd as tp
@@ -596,6 +782,9 @@ def main():
     log("8 rank shares of the layer resident in HBM")
     if args.traffic_probe:
         traffic_probe(torch, tp, layer, I)
+        return
+    if args.prefill_profile:
+        prefill_profile(torch, tp, layer)
         return
     Xh = datagen.gaussian("X", (I, D), 1.0, "bf16", 42)
     X = to_dev(torch, Xh)
@@ -629,12 +818,20 @@ def main():
     ceiling = read_ceiling(torch, tp)
     log(f"read ceiling: {ceiling['GBps']} GB/s over 2 GiB")
     roof["frac_of_read_ceiling"] = round(achieved / ceiling["GBps"], 4)
+    roof_pf = prefill_roofline(torch, tp, layer, max(args.calls, 8))
+    log(f"prefill roofline: TP=8 MLP 512 {roof_pf['avg_call_us']} us, "
+        f"{roof_pf['achieved']} TFLOP/s")
+    clocks = sample_clocks(torch, prefill_mlp_fns(torch, tp, layer))
+    log(f"clocks under load: {clocks}")
     tf = ROOT / "profiles" / "traffic.json"
     if tf.exists():
         tr = json.loads(tf.read_text())
         key = f"mlp_I{I}"
         if key in tr and tr[key].get("src_hash") == src_hash():
             roof["traffic"] = tr[key]["bytes_per_call"]
+        pk = "mlp_prefill_I512"
+        if pk in tr and tr[pk].get("src_hash") == src_hash(MLP_PREFILL_SOURCES):
+            roof_pf["traffic"] = tr[pk]["bytes_per_call"]
 
     line = dict(
         metric="TP-rank MLP shard: decode HBM GB/s, prefill MFMA TFLOP/s, % roofline",
@@ -649,7 +846,7 @@ def main():
                     tokens_per_s_excl_comm=round(I / (ms * 1e-3), 1),
                     frac_hbm=round(value / PEAK_HBM, 4),
                     frac_read_ceiling=round(value / ceiling["GBps"], 4)),
-        roofline=roof, read_ceiling=ceiling)
+        roofline=roof, roofline_prefill=roof_pf, clocks=clocks, read_ceiling=ceiling)
 
     if not args.no_detail:
         line["detail"] = detail(torch, tp, layer, args.calls)

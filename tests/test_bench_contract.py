@@ -48,3 +48,13 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, env=env, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_prefill_roofline_flops():
+    """The prefill side of the line: one TP=8 rank's 512-token MLP call,
+    2 * 512 * 8192 * 3584 FLOPs per matrix, three matrices; per matrix this is
+    the lecture's per-device 2 B D F / n at B = 512, D = 8192, F = 28672, n = 8."""
+    b = _bench()
+    m = b.wl.MlpShape(b.PREFILL_I, 8192, 3584)
+    assert m.flops() == 90_194_313_216
+    assert m.flops() // 3 == 2 * 512 * 8192 * 28672 // 8
