@@ -3,16 +3,17 @@
 // This is the value the all-reduce after a row-parallel block delivers
 // (lecture "Distributed Serving", §3.3 and §4.3); on one device it is an
 // HBM-bound streaming sum of t*n fp32 values.  Each thread owns 4
-// consecutive elements.  It issues the 16-byte loads of up to kBatch ranks
-// of its column together, then adds them in rank order, batch after batch, so
-// the result is bitwise deterministic and a batch costs one memory round
-// trip instead of one per rank.
+// consecutive elements and adds its t values in rank order, so the result is
+// bitwise deterministic.  A thread waits for each load before the next add;
+// the bytes in flight come from the many resident waves instead (a few
+// thousand workgroups at prefill sizes, about 32 KB per CU).  Issuing 4 or 8
+// of a thread's rank loads before adding them was slower on MI355X: 29 and
+// 31 us against 26 us for 8 partials of [512, 8192] (too many bytes in flight
+// per CU), and no faster at [32, 8192], where the launch dominates.
 #include "common.h"
 #include "kernels.h"
 
 namespace tpk {
-
-constexpr int kBatch = 8;  // rank loads in flight per thread
 
 template <int OUT_BF16>
 __global__ void __launch_bounds__(256)
@@ -20,17 +21,10 @@ reduce_kernel(int t, int64_t n4, int64_t n, const f32x4_t* __restrict__ P, void*
   const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (v >= n4) return;
   const int64_t stride = n / 4;  // float4 per rank
-  f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int r0 = 0; r0 < t; r0 += kBatch) {
-    f32x4_t p[kBatch];
-#pragma unroll
-    for (int e = 0; e < kBatch; ++e)
-      p[e] = r0 + e < t ? __builtin_nontemporal_load(P + (int64_t)(r0 + e) * stride + v)
-                        : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // rank order, starting from rank 0's value itself
-#pragma unroll
-    for (int e = 0; e < kBatch; ++e)
-      if (r0 + e < t) s = (r0 + e == 0) ? p[e] : s + p[e];
+  f32x4_t s = __builtin_nontemporal_load(P + v);
+  for (int r = 1; r < t; ++r) {
+    const f32x4_t p = __builtin_nontemporal_load(P + (int64_t)r * stride + v);
+    s += p;
   }
   if constexpr (OUT_BF16) {
     u32x2_t o;

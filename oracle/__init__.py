@@ -52,6 +52,12 @@ class Oracle:
         lib.orc_shard_range.argtypes = [_i64, _i64, _i64, _pi64, _pi64]
         lib.orc_mlp_rank.restype = None
         lib.orc_mlp_rank.argtypes = [_i64] * 5 + [_pd] * 6 + [_pi64, _i64]
+        lib.orc_bf16_round.restype = ctypes.c_double
+        lib.orc_bf16_round.argtypes = [ctypes.c_double]
+        lib.orc_bf16_round_array.restype = None
+        lib.orc_bf16_round_array.argtypes = [_i64, _pd, _pd]
+        lib.orc_mlp_rank_bf16h.restype = None
+        lib.orc_mlp_rank_bf16h.argtypes = [_i64] * 5 + [_pd] * 8 + [_pi64, _i64]
         lib.orc_reduce.restype = None
         lib.orc_reduce.argtypes = [_i64, _i64, _pd, _pd]
         lib.orc_qkv_rank.restype = None
@@ -106,6 +112,36 @@ class Oracle:
         self.lib.orc_mlp_rank(I, D, F, t, r, self._p(X), self._p(Wg), self._p(Wu),
                               self._p(Wd), self._p(H), self._p(P), rp, n_out)
         return H, P
+
+    def mlp_rank_bf16h(self, X, Wg, Wu, Wd, t: int = 1, r: int = 0, rows=None):
+        """(H, P, Hb, Pb): mlp_rank's H and P, plus H rounded to bf16 as the
+        device stores it and the partial computed from that rounded H."""
+        X, Wg, Wu, Wd = (self._f64(a) for a in (X, Wg, Wu, Wd))
+        I, D = X.shape
+        F = Wg.shape[0]
+        assert Wg.shape == (F, D) and Wu.shape == (F, D) and Wd.shape == (D, F)
+        assert F % t == 0 and 0 <= r < t
+        if rows is None:
+            n_out, rp = I, None
+        else:
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+            assert rows.min() >= 0 and rows.max() < I
+            n_out, rp = len(rows), rows.ctypes.data_as(_pi64)
+        H, Hb = np.empty((n_out, F // t)), np.empty((n_out, F // t))
+        P, Pb = np.empty((n_out, D)), np.empty((n_out, D))
+        self.lib.orc_mlp_rank_bf16h(I, D, F, t, r, self._p(X), self._p(Wg), self._p(Wu),
+                                    self._p(Wd), self._p(H), self._p(P), self._p(Hb),
+                                    self._p(Pb), rp, n_out)
+        return H, P, Hb, Pb
+
+    def bf16_round(self, a):
+        """Nearest bfloat16 value of each element (ties to even), as float64."""
+        if np.isscalar(a):
+            return self.lib.orc_bf16_round(float(a))
+        a = self._f64(a)
+        out = np.empty_like(a)
+        self.lib.orc_bf16_round_array(a.size, self._p(a), self._p(out))
+        return out
 
     def mlp_full(self, X, Wg, Wu, Wd, rows=None):
         return self.mlp_rank(X, Wg, Wu, Wd, 1, 0, rows)

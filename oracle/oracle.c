@@ -91,6 +91,72 @@ void orc_mlp_rank(int64_t I, int64_t D, int64_t F, int64_t t, int64_t r,
 }
 
 /*
+ * Nearest bfloat16 value of x, ties to even (the storage rounding of every
+ * bf16 intermediate on the device: H, the QKV output, the attention output,
+ * a bf16 reduce output).  bfloat16 keeps 8 significant bits (1 implicit +
+ * 7 stored) and the float32 exponent range, so near x, with x = m 2^e and
+ * 1/2 <= |m| < 1, the representable values are the multiples of 2^(e-8);
+ * below the smallest normal (2^-126) the spacing stays at 2^-133.  nearbyint
+ * in the default rounding mode rounds half to even.  Zero, infinities and NaN
+ * pass through.  Results past the largest bf16 (about 3.39e38) are not
+ * clamped to infinity: no value of this layer comes near it.
+ */
+double orc_bf16_round(double x) {
+  if (x == 0.0 || isnan(x) || isinf(x)) return x;
+  int e;
+  frexp(x, &e);
+  int q = e - 8;
+  if (q < -133) q = -133;
+  return ldexp(nearbyint(ldexp(x, -q)), q);
+}
+
+void orc_bf16_round_array(int64_t n, const double *in, double *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < n; ++j) out[j] = orc_bf16_round(in[j]);
+}
+
+/*
+ * orc_mlp_rank with the device's storage of H made explicit (the diagnostic
+ * reading of the oracle): the same H and P as orc_mlp_rank, and also
+ *   Hb[i, f] = bf16(H[i, f])                       (H as the bf16 path stores it)
+ *   Pb[i, n] = sum over f in F_r of Hb[i, f] W_down[f, n]
+ * so that a bf16 device result can be compared with what its arithmetic
+ * would give with exact fp64 sums: Pb differs from a correct device P by
+ * fp32 accumulation error only.  The plain P is accumulated exactly as in
+ * orc_mlp_rank.  Arguments as orc_mlp_rank; Hb and Pb have the shapes of H
+ * and P.
+ */
+void orc_mlp_rank_bf16h(int64_t I, int64_t D, int64_t F, int64_t t, int64_t r,
+                        const double *X, const double *Wg, const double *Wu,
+                        const double *Wd, double *H, double *P, double *Hb, double *Pb,
+                        const int64_t *rows, int64_t nrows) {
+  int64_t f0, f1;
+  orc_shard_range(F, t, r, &f0, &f1);
+  const int64_t Fl = f1 - f0;
+  const int64_t n_out = rows ? nrows : I;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t q = 0; q < n_out; ++q)
+    for (int64_t f = f0; f < f1; ++f) {
+      const int64_t i = rows ? rows[q] : q;
+      const double g = dot(X + i * D, Wg + f * D, D);
+      const double u = dot(X + i * D, Wu + f * D, D);
+      H[q * Fl + (f - f0)] = orc_silu(g) * u;
+      Hb[q * Fl + (f - f0)] = orc_bf16_round(H[q * Fl + (f - f0)]);
+    }
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t q = 0; q < n_out; ++q)
+    for (int64_t n = 0; n < D; ++n) {
+      double s = 0.0, sb = 0.0;
+      for (int64_t f = f0; f < f1; ++f) {
+        s += H[q * Fl + (f - f0)] * Wd[n * F + f];
+        sb += Hb[q * Fl + (f - f0)] * Wd[n * F + f];
+      }
+      P[q * D + n] = s;
+      Pb[q * D + n] = sb;
+    }
+}
+
+/*
  * Sum of the t rank partials in rank order 0..t-1: what the all-reduce after
  * a row-parallel block delivers (lecture §3.3: all-reduce sums the partials;
  * §4.3: the sharded result equals the single-device one up to the order of

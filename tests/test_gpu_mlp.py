@@ -8,7 +8,7 @@ import pytest
 
 import megatron_tensor_layer_amd as tp
 from megatron_tensor_layer_amd import datagen
-from tests.common import normwise_err
+from tests.common import BF16_STEP, DIAG_BF16_FLIPS, DIAG_TOL, bf16_flips, normwise_err
 from tests.gpu_util import empty, to_dev, to_host, torch
 
 pytestmark = pytest.mark.gpu
@@ -171,15 +171,24 @@ def test_llama_mlp_decode_tp8(orc, llama_mlp, I):
     t = L["t"]
     X = datagen.gaussian("X", (I, L["D"]), 1.0, "bf16", 200 + I)
     Hs, parts, Y, Y1 = sharded_mlp(L, to_dev(X, "bf16"), I)
-    Prefs = []
+    Prefs, Pbs = [], []
     for r in range(t):
-        Href, Pref = orc.mlp_rank(X, *L["W64"], t, r)
-        assert normwise_err(to_host(Hs[r]), Href) <= TOL["bf16"], r
-        assert normwise_err(to_host(parts[r]), Pref) <= TOL["bf16"], r
+        Href, Pref, Hb, Pb = orc.mlp_rank_bf16h(X, *L["W64"], t, r)
+        Hg, Pg = to_host(Hs[r]), to_host(parts[r])
+        assert normwise_err(Hg, Href) <= TOL["bf16"], r
+        assert normwise_err(Pg, Pref) <= TOL["bf16"], r
+        # diagnostic: against the oracle with H rounded to bf16 as stored
+        print(f"diagnostic I={I} rank {r}: H flips {bf16_flips(Hg, Hb):.2e}, "
+              f"H {normwise_err(Hg, Hb):.2e}, P {normwise_err(Pg, Pb):.2e}")
+        assert bf16_flips(Hg, Hb) <= DIAG_BF16_FLIPS, r
+        assert normwise_err(Hg, Hb) <= BF16_STEP, r
+        assert normwise_err(Pg, Pb) <= DIAG_TOL, r
         Prefs.append(Pref)
+        Pbs.append(Pb)
     Yref = orc.reduce(np.stack(Prefs))
     Yh = to_host(Y)
     assert normwise_err(Yh, Yref) <= TOL["bf16"]
+    assert normwise_err(Yh, orc.reduce(np.stack(Pbs))) <= DIAG_TOL
     rows = sample_rows(I)
     _, Yfull = orc.mlp_full(X, *L["W64"], rows=rows)
     assert normwise_err(Yh[rows], Yfull) <= TOL["bf16"]
@@ -195,17 +204,26 @@ def test_llama_mlp_prefill(orc, llama_mlp):
     t, I = L["t"], 512
     X = datagen.gaussian("X", (I, L["D"]), 1.0, "bf16", 512)
     Hs, parts, Y, Y1 = sharded_mlp(L, to_dev(X, "bf16"), I)
-    Prefs = []
+    Prefs, Pbs = [], []
     for r in range(t):
-        Href, Pref = orc.mlp_rank(X, *L["W64"], t, r)
-        assert normwise_err(to_host(Hs[r]), Href) <= TOL["bf16"], r
-        assert normwise_err(to_host(parts[r]), Pref) <= TOL["bf16"], r
+        Href, Pref, Hb, Pb = orc.mlp_rank_bf16h(X, *L["W64"], t, r)
+        Hg, Pg = to_host(Hs[r]), to_host(parts[r])
+        assert normwise_err(Hg, Href) <= TOL["bf16"], r
+        assert normwise_err(Pg, Pref) <= TOL["bf16"], r
+        print(f"diagnostic prefill rank {r}: H flips {bf16_flips(Hg, Hb):.2e}, "
+              f"H {normwise_err(Hg, Hb):.2e}, P {normwise_err(Pg, Pb):.2e}")
+        assert bf16_flips(Hg, Hb) <= DIAG_BF16_FLIPS, r
+        assert normwise_err(Hg, Hb) <= BF16_STEP, r
+        assert normwise_err(Pg, Pb) <= DIAG_TOL, r
         Prefs.append(Pref)
+        Pbs.append(Pb)
     Yh, Y1h = to_host(Y), to_host(Y1)
     assert normwise_err(Yh, orc.reduce(np.stack(Prefs))) <= TOL["bf16"]
+    assert normwise_err(Yh, orc.reduce(np.stack(Pbs))) <= DIAG_TOL
     rows = sample_rows(I)
-    _, Yfull = orc.mlp_full(X, *L["W64"], rows=rows)
+    _, Yfull, _, Yfull_b = orc.mlp_rank_bf16h(X, *L["W64"], rows=rows)
     assert normwise_err(Y1h[rows], Yfull) <= TOL["bf16"]
+    assert normwise_err(Y1h[rows], Yfull_b) <= DIAG_TOL
     assert normwise_err(Yh[rows], Yfull) <= TOL["bf16"]
     assert normwise_err(Yh, Y1h) <= TOL["bf16"]
 

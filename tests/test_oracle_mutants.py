@@ -38,6 +38,10 @@ MUTANTS = {
     "decode_gqa_map": ("const int64_t g = (j * nkv) / nq, L = lens[b];", "const int64_t g = j % nkv, L = lens[b];"),
     "decode_cache_batch": (": Kc + ((b * nkv + g) * Lmax + p) * hd;", ": Kc + (g * Lmax + p) * hd;"),
     "decode_v_new_token": ("const double *v = (p == L - 1) ? qkv + b * N + (nq + nkv + g) * hd", "const double *v = (p == L - 1) ? qkv + b * N + (nq + g) * hd"),
+    "bf16_round_toward_zero": ("ldexp(nearbyint(ldexp(x, -q)), q)", "ldexp(trunc(ldexp(x, -q)), q)"),
+    "bf16_round_extra_bit": ("int q = e - 8;", "int q = e - 9;"),
+    "bf16_round_no_subnormal_floor": ("if (q < -133) q = -133;", "if (q < -140) q = -140;"),
+    "bf16h_down_from_unrounded": ("sb += Hb[q * Fl + (f - f0)] * Wd[n * F + f];", "sb += H[q * Fl + (f - f0)] * Wd[n * F + f];"),
     "fp8_row_scale": ("scales[n] * orc_e4m3(codes[n * K + k])", "scales[k % N] * orc_e4m3(codes[n * K + k])"),
 }
 

@@ -426,6 +426,68 @@ def pin_attn_decode(orc):
     assert np.allclose(A[0], ref, rtol=1e-12, atol=1e-13)
 
 
+def _bf16_round_ref(x: float) -> float:
+    """Nearest bfloat16 value by enumeration, written out independently of the
+    oracle: bfloat16 values are the float32 values whose low 16 bits are
+    zero; take the candidates around x, keep the nearest in exact rationals,
+    ties to the candidate whose last kept bit (bit 16) is 0."""
+    import struct
+    if x == 0.0 or math.isnan(x) or math.isinf(x):
+        return x
+    sign = -1.0 if x < 0 else 1.0
+    ax = abs(x)
+    b32 = struct.unpack("<I", struct.pack("<f", ax))[0] & 0xFFFF0000
+    cands = []
+    for d in (-2, -1, 0, 1, 2):
+        bits = b32 + d * 0x10000
+        if 0 <= bits < 0x7F800000:
+            cands.append((struct.unpack("<f", struct.pack("<I", bits))[0], bits))
+    xf = Fraction(ax)
+    best = min(cands, key=lambda c: (abs(Fraction(c[0]) - xf), (c[1] >> 16) & 1))
+    return sign * best[0]
+
+
+def pin_bf16_round(orc):
+    """The rounding of bf16 intermediates: the enumeration above on values
+    across the range (normal, below the smallest normal, exact ties), and
+    hand-worked cases."""
+    rng = np.random.default_rng(5)
+    xs = list(rng.standard_normal(400) * np.exp(rng.uniform(-30, 30, 400)))
+    xs += [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 3.0 * 2.0 ** -134,
+           2.0 ** -126 * (1 + 2.0 ** -8), 1e-40, 65504.0, 1.0 / 3.0]
+    for x in xs:
+        assert orc.bf16_round(float(x)) == _bf16_round_ref(float(x)), x
+    assert orc.bf16_round(1.0 + 2.0 ** -8) == 1.0                  # tie to even (down)
+    assert orc.bf16_round(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6   # tie to even (up)
+    assert orc.bf16_round(1.0 + 2.0 ** -8 + 2.0 ** -30) == 1.0 + 2.0 ** -7
+    assert orc.bf16_round(-2.0) == -2.0 and orc.bf16_round(0.0) == 0.0
+    a = np.array(xs[:50])
+    assert np.array_equal(orc.bf16_round(a), [orc.bf16_round(float(v)) for v in a])
+
+
+def pin_mlp_bf16h(orc):
+    """The diagnostic form of the MLP share: H and P equal mlp_rank's bit for
+    bit, Hb is H rounded to bf16 (enumeration reference), and Pb is the
+    down projection of Hb in exact rationals."""
+    for (I, D, F, t, r, pool) in ((3, 16, 32, 2, 1, 4), (2, 8, 16, 1, 0, 5), (1, 16, 64, 4, 3, 6)):
+        X, Wg, Wu, Wd = tiny_mlp(I, D, F, pool=pool)
+        H0, P0 = orc.mlp_rank(X, Wg, Wu, Wd, t, r)
+        H, P, Hb, Pb = orc.mlp_rank_bf16h(X, Wg, Wu, Wd, t, r)
+        assert np.array_equal(H, H0) and np.array_equal(P, P0)
+        for i in range(I):
+            for f in range(F // t):
+                assert Hb[i, f] == _bf16_round_ref(float(H[i, f]))
+        Fl = F // t
+        for i in range(I):
+            for n in range(D):
+                exact = sum(Fraction(float(Hb[i, fl])) * Fraction(float(Wd[n, r * Fl + fl]))
+                            for fl in range(Fl))
+                assert abs(Pb[i, n] - float(exact)) <= 1e-14 * max(1.0, abs(float(exact)))
+        rows = [I - 1, 0]
+        _, _, Hs, Ps = orc.mlp_rank_bf16h(X, Wg, Wu, Wd, t, r, rows=rows)
+        assert np.array_equal(Hs, Hb[rows]) and np.array_equal(Ps, Pb[rows])
+
+
 ALL_PINS = [
     pin_silu_closed_forms,
     pin_mlp_bruteforce_exact,
@@ -445,6 +507,8 @@ ALL_PINS = [
     pin_fp8_dequant_rows,
     pin_sequence_shards_concatenate,
     pin_attn_decode,
+    pin_bf16_round,
+    pin_mlp_bf16h,
 ]
 
 
