@@ -37,7 +37,8 @@ The printed JSON line also carries
                 the layer at prefill 512, the partial reduce, the residual
                 update + RMSNorm after a block, the layer as a pre-norm block
                 with those at decode 32, the MLP with weight-only FP8
-                storage at decode 1, 8 and 32, and decode attention over a
+                storage at decode 1, 8 and 32, the same with int8 storage,
+                and decode attention over a
                 rank's KV cache); calls rotating over weight sets are timed
                 in groups of back-to-back calls, one per set, with one event
                 pair per group, queued behind a spin kernel.
@@ -536,6 +537,23 @@ def detail(torch, tp, layer, calls):
             **st, bytes_per_call=nbytes, GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM, 3),
             tokens_per_s=round(I / (st["median_us"] * 1e-6)))
     del fp8_ranks
+    # and with weight-only int8 storage (signed codes + one fp32 scale per row)
+    i8_ranks = [tuple((T.randint(-128, 128, shp, generator=gen, device="cuda",
+                                 dtype=T.int32).to(T.int8), scales(shp[0]))
+                      for shp in ((Fl, D), (Fl, D), (D, Fl))) for _ in range(TP)]
+    for I in (1, 8, 32):
+        X = to_dev(T, datagen.gaussian("X", (I, D), 1.0, "bf16", 1200 + I))
+        H = T.empty((I, Fl), dtype=T.bfloat16, device="cuda")
+        P = T.empty((I, D), dtype=T.float32, device="cuda")
+        fns = [(lambda w=w: tp.shard_mlp_int8(X, *w, H, P)) for w in i8_ranks]
+        st = stats(time_calls(T, fns, calls))
+        nbytes = 3 * D * Fl + 4 * (2 * Fl + D) + 2 * I * D + 4 * I * D
+        gbs = nbytes / (st["median_us"] * 1e-6) / 1e9
+        log(f"int8 MLP TP=8 decode I={I}: {st['median_us']} us")
+        out[f"llama70b_mlp_int8_tp8_decode_I{I}"] = dict(
+            **st, bytes_per_call=nbytes, GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM, 3),
+            tokens_per_s=round(I / (st["median_us"] * 1e-6)))
+    del i8_ranks
     # the attention projections of the layer's rank shares at decode 32
     I = 32
     nql, nkl = NQ // TP, NKV // TP

@@ -205,6 +205,23 @@ tp_status_t tp_partial_reduce(int32_t t, int64_t n, const float* partials,
                               tp_dtype_t out_dt, void* Y, void* stream);
 
 /*
+ * tp_shard_mlp_fp8 with int8 codes: weight-only int8 storage for decode, the
+ * variant behind the pages' PaLM int8-weight figures ([L4] §5.5).  Every
+ * weight is one signed byte c in [-128, 127] and every output row n of a
+ * matrix carries one fp32 scale, W[n, k] = s[n] * c[n, k].  Activations, H
+ * and P keep the dtypes of the bf16 path; the int8 values are exact in bf16,
+ * so the products are those of the dequantized weights.  Arguments, shapes,
+ * alignment, workspace, supported sizes (1..64 tokens) and errors as
+ * tp_shard_mlp_fp8, with W_gate, W_up, W_down holding int8 codes.
+ */
+size_t tp_shard_mlp_int8_workspace_size(int64_t I, int64_t D, int64_t F_local);
+tp_status_t tp_shard_mlp_int8(int64_t I, int64_t D, int64_t F_local, const void* X,
+                              const void* W_gate, const float* s_gate, const void* W_up,
+                              const float* s_up, const void* W_down, const float* s_down,
+                              void* H, float* P, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * The step after a row-parallel block's all-reduce, fused into one pass over
  * each hidden row: the residual update and the replicated RMSNorm in front of
  * the next column-parallel projection ([L4] §4.2: the RMSNorm scale is

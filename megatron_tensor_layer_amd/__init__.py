@@ -46,6 +46,8 @@ SIGNATURES = {
     "tp_attn_decode": (ctypes.c_int, [_i64] * 5 + [_vp] * 6 + [_sz, _vp]),
     "tp_shard_mlp_fp8_workspace_size": (_sz, [_i64] * 3),
     "tp_shard_mlp_fp8": (ctypes.c_int, [_i64, _i64, _i64] + [_vp] * 10 + [_sz, _vp]),
+    "tp_shard_mlp_int8_workspace_size": (_sz, [_i64] * 3),
+    "tp_shard_mlp_int8": (ctypes.c_int, [_i64, _i64, _i64] + [_vp] * 10 + [_sz, _vp]),
     "tp_residual_rmsnorm": (ctypes.c_int, [_i32, _i64, _i64, _vp, _vp, ctypes.c_int, _vp, _vp,
                                            ctypes.c_int, _vp, ctypes.c_float, _vp]),
     "tp_workspace_reset": (ctypes.c_int, [_vp, _sz, _vp]),
@@ -286,13 +288,9 @@ def stream_read(buf, sink=None, stream=None):
     return sink
 
 
-def shard_mlp_fp8(X, gate, up, down, H, P, workspace=None, stream=None) -> None:
-    """Weight-only FP8 MLP rank share for decode (1..64 tokens): gate, up, down
-    are (codes uint8, scales float32) pairs -- gate/up codes [F_local, D] with
-    scales [F_local], down codes [D, F_local] with scales [D]; X and H bf16,
-    P float32.  Past 8 tokens the call needs a workspace (the binding keeps
-    one per device unless one is passed)."""
+def _shard_mlp_bytew(kind, X, gate, up, down, H, P, workspace, stream) -> None:
     torch = _torch()
+    code_dtype = torch.uint8 if kind == "fp8" else torch.int8
     (Wg, sg), (Wu, su), (Wd, sd) = gate, up, down
     dev = _dev(X, Wg, sg, Wu, su, Wd, sd, H, P)
     I, D = X.shape
@@ -300,20 +298,37 @@ def shard_mlp_fp8(X, gate, up, down, H, P, workspace=None, stream=None) -> None:
     if X.dtype != torch.bfloat16 or H.dtype != torch.bfloat16 or P.dtype != torch.float32:
         raise TypeError("X and H bfloat16, P float32")
     for W, s_, shape in ((Wg, sg, (F_local, D)), (Wu, su, (F_local, D)), (Wd, sd, (D, F_local))):
-        if W.dtype != torch.uint8 or tuple(W.shape) != shape:
-            raise ValueError(f"FP8 codes must be uint8 {shape}")
+        if W.dtype != code_dtype or tuple(W.shape) != shape:
+            raise ValueError(f"{kind} codes must be {code_dtype} {shape}")
         if s_.dtype != torch.float32 or s_.numel() != shape[0]:
             raise ValueError("scales must be float32, one per output row")
     if tuple(H.shape) != (I, F_local) or tuple(P.shape) != (I, D):
         raise ValueError("H [I, F_local], P [I, D]")
+    L = lib()
+    size_fn = getattr(L, f"tp_shard_mlp_{kind}_workspace_size")
     if workspace is not None:
         ws_ptr, ws_bytes = _user_workspace(workspace)
     else:
-        ws_ptr, ws_bytes = _workspace(dev, lib().tp_shard_mlp_fp8_workspace_size(I, D, F_local),
-                                      stream)
-    _check("tp_shard_mlp_fp8", lib().tp_shard_mlp_fp8(
+        ws_ptr, ws_bytes = _workspace(dev, size_fn(I, D, F_local), stream)
+    name = f"tp_shard_mlp_{kind}"
+    _check(name, getattr(L, name)(
         I, D, F_local, _ptr(X), _ptr(Wg), _ptr(sg), _ptr(Wu), _ptr(su), _ptr(Wd), _ptr(sd),
         _ptr(H), _ptr(P), ws_ptr, ws_bytes, _stream(stream, dev)))
+
+
+def shard_mlp_fp8(X, gate, up, down, H, P, workspace=None, stream=None) -> None:
+    """Weight-only FP8 MLP rank share for decode (1..64 tokens): gate, up, down
+    are (codes uint8, scales float32) pairs -- gate/up codes [F_local, D] with
+    scales [F_local], down codes [D, F_local] with scales [D]; X and H bf16,
+    P float32.  Past 4 tokens the call needs a workspace (the binding keeps
+    one per device and stream unless one is passed)."""
+    _shard_mlp_bytew("fp8", X, gate, up, down, H, P, workspace, stream)
+
+
+def shard_mlp_int8(X, gate, up, down, H, P, workspace=None, stream=None) -> None:
+    """Weight-only int8 MLP rank share for decode (1..64 tokens): as
+    shard_mlp_fp8 with int8 codes, W[n, k] = scale[n] * code[n, k]."""
+    _shard_mlp_bytew("int8", X, gate, up, down, H, P, workspace, stream)
 
 
 def residual_rmsnorm(partials, residual, h, gamma=None, x=None, eps: float = 1e-5,

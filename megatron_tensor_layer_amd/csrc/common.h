@@ -135,6 +135,30 @@ __device__ __forceinline__ void decode16(const u32x4_t& w, u32x4_t& lo, u32x4_t&
   hi = u32x4_t{p[4], p[5], p[6], p[7]};
 }
 
+// One-byte weight codes of the weight-only variants: OCP E4M3, or signed int8.
+constexpr int kFmtE4M3 = 0;
+constexpr int kFmtInt8 = 1;
+
+// 16 signed int8 codes -> two 8-element bf16 chunks (K 0..7, K 8..15), exact:
+// every integer in [-128, 127] is a bf16 value.
+__device__ __forceinline__ void decode16_i8(const u32x4_t& w, u32x4_t& lo, u32x4_t& hi) {
+  uint32_t p[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int v = (int)w[q];
+    p[2 * q] = pack_bf16x2((float)(int8_t)(v & 0xff), (float)(int8_t)((v >> 8) & 0xff));
+    p[2 * q + 1] = pack_bf16x2((float)(int8_t)((v >> 16) & 0xff), (float)(int8_t)(v >> 24));
+  }
+  lo = u32x4_t{p[0], p[1], p[2], p[3]};
+  hi = u32x4_t{p[4], p[5], p[6], p[7]};
+}
+
+// Weight storage of a streaming kernel's template instance: bf16, or one-byte
+// codes (E4M3, int8) with one fp32 scale per row.
+constexpr int kWBf16 = 0;
+constexpr int kWE4M3 = 1;
+constexpr int kWInt8 = 2;
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -1,5 +1,6 @@
-// Decode projections for few tokens (I <= 8) with weight-only FP8 storage:
-// y[i, n] = s[n] * sum_k x[i, k] e4m3(code[n, k]), activations bf16.
+// Decode projections for few tokens (I <= 8) with weight-only one-byte
+// storage: y[i, n] = s[n] * sum_k x[i, k] w(code[n, k]), activations bf16,
+// w = e4m3 (FP8) or the signed int8 value, by the launch's format.
 //
 // Decode streams the rank's weights once per step (lecture "Distributed
 // Serving", §1.1 and §3.4); one byte per weight halves that stream.  The
@@ -26,7 +27,7 @@ __device__ __forceinline__ float dot8(const u32x4_t& w, const u32x4_t& x, float 
 
 // X [I, K] bf16 (row stride ldx); W0/W1 [N, K] fp8 codes, S0/S1 [N] fp32 row
 // scales (W1/S1: up matrix, SwiGLU only); out [I, N] (row stride ldo).
-template <int NI, int J, int R, int EPI>
+template <int NI, int J, int R, int EPI, int FMT>
 __global__ void __launch_bounds__(512)
 gemv_fp8_kernel(int I, int K, int N, const uint16_t* __restrict__ X, int64_t ldx,
                 const uint8_t* __restrict__ W0, const float* __restrict__ S0,
@@ -83,7 +84,10 @@ gemv_fp8_kernel(int I, int K, int N, const uint16_t* __restrict__ X, int64_t ldx
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         u32x4_t lo, hi;
-        decode16(wr[r][j], lo, hi);
+        if constexpr (FMT == kFmtInt8)
+          decode16_i8(wr[r][j], lo, hi);
+        else
+          decode16(wr[r][j], lo, hi);
 #pragma unroll
         for (int i = 0; i < NI; ++i)
           acc[r * NI + i] = dot8(hi, xr[j][i][1], dot8(lo, xr[j][i][0], acc[r * NI + i]));
@@ -126,26 +130,30 @@ constexpr int fp8_rows_per_block() {
 template <int NI, int J, int EPI>
 hipError_t launch_fp8(int I, int K, int N, const uint16_t* X, int64_t ldx, const uint8_t* W0,
                       const float* S0, const uint8_t* W1, const float* S1, void* out, int64_t ldo,
-                      int nthreads, hipStream_t stream) {
+                      int nthreads, int fmt, hipStream_t stream) {
   constexpr int R = fp8_rows_per_block<NI, J, EPI>();
   constexpr int RP = (EPI == EPI_SWIGLU) ? R / 2 : R;
   const int nblk = (N + RP - 1) / RP;
-  hipLaunchKernelGGL((gemv_fp8_kernel<NI, J, R, EPI>), dim3(nblk), dim3(nthreads), 0, stream, I,
-                     K, N, X, ldx, W0, S0, W1, S1, out, ldo);
+  if (fmt == kFmtInt8)
+    hipLaunchKernelGGL((gemv_fp8_kernel<NI, J, R, EPI, kFmtInt8>), dim3(nblk), dim3(nthreads), 0,
+                       stream, I, K, N, X, ldx, W0, S0, W1, S1, out, ldo);
+  else
+    hipLaunchKernelGGL((gemv_fp8_kernel<NI, J, R, EPI, kFmtE4M3>), dim3(nblk), dim3(nthreads), 0,
+                       stream, I, K, N, X, ldx, W0, S0, W1, S1, out, ldo);
   return hipGetLastError();
 }
 
 template <int NI, int EPI>
 hipError_t launch_fp8_j(int I, int K, int N, const uint16_t* X, int64_t ldx, const uint8_t* W0,
                         const float* S0, const uint8_t* W1, const float* S1, void* out,
-                        int64_t ldo, hipStream_t stream) {
+                        int64_t ldo, int fmt, hipStream_t stream) {
   const int chunks = K / 16;
   int J = 1;
   while (chunks > J * 512) J *= 2;
   const int nthreads = std::min(512, ((chunks + J - 1) / J + 63) / 64 * 64);
   switch (J) {  // K <= kFp8MaxK = 16 * 512 * 2
-    case 1: return launch_fp8<NI, 1, EPI>(I, K, N, X, ldx, W0, S0, W1, S1, out, ldo, nthreads, stream);
-    case 2: return launch_fp8<NI, 2, EPI>(I, K, N, X, ldx, W0, S0, W1, S1, out, ldo, nthreads, stream);
+    case 1: return launch_fp8<NI, 1, EPI>(I, K, N, X, ldx, W0, S0, W1, S1, out, ldo, nthreads, fmt, stream);
+    case 2: return launch_fp8<NI, 2, EPI>(I, K, N, X, ldx, W0, S0, W1, S1, out, ldo, nthreads, fmt, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -155,18 +163,18 @@ hipError_t launch_fp8_j(int I, int K, int N, const uint16_t* X, int64_t ldx, con
 template <int EPI>
 hipError_t gemv_fp8_launch(int I, int K, int N, const uint16_t* X, const uint8_t* W0,
                            const float* S0, const uint8_t* W1, const float* S1, void* out,
-                           int64_t ldo, hipStream_t stream) {
-  if (I <= 1) return launch_fp8_j<1, EPI>(I, K, N, X, K, W0, S0, W1, S1, out, ldo, stream);
-  if (I <= 2) return launch_fp8_j<2, EPI>(I, K, N, X, K, W0, S0, W1, S1, out, ldo, stream);
-  if (I <= 4) return launch_fp8_j<4, EPI>(I, K, N, X, K, W0, S0, W1, S1, out, ldo, stream);
-  return launch_fp8_j<8, EPI>(I, K, N, X, K, W0, S0, W1, S1, out, ldo, stream);
+                           int64_t ldo, int fmt, hipStream_t stream) {
+  if (I <= 1) return launch_fp8_j<1, EPI>(I, K, N, X, K, W0, S0, W1, S1, out, ldo, fmt, stream);
+  if (I <= 2) return launch_fp8_j<2, EPI>(I, K, N, X, K, W0, S0, W1, S1, out, ldo, fmt, stream);
+  if (I <= 4) return launch_fp8_j<4, EPI>(I, K, N, X, K, W0, S0, W1, S1, out, ldo, fmt, stream);
+  return launch_fp8_j<8, EPI>(I, K, N, X, K, W0, S0, W1, S1, out, ldo, fmt, stream);
 }
 
 template hipError_t gemv_fp8_launch<EPI_F32>(int, int, int, const uint16_t*, const uint8_t*,
                                              const float*, const uint8_t*, const float*, void*,
-                                             int64_t, hipStream_t);
+                                             int64_t, int, hipStream_t);
 template hipError_t gemv_fp8_launch<EPI_SWIGLU>(int, int, int, const uint16_t*, const uint8_t*,
                                                 const float*, const uint8_t*, const float*, void*,
-                                                int64_t, hipStream_t);
+                                                int64_t, int, hipStream_t);
 
 }  // namespace tpk

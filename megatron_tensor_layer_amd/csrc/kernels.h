@@ -45,10 +45,11 @@ hipError_t gemv_launch(int I, int K, int N, const T* X, int64_t ldx, const T* W0
 // most kFp8MaxK.
 constexpr int kFp8MaxTokens = 8;
 constexpr int64_t kFp8MaxK = 16384;
+// fmt: kFmtE4M3 or kFmtInt8 (common.h), the code format of W0 and W1.
 template <int EPI>
 hipError_t gemv_fp8_launch(int I, int K, int N, const uint16_t* X, const uint8_t* W0,
                            const float* S0, const uint8_t* W1, const float* S1, void* out,
-                           int64_t ldo, hipStream_t stream);
+                           int64_t ldo, int fmt, hipStream_t stream);
 
 // Same product on bf16 MFMA for 9..64 tokens, weights streamed once from HBM,
 // K split over workgroups; `workspace` (splitk_workspace_bytes) holds the
@@ -71,7 +72,7 @@ hipError_t splitk_launch(int I, int K, int N, const uint16_t* X, const uint16_t*
 template <int EPI>
 hipError_t splitk_fp8_launch(int I, int K, int N, const uint16_t* X, const uint8_t* W0,
                              const float* S0, const uint8_t* W1, const float* S1, void* out,
-                             int64_t ldo, void* workspace, hipStream_t stream);
+                             int64_t ldo, void* workspace, int fmt, hipStream_t stream);
 
 // Same product for 9..32 tokens with each workgroup covering the whole K
 // axis of two 16-row weight tiles (no workspace); rowstream_suits says when
@@ -90,7 +91,7 @@ hipError_t rowstream_launch(int I, int K, int N, const uint16_t* X, const uint16
 template <int EPI>
 hipError_t rowstream_fp8_launch(int I, int K, int N, const uint16_t* X, const uint8_t* W0,
                                 const float* S0, const uint8_t* W1, const float* S1, void* out,
-                                int64_t ldo, hipStream_t stream);
+                                int64_t ldo, int fmt, hipStream_t stream);
 
 // Same product on bf16 MFMA for any M (128 x 128 tiles).  When the tiles
 // cannot fill the chip, K is split over workgroups and `workspace`

@@ -58,12 +58,13 @@ static_assert(lds_bytes<2>() <= 160 * 1024, "two chunks of 32 tokens and the til
 template <int MT>
 constexpr int xpw() { return kKW * 8 * MT / kWaves; }
 
-template <int MT, int EPI, int P, bool F8>
+template <int MT, int EPI, int P, int WF>
 __global__ void __launch_bounds__(kThreads)
 rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
                  const void* __restrict__ W0, const void* __restrict__ W1,
                  const float* __restrict__ S0, const float* __restrict__ S1, int KS,
                  int RPT, void* __restrict__ out, int64_t ldo) {
+  constexpr bool F8 = WF != kWBf16;  // one-byte codes with a row scale
   constexpr int XPW = xpw<MT>();
   constexpr int ES = F8 ? 1 : 2;   // bytes per weight
   constexpr int LPG = F8 ? 2 : 4;  // load instructions per 128-K group
@@ -166,7 +167,10 @@ rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
         for (int p = 0; p < LPG; ++p) {
           const int r = 8 * p + (lane >> 3), c = 2 * (lane & 7);
           u32x4_t lo, hi;
-          decode16(w[p], lo, hi);
+          if constexpr (WF == kWInt8)
+            decode16_i8(w[p], lo, hi);
+          else
+            decode16(w[p], lo, hi);
           *reinterpret_cast<u32x4_t*>(tile + r * 256 + ((c ^ r) * 16)) = lo;
           *reinterpret_cast<u32x4_t*>(tile + r * 256 + (((c + 1) ^ r) * 16)) = hi;
         }
@@ -253,13 +257,14 @@ rowstream_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
   }
 }
 
-template <int MT, int EPI, bool F8>
+template <int MT, int EPI, int WF>
 hipError_t launch_mt(int I, int K, int N, const uint16_t* X, const void* W0, const void* W1,
                      const float* S0, const float* S1, void* out, int64_t ldo,
                      hipStream_t stream) {
+  constexpr bool F8 = WF != kWBf16;
   // bf16: 2 groups of 128 K in flight per wave (4 measured slower); FP8: 4,
   // the same bytes in flight
-  auto kern = rowstream_kernel<MT, EPI, F8 ? 4 : 2, F8>;
+  auto kern = rowstream_kernel<MT, EPI, F8 ? 4 : 2, WF>;
   static bool attr_set = false;  // raising the dynamic-LDS limit once per process is enough
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -314,27 +319,31 @@ hipError_t rowstream_launch(int I, int K, int N, const uint16_t* X, const uint16
                             const uint16_t* W1, void* out, int64_t ldo, hipStream_t stream) {
   if (I < 1 || I > kRowStreamMaxTokens || K < 1 || K > kRowStreamMaxK || N < 1)
     return hipErrorInvalidValue;
-  if (I <= 16) return launch_mt<1, EPI, false>(I, K, N, X, W0, W1, nullptr, nullptr, out, ldo, stream);
-  return launch_mt<2, EPI, false>(I, K, N, X, W0, W1, nullptr, nullptr, out, ldo, stream);
+  if (I <= 16) return launch_mt<1, EPI, kWBf16>(I, K, N, X, W0, W1, nullptr, nullptr, out, ldo, stream);
+  return launch_mt<2, EPI, kWBf16>(I, K, N, X, W0, W1, nullptr, nullptr, out, ldo, stream);
 }
 
 template <int EPI>
 hipError_t rowstream_fp8_launch(int I, int K, int N, const uint16_t* X, const uint8_t* W0,
                                 const float* S0, const uint8_t* W1, const float* S1, void* out,
-                                int64_t ldo, hipStream_t stream) {
+                                int64_t ldo, int fmt, hipStream_t stream) {
   if (I < 1 || I > kRowStreamMaxTokens || K < 1 || K > kRowStreamMaxK || N < 1 || (K % 16))
     return hipErrorInvalidValue;
-  if (I <= 16) return launch_mt<1, EPI, true>(I, K, N, X, W0, W1, S0, S1, out, ldo, stream);
-  return launch_mt<2, EPI, true>(I, K, N, X, W0, W1, S0, S1, out, ldo, stream);
+  if (fmt == kFmtInt8) {
+    if (I <= 16) return launch_mt<1, EPI, kWInt8>(I, K, N, X, W0, W1, S0, S1, out, ldo, stream);
+    return launch_mt<2, EPI, kWInt8>(I, K, N, X, W0, W1, S0, S1, out, ldo, stream);
+  }
+  if (I <= 16) return launch_mt<1, EPI, kWE4M3>(I, K, N, X, W0, W1, S0, S1, out, ldo, stream);
+  return launch_mt<2, EPI, kWE4M3>(I, K, N, X, W0, W1, S0, S1, out, ldo, stream);
 }
 
 template hipError_t rowstream_fp8_launch<EPI_F32>(int, int, int, const uint16_t*, const uint8_t*,
                                                   const float*, const uint8_t*, const float*,
-                                                  void*, int64_t, hipStream_t);
+                                                  void*, int64_t, int, hipStream_t);
 template hipError_t rowstream_fp8_launch<EPI_SWIGLU>(int, int, int, const uint16_t*,
                                                      const uint8_t*, const float*,
                                                      const uint8_t*, const float*, void*,
-                                                     int64_t, hipStream_t);
+                                                     int64_t, int, hipStream_t);
 
 template hipError_t rowstream_launch<EPI_F32>(int, int, int, const uint16_t*, const uint16_t*,
                                               const uint16_t*, void*, int64_t, hipStream_t);

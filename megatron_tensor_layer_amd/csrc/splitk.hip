@@ -49,13 +49,14 @@ constexpr int kCUs = 256;
 // matrix (N rows): block rb covers rows [16 NW rb, 16 NW (rb + 1)).  SwiGLU
 // (gate W0 and up W1, N rows each): block rb covers F rows f0 = 8 NW rb ..
 // f0 + 8 NW, its first NW/2 tiles from gate, the other NW/2 from up.
-template <int MT, int P, int EPI, bool F8, int MAXT>
+template <int MT, int P, int EPI, int WF, int MAXT>
 __global__ void __launch_bounds__(MAXT)
 splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
               const void* __restrict__ W0, const void* __restrict__ W1,
               const float* __restrict__ S0, const float* __restrict__ S1, int KR,
               unsigned* __restrict__ counters, float* __restrict__ part, int NR,
               void* __restrict__ out, int64_t ldo) {
+  constexpr bool F8 = WF != kWBf16;  // one-byte codes with a row scale
   constexpr int TOK = 16 * MT;
   constexpr int ES = F8 ? 1 : 2;    // bytes per weight
   constexpr int LPG = F8 ? 2 : 4;   // load instructions per 128-K group
@@ -141,7 +142,10 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
         for (int p = 0; p < LPG; ++p) {
           const int r = 8 * p + (lane >> 3), c = 2 * (lane & 7);
           u32x4_t lo, hi;
-          decode16(wv[b][p], lo, hi);
+          if constexpr (WF == kWInt8)
+            decode16_i8(wv[b][p], lo, hi);
+          else
+            decode16(wv[b][p], lo, hi);
           *reinterpret_cast<u32x4_t*>(tile + r * 256 + ((c ^ r) * 16)) = lo;
           *reinterpret_cast<u32x4_t*>(tile + r * 256 + (((c + 1) ^ r) * 16)) = hi;
         }
@@ -372,15 +376,16 @@ Plan make_plan(int I, int K, int N, bool swiglu) {
   }
 }
 
-template <int MT, int EPI, bool F8 = false>
+template <int MT, int EPI, int WF = kWBf16>
 hipError_t launch_plan(const Plan& pl, int I, int K, int N, const uint16_t* X, const void* W0,
                        const void* W1, void* out, int64_t ldo, void* workspace,
                        hipStream_t stream, const float* S0 = nullptr, const float* S1 = nullptr) {
+  constexpr bool F8 = WF != kWBf16;
   // plans of at most 4 waves run the variant bounded to 256 threads (more
   // registers per wave: the finish sums two items per batch)
   const bool small = pl.nw <= 4;
-  auto kern = small ? splitk_kernel<MT, F8 ? 4 : 2, EPI, F8, 256>
-                    : splitk_kernel<MT, F8 ? 4 : 2, EPI, F8, 1024>;
+  auto kern = small ? splitk_kernel<MT, F8 ? 4 : 2, EPI, WF, 256>
+                    : splitk_kernel<MT, F8 ? 4 : 2, EPI, WF, 1024>;
   static bool attr_set[2] = {false, false};  // raising the dynamic-LDS limit once is enough
   if (!attr_set[small]) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -438,11 +443,14 @@ template hipError_t splitk_launch<EPI_SWIGLU>(int, int, int, const uint16_t*, co
 template <int EPI>
 hipError_t splitk_fp8_launch(int I, int K, int N, const uint16_t* X, const uint8_t* W0,
                              const float* S0, const uint8_t* W1, const float* S1, void* out,
-                             int64_t ldo, void* workspace, hipStream_t stream) {
+                             int64_t ldo, void* workspace, int fmt, hipStream_t stream) {
   const Plan pl = make_plan(I, K, N, EPI == EPI_SWIGLU);
   if (pl.grid == 0) return hipErrorInvalidValue;
-#define TPK_F8(MTV) \
-  launch_plan<MTV, EPI, true>(pl, I, K, N, X, W0, W1, out, ldo, workspace, stream, S0, S1)
+#define TPK_F8(MTV)                                                                       \
+  (fmt == kFmtInt8 ? launch_plan<MTV, EPI, kWInt8>(pl, I, K, N, X, W0, W1, out, ldo, workspace, \
+                                                    stream, S0, S1)                           \
+                   : launch_plan<MTV, EPI, kWE4M3>(pl, I, K, N, X, W0, W1, out, ldo, workspace, \
+                                                    stream, S0, S1))
   if (I <= 16) return TPK_F8(1);
   if (I <= 32) return TPK_F8(2);
   if (I <= 48) return TPK_F8(3);
@@ -452,9 +460,9 @@ hipError_t splitk_fp8_launch(int I, int K, int N, const uint16_t* X, const uint8
 
 template hipError_t splitk_fp8_launch<EPI_F32>(int, int, int, const uint16_t*, const uint8_t*,
                                                const float*, const uint8_t*, const float*, void*,
-                                               int64_t, void*, hipStream_t);
+                                               int64_t, void*, int, hipStream_t);
 template hipError_t splitk_fp8_launch<EPI_SWIGLU>(int, int, int, const uint16_t*, const uint8_t*,
                                                   const float*, const uint8_t*, const float*,
-                                                  void*, int64_t, void*, hipStream_t);
+                                                  void*, int64_t, void*, int, hipStream_t);
 
 }  // namespace tpk

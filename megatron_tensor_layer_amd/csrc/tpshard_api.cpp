@@ -322,11 +322,16 @@ size_t tp_shard_mlp_fp8_workspace_size(int64_t I, int64_t D, int64_t F_local) {
   return std::max(tpk::splitk_workspace_bytes((int)I, (int)D, (int)F_local, true), down);
 }
 
-tp_status_t tp_shard_mlp_fp8(int64_t I, int64_t D, int64_t F_local, const void* X,
-                             const void* W_gate, const float* s_gate, const void* W_up,
-                             const float* s_up, const void* W_down, const float* s_down,
-                             void* H, float* P, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+}  // extern "C"
+
+namespace {
+// The weight-only MLP share with one-byte codes of format fmt (kFmtE4M3 or
+// kFmtInt8) and one fp32 scale per output row; both formats run the same
+// kernels and plans, only the decode of a 16-byte chunk of codes differs.
+tp_status_t mlp_bytew(int fmt, int64_t I, int64_t D, int64_t F_local, const void* X,
+                      const void* W_gate, const float* s_gate, const void* W_up,
+                      const float* s_up, const void* W_down, const float* s_down, void* H,
+                      float* P, void* workspace, size_t workspace_bytes, void* stream) {
   if (I < 0 || I > kMaxDim || !dims_ok(D) || !dims_ok(F_local)) return TP_ERR_INVALID;
   if (I == 0) return TP_OK;
   if (!X || !W_gate || !s_gate || !W_up || !s_up || !W_down || !s_down || !H || !P)
@@ -363,20 +368,46 @@ tp_status_t tp_shard_mlp_fp8(int64_t I, int64_t D, int64_t F_local, const void* 
   hipError_t e;
   if (path == Fp8Path::Gemv) {
     e = tpk::gemv_fp8_launch<tpk::EPI_SWIGLU>((int)I, (int)D, (int)F_local, Xb, g8, s_gate, u8,
-                                              s_up, H, F_local, s);
+                                              s_up, H, F_local, fmt, s);
     if (e != hipSuccess) return TP_ERR_LAUNCH;
     return launched(tpk::gemv_fp8_launch<tpk::EPI_F32>((int)I, (int)F_local, (int)D, Hb, d8,
-                                                       s_down, nullptr, nullptr, P, D, s));
+                                                       s_down, nullptr, nullptr, P, D, fmt, s));
   }
   e = tpk::splitk_fp8_launch<tpk::EPI_SWIGLU>((int)I, (int)D, (int)F_local, Xb, g8, s_gate, u8,
-                                              s_up, H, F_local, workspace, s);
+                                              s_up, H, F_local, workspace, fmt, s);
   if (e != hipSuccess) return TP_ERR_LAUNCH;
   if (fp8_down_rowstream(I, D, F_local))
     return launched(tpk::rowstream_fp8_launch<tpk::EPI_F32>((int)I, (int)F_local, (int)D, Hb, d8,
-                                                            s_down, nullptr, nullptr, P, D, s));
+                                                            s_down, nullptr, nullptr, P, D, fmt,
+                                                            s));
   return launched(tpk::splitk_fp8_launch<tpk::EPI_F32>((int)I, (int)F_local, (int)D, Hb, d8,
                                                        s_down, nullptr, nullptr, P, D, workspace,
-                                                       s));
+                                                       fmt, s));
+}
+}  // namespace
+
+extern "C" {
+
+tp_status_t tp_shard_mlp_fp8(int64_t I, int64_t D, int64_t F_local, const void* X,
+                             const void* W_gate, const float* s_gate, const void* W_up,
+                             const float* s_up, const void* W_down, const float* s_down,
+                             void* H, float* P, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return mlp_bytew(tpk::kFmtE4M3, I, D, F_local, X, W_gate, s_gate, W_up, s_up, W_down, s_down,
+                   H, P, workspace, workspace_bytes, stream);
+}
+
+size_t tp_shard_mlp_int8_workspace_size(int64_t I, int64_t D, int64_t F_local) {
+  return tp_shard_mlp_fp8_workspace_size(I, D, F_local);
+}
+
+tp_status_t tp_shard_mlp_int8(int64_t I, int64_t D, int64_t F_local, const void* X,
+                              const void* W_gate, const float* s_gate, const void* W_up,
+                              const float* s_up, const void* W_down, const float* s_down,
+                              void* H, float* P, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return mlp_bytew(tpk::kFmtInt8, I, D, F_local, X, W_gate, s_gate, W_up, s_up, W_down, s_down,
+                   H, P, workspace, workspace_bytes, stream);
 }
 
 tp_status_t tp_residual_rmsnorm(int32_t t, int64_t I, int64_t D, const float* partials,

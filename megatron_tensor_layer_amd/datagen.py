@@ -192,6 +192,27 @@ def fp8_mlp_weights(D: int, F: int, pool: int):
             fp8_weights("W_down8", (D, F), sigma, pool))
 
 
+def int8_weights(name: str, shape, sigma: float, pool: int):
+    """Synthetic int8 weight-only storage of an [N, K] matrix: N(0, sigma^2)
+    weights, one fp32 scale per row (row absmax / 127) and each weight /
+    scale rounded to the nearest integer (ties to even), which lies in
+    [-127, 127].  Returns (codes int8 [N, K], scales float32 [N])."""
+    w = gaussian(name, shape, sigma, "f32", pool).astype(np.float64)
+    amax = np.abs(w).max(axis=1)
+    scales = (np.where(amax > 0, amax, 1.0) / 127.0).astype(np.float32)
+    q = np.rint(w / scales.astype(np.float64)[:, None])
+    return np.clip(q, -127, 127).astype(np.int8), scales
+
+
+def int8_mlp_weights(D: int, F: int, pool: int):
+    """int8 storage of a full MLP: (gate, up [F, D], down [D, F]) as
+    (codes, scales) pairs, weights N(0, 1/D)."""
+    sigma = D ** -0.5
+    return (int8_weights("W_gate8", (F, D), sigma, pool),
+            int8_weights("W_up8", (F, D), sigma, pool),
+            int8_weights("W_down8", (D, F), sigma, pool))
+
+
 def fp8_mlp_rank_shards(fp8_full, t: int, r: int):
     """Rank r's contiguous F block of FP8 MLP storage: gate/up rows and down
     columns (the down scales are per output row, so they are shared)."""

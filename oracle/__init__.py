@@ -72,6 +72,8 @@ class Oracle:
         lib.orc_e4m3.argtypes = [ctypes.c_ubyte]
         lib.orc_dequant_fp8.restype = None
         lib.orc_dequant_fp8.argtypes = [_i64, _i64, ctypes.POINTER(ctypes.c_ubyte), _pd, _pd]
+        lib.orc_dequant_int8.restype = None
+        lib.orc_dequant_int8.argtypes = [_i64, _i64, ctypes.POINTER(ctypes.c_byte), _pd, _pd]
         lib.orc_residual_rmsnorm.restype = None
         lib.orc_residual_rmsnorm.argtypes = [_i64] * 3 + [_pd] * 3 + [ctypes.c_double, _pd, _pd]
 
@@ -217,6 +219,16 @@ class Oracle:
         W = np.empty((N, K))
         self.lib.orc_dequant_fp8(N, K, c.ctypes.data_as(ctypes.POINTER(ctypes.c_ubyte)),
                                  self._p(sc), self._p(W))
+        return W
+
+    def dequant_int8(self, codes, scales) -> np.ndarray:
+        """W[n, k] = scales[n] * codes[n, k] for int8 codes (fp64)."""
+        c = np.ascontiguousarray(codes, dtype=np.int8)
+        sc = self._f64(scales)
+        N, K = c.shape
+        W = np.empty((N, K))
+        self.lib.orc_dequant_int8(N, K, c.ctypes.data_as(ctypes.POINTER(ctypes.c_byte)),
+                                  self._p(sc), self._p(W))
         return W
 
     # ------------------------------------------------------------ around the block

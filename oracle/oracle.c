@@ -322,6 +322,19 @@ void orc_dequant_fp8(int64_t N, int64_t K, const unsigned char *codes, const dou
 }
 
 /*
+ * Weight-only int8 storage for decode (the PaLM int8-weight figures of
+ * lecture §5.5; the pages give no convention, the reading here is): each
+ * weight is one signed byte and every output row n carries one scale s[n]:
+ * W[n, k] = s[n] * code[n, k], codes in [-128, 127].
+ */
+void orc_dequant_int8(int64_t N, int64_t K, const signed char *codes, const double *scales,
+                      double *W) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) W[n * K + k] = scales[n] * (double)codes[n * K + k];
+}
+
+/*
  * Decode attention of one rank over its KV cache, lecture §4.4: the cache is
  * split with the heads, each rank storing and reading only the KV groups of
  * its own query heads (a group is stored on every rank that needs it once

@@ -42,6 +42,8 @@ MUTANTS = {
     "bf16_round_extra_bit": ("int q = e - 8;", "int q = e - 9;"),
     "bf16_round_no_subnormal_floor": ("if (q < -133) q = -133;", "if (q < -140) q = -140;"),
     "bf16h_down_from_unrounded": ("sb += Hb[q * Fl + (f - f0)] * Wd[n * F + f];", "sb += H[q * Fl + (f - f0)] * Wd[n * F + f];"),
+    "int8_unsigned": ("scales[n] * (double)codes[n * K + k]", "scales[n] * (double)(unsigned char)codes[n * K + k]"),
+    "int8_row_scale": ("W[n * K + k] = scales[n] * (double)codes", "W[n * K + k] = scales[k % N] * (double)codes"),
     "fp8_row_scale": ("scales[n] * orc_e4m3(codes[n * K + k])", "scales[k % N] * orc_e4m3(codes[n * K + k])"),
 }
 

@@ -359,6 +359,19 @@ def pin_fp8_dequant_rows(orc):
     assert np.array_equal(W, ref)
 
 
+def pin_int8_dequant_rows(orc):
+    """int8 weight-only storage: each row scales its signed codes by its own
+    scale, over the whole code range (two's complement bytes)."""
+    codes = np.array([[-128, -1, 0, 1], [127, 64, -64, 5]], dtype=np.int8)
+    W = orc.dequant_int8(codes, [0.5, -2.0])
+    ref = np.array([[-64.0, -0.5, 0.0, 0.5], [-254.0, -128.0, 128.0, -10.0]])
+    assert np.array_equal(W, ref)
+    allc = np.arange(-128, 128, dtype=np.int8).reshape(2, 128)
+    W = orc.dequant_int8(allc, [1.0, 3.0])
+    assert np.array_equal(W[0], np.arange(-128, 0, dtype=np.float64))
+    assert np.array_equal(W[1], 3.0 * np.arange(0, 128, dtype=np.float64))
+
+
 def pin_sequence_shards_concatenate(orc):
     """Sequence parallelism (reduce-scatter, norm on each rank's rows,
     all-gather) gives the all-reduce layout's values: the residual update and
@@ -505,6 +518,7 @@ ALL_PINS = [
     pin_rmsnorm_closed_forms,
     pin_fp8_decode,
     pin_fp8_dequant_rows,
+    pin_int8_dequant_rows,
     pin_sequence_shards_concatenate,
     pin_attn_decode,
     pin_bf16_round,
