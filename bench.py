@@ -172,8 +172,8 @@ def prefill_roofline(torch, tp, layer, calls):
     return dict(bound="mfma", achieved=round(tf, 1), peak=PEAK_BF16, unit="TFLOP/s",
                 frac=round(tf / PEAK_BF16, 4), traffic=None,
                 kernel=f"tp_shard_mlp I={PREFILL_I} D={D} F_local={F // TP} "
-                       "(gemm_kernel SwiGLU epilogue for gate/up, then gemm_kernel fp32 "
-                       "epilogue for down, 128 x 128 tiles)",
+                       "(gate/up + SwiGLU on gemm_wide_kernel, 256 x 128 tiles with K split "
+                       "2 ways, then down on gemm_kernel, 128 x 128 tiles)",
                 avg_call_us=round(avg, 2), median_call_us=stats(us)["median_us"],
                 algorithmic_flops_per_call=m.flops())
 

@@ -1,5 +1,7 @@
 // Projections for many tokens: C[M, N] = A[M, K] . W[N, K]^T on bf16 MFMA
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation), in three tile shapes chosen
+// per call by a cost model: 128 x 128 (described here), 256 x 256 and 256 x
+// 128 (described at their kernels below).
 //
 // Prefill and large decode batches are the compute-heavy side of the layer
 // (lecture "Distributed Serving", §3.4: 2·B·D·F/n FLOPs per rank); the kernel
@@ -108,7 +110,8 @@ __device__ __forceinline__ void store_out4(void* out, int64_t ldo, int m, int co
 // load needs no address register of its own.  Rows past M read zero through
 // an out-of-range lane offset, splits past ns are not loaded.  When the
 // finishing workgroup's own partial is still in LDS (own >= 0: the sum of
-// the row-major tiles own0 and own1), that split is taken from there.
+// the row-major tiles own0 and own1, or own0 alone when own1 is null), that
+// split is taken from there.
 template <int EPI, int TM, int TN, int THREADS, int IQ>
 __device__ __forceinline__ void finish_splits(const __amdgpu_buffer_rsrc_t pr, int64_t tbase,
                                               int64_t plane, int ns, int m0, int c0, int M,
@@ -149,7 +152,7 @@ __device__ __forceinline__ void finish_splits(const __amdgpu_buffer_rsrc_t pr, i
 #pragma unroll
           for (int q = 0; q < kNQ; ++q) {
             if (sp == own)
-              v[i][q][e] = own0[fi[i][q]] + own1[fi[i][q]];
+              v[i][q][e] = own1 ? own0[fi[i][q]] + own1[fi[i][q]] : own0[fi[i][q]];
             else if (sp < ns)
               v[i][q][e] = __builtin_bit_cast(
                   f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
@@ -644,31 +647,283 @@ gemm_big_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda
                                       nullptr, nullptr);
 }
 
+// ---------------------------------------------------------------- 256 x 128
+// The same product with 256 x 128 workgroup tiles (256 activation rows, 128
+// weight rows): per K element a CU copies 384 rows for 2 x 256 x 128 FLOPs, a
+// quarter fewer bytes per FLOP than the 128 x 128 tile.  Where the copy
+// stream of a CU is the limit (the 512-token rank shapes) that is the gain;
+// the per-rank shapes then give half as many tiles, and K is split in two
+// to fill the chip.
+//   * eight waves: a 2 x 2 grid of 128 x 64 wave tiles (4 x 2 MFMA
+//     fragments, 128 fp32 accumulators per lane), twice -- the two groups of
+//     four waves take alternate halves of every stage's 16-wide K steps, so
+//     the LDS bytes read per MFMA are those of the 256 x 256 tile;
+//   * KB K per stage: 64 (128-byte tile rows, the 128 x 128 kernel's
+//     layout, three 48 KB stages, two in flight) or 32 (64-byte rows, the
+//     256 x 256 kernel's layout, six 24 KB stages, five in flight);
+//   * after the K loop the second group's accumulators go to one row-major
+//     [256][128] fp32 tile in LDS and the first group adds its own in place,
+//     then the epilogue (or the split-K partial store) reads that tile;
+//   * SwiGLU, split K and the XCD-aware order as in the 128 x 128 kernel.
+constexpr int WM = 256, WN = 128;
+
+template <int KB>
+struct WideCfg {
+  static constexpr int kRow = KB * 2;               // bytes per LDS tile row
+  static constexpr int kRowsPerInst = 1024 / kRow;  // tile rows one 1 KB copy fills
+  static constexpr int kLanesPerRow = kRow / 16;
+  static constexpr int kStageA = WM * kRow;
+  static constexpr int kStage = (WM + WN) * kRow;   // 24 KB or 48 KB
+  static constexpr int kS = KB == 64 ? 3 : 6;       // stages
+  static constexpr int kLds = kS * kStage;          // 144 KB
+  static constexpr int kInstA = WM / kRowsPerInst / 8;  // per wave and stage
+  static constexpr int kInstW = WN / kRowsPerInst / 8;
+  static constexpr int kInst = kInstA + kInstW;
+  static constexpr int kStepsPerGroup = KB / 32;    // 16-wide K steps of a group per stage
+  // byte offset of (row, logical 16-byte chunk): chunk c of row r sits in slot
+  // c ^ ((r / 2) % 8) (128-byte rows) or c ^ ((r / 4) % 4) (64-byte rows), so
+  // the 32 rows of one operand read cover all 64 banks
+  static __device__ __forceinline__ int off(int row, int chunk) {
+    if constexpr (KB == 64)
+      return row * kRow + ((chunk ^ ((row >> 1) & 7)) << 4);
+    else
+      return row * kRow + ((chunk ^ ((row >> 2) & 3)) << 4);
+  }
+  static __device__ __forceinline__ int slot_chunk(int row, int slot) {
+    if constexpr (KB == 64)
+      return slot ^ ((row >> 1) & 7);
+    else
+      return slot ^ ((row >> 2) & 3);
+  }
+  static_assert(WM * WN * 4 + 4 <= kLds, "the K-group tile and the arrival flag fit");
+  static_assert(kInstA * 8 * kRowsPerInst == WM && kInstW * 8 * kRowsPerInst == WN,
+                "whole copy instructions per wave");
+};
+
+template <int EPI, int KB>
+__global__ void __launch_bounds__(kThreads)
+gemm_wide_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
+                 const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
+                 void* __restrict__ out, int64_t ldo, int KR, unsigned* __restrict__ counters,
+                 float* __restrict__ part) {
+  using C = WideCfg<KB>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLds];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wave >> 2;  // K group
+  const int wm = (wave >> 1) & 1, wn = wave & 1;
+
+  const int mt_n = (M + WM - 1) / WM;
+  constexpr int kCols = (EPI == EPI_SWIGLU) ? WN / 2 : WN;  // output columns per tile
+  const int nt_n = (N + kCols - 1) / kCols;
+  const int tiles = mt_n * nt_n;
+  const int ns = (K + KR - 1) / KR;
+  const int G = tiles * ns;
+  int b = blockIdx.x;
+  const int G8 = G & ~7;
+  if (b < G8) b = (b & 7) * (G8 >> 3) + (b >> 3);
+  const int split = b / tiles;
+  const int tile = b % tiles;
+  const int tm = tile % mt_n, tn = tile / mt_n;
+  const int m0 = tm * WM, c0 = tn * kCols;
+  const int kb = split * KR, ke = min(K, kb + KR);
+
+  const u32x4_t ra = rsrc_words(A + (int64_t)m0 * lda, (uint32_t)min(WM, M - m0) * (uint32_t)lda * 2u);
+  const int wrows = min(kCols, N - c0);
+  const u32x4_t rw0 = rsrc_words(W0 + (int64_t)c0 * K, (uint32_t)wrows * (uint32_t)K * 2u);
+  const u32x4_t rw1 = rsrc_words((EPI == EPI_SWIGLU ? W1 : W0) + (int64_t)c0 * K,
+                                 (uint32_t)wrows * (uint32_t)K * 2u);
+
+  // Stage st into buffer buf: 1 KB copy instructions, first the A rows, then
+  // the W rows; wave w issues A instructions w, w + 8, ... and W instructions
+  // likewise.  Lane l fills slot l % kLanesPerRow of row
+  // kRowsPerInst q + l / kLanesPerRow with the logical chunk that C::off
+  // places there; past the K range, M or N the offset is out of range and
+  // the slot is zero-filled.
+  const int rr = lane / C::kLanesPerRow, sl = lane % C::kLanesPerRow;
+  const uint32_t lsm = lds_addr(smem);
+  auto issue = [&](int st, int buf) {
+    const uint32_t la = lsm + buf * C::kStage;
+    const int k0 = kb + st * KB;
+#pragma unroll
+    for (int h = 0; h < C::kInstA; ++h) {
+      const int q = wave + h * 8;
+      const int r = q * C::kRowsPerInst + rr;
+      const int k = k0 + C::slot_chunk(r, sl) * 8;
+      const uint32_t oa = (k < ke && m0 + r < M) ? (uint32_t)r * (uint32_t)lda * 2u + (uint32_t)k * 2u
+                                                 : kOob;
+      lds_dma16(ra, oa, la + q * 1024);
+    }
+#pragma unroll
+    for (int h = 0; h < C::kInstW; ++h) {
+      const int q = wave + h * 8;
+      const int r = q * C::kRowsPerInst + rr;  // W tile row
+      const int k = k0 + C::slot_chunk(r, sl) * 8;
+      const int wr = (EPI == EPI_SWIGLU) ? (r & 63) : r;  // SwiGLU: 64 gate rows, then 64 up
+      const uint32_t ow = (k < ke && wr < wrows) ? (uint32_t)wr * (uint32_t)K * 2u + (uint32_t)k * 2u
+                                                 : kOob;
+      lds_dma16((EPI == EPI_SWIGLU && r >= 64) ? rw1 : rw0, ow, la + C::kStageA + q * 1024);
+    }
+  };
+
+  // W tile rows of this wave's two 32-column fragments
+  int brow[2];
+  if constexpr (EPI == EPI_SWIGLU) {
+    brow[0] = wn * 32;       // gate f = c0 + wn*32 + lane%32
+    brow[1] = 64 + wn * 32;  // up, same f
+  } else {
+    brow[0] = wn * 64;
+    brow[1] = wn * 64 + 32;
+  }
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int NT = (ke - kb + KB - 1) / KB;
+#pragma unroll
+  for (int st = 0; st < C::kS - 1; ++st) issue(st, st);
+
+  int buf = 0;  // kt % kS
+  for (int kt = 0; kt < NT; ++kt) {
+    wait_vmcnt<(C::kS - 2) * C::kInst>();  // this wave's part of stage kt has landed
+    __syncthreads();                       // everyone's has; stage kt - 1 is consumed
+    const unsigned char* sa = smem + buf * C::kStage;
+    const unsigned char* sb = sa + C::kStageA;
+#pragma unroll
+    for (int h = 0; h < C::kStepsPerGroup; ++h) {
+      const int c = (g * C::kStepsPerGroup + h) * 2 + (lane >> 5);  // 16-byte chunk
+      bf16x8_t af[4], bw[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + C::off(wm * 128 + i * 32 + (lane & 31), c));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bw[j] = *reinterpret_cast<const bf16x8_t*>(sb + C::off(brow[j] + (lane & 31), c));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bw[j], acc[i][j], 0, 0, 0);
+    }
+    // refill stage kt - 1's buffer after this stage's MFMAs are issued
+    issue(kt + C::kS - 1, buf == 0 ? C::kS - 1 : buf - 1);
+    buf = buf == C::kS - 1 ? 0 : buf + 1;
+  }
+
+  wait_vmcnt<0>();  // zero-fill loads of stages past the end have landed
+  __syncthreads();
+
+  // ---- one row-major [WM][WN] fp32 tile: group 1 writes, group 0 adds
+  float* T = reinterpret_cast<float*>(smem);
+  if (g == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          T[(wm * 128 + i * 32 + acc_row32(r, lane)) * WN + brow[j] + (lane & 31)] = acc[i][j][r];
+  }
+  __syncthreads();
+  if (g == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          T[(wm * 128 + i * 32 + acc_row32(r, lane)) * WN + brow[j] + (lane & 31)] += acc[i][j][r];
+  }
+  __syncthreads();
+  const f32x4_t* t0 = reinterpret_cast<const f32x4_t*>(smem);
+
+  if (ns > 1) {
+    const int64_t tile_elems = (int64_t)WM * WN;
+    const __amdgpu_buffer_rsrc_t pr =
+        make_rsrc(part, (uint32_t)((int64_t)ns * tiles * tile_elems * 4));
+    const int64_t tbase = (int64_t)tile * tile_elems;
+    const int64_t plane = (int64_t)tiles * tile_elems;
+#pragma unroll
+    for (int k = 0; k < WM * WN / 4 / kThreads; ++k) {
+      const int q = tid + k * kThreads;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, t0[q]), pr,
+                                             (uint32_t)((split * plane + tbase + 4 * q) * 4), 0,
+                                             kAuxSys);
+    }
+    int* is_last = reinterpret_cast<int*>(smem + WM * WN * 4);  // past the tile
+    wait_vmcnt<0>();  // partial stores have reached memory
+    __syncthreads();
+    if (tid == 0) *is_last = arrive_last(counters + tile, (unsigned)ns);
+    __syncthreads();
+    if (!*is_last) return;
+    finish_splits<EPI, WM, WN, kThreads, 8>(pr, tbase, plane, ns, m0, c0, M, N, out, ldo, tid,
+                                            split, t0, nullptr);
+    return;
+  }
+
+  constexpr int kQ = kCols / 4;  // items (4 output columns of one row) per tile row
+#pragma unroll
+  for (int k = 0; k < WM * kQ / kThreads; ++k) {
+    const int idx = tid + k * kThreads;
+    const int tr = idx / kQ, tc = (idx % kQ) * 4;
+    const int m = m0 + tr;
+    if (m >= M || c0 + tc >= N) continue;
+    const int fi = (tr * WN + tc) / 4;
+    f32x4_t v = t0[fi];
+    if constexpr (EPI == EPI_SWIGLU) {
+      const f32x4_t u = t0[fi + 16];  // up: 64 columns on
+      v = f32x4_t{silu(v.x) * u.x, silu(v.y) * u.y, silu(v.z) * u.z, silu(v.w) * u.w};
+    }
+    store_out4<EPI == EPI_F32 ? EPI_F32 : EPI_DT>(out, ldo, m, c0 + tc, min(4, N - (c0 + tc)), v);
+  }
+}
+
+constexpr int kWideKB = 64;  // K per stage of the launched 256 x 128 kernel
+
+enum Tile { kT128 = 0, kT256 = 1, kTWide = 2 };  // 128 x 128, 256 x 256, 256 x 128
+
 struct Plan {
-  bool big = false;  // 256 x 256 tiles
+  int shape = kT128;
   int tiles = 0;
   int ns = 0;  // K splits
   int kr = 0;  // K per split
   int grid = 0;
 };
 
-// Cost model (CU cycles) for a tile size and split count.  A workgroup's
+struct TileShape {
+  int bm, bn;   // activation rows, weight rows
+  int bk;       // K per stage
+  double rate;  // copy stream of a CU next to the MFMA work, B/clk
+};
+
+// Measured on this chip at the prefill shapes with every CU busy: the 128 x
+// 128 kernel's copies run at about 21 B/clk per CU, the 256 x 128 kernel's at
+// about 19 and the 256 x 256 kernel's at 12.5.  The two 256-row kernels copy
+// the same bytes per FLOP from the weights; the 256 x 256 kernel's 64-byte
+// tile rows request each 128-byte line in two halves, one stage apart, and
+// the 256 x 128 kernel with such rows was as slow (TP=1 MLP at 512 tokens:
+// 927 us with 64-byte rows, 723 with 128-byte rows, 751 on 256 x 256 tiles).
+constexpr TileShape kShapes[3] = {
+    {BM, BN, BK, 21.0}, {BB, BB, BKB, 12.5}, {WM, WN, kWideKB, 19.0}};
+
+// Cost model (CU cycles) for a tile shape and split count.  A workgroup's
 // main loop runs at the rate its copy stream reaches next to the MFMA work,
-// measured on this chip at the prefill shapes with every CU busy: about
-// 21 B/clk per CU for 128 x 128 tiles and 12.5 B/clk for 256 x 256 (whose
-// copies then interleave less well with the longer MFMA runs), or at the
-// MFMA rate if that is lower.  Workgroups run in rounds of one per CU; with
-// split K each workgroup also writes its partial tile and the last of a
-// tile's workgroups reads all of them, each at the slower of a CU's stream
-// (about 24 B/clk) and its share of HBM (about 2 KB/clk for the chip).
-double plan_cost(int tiles, int ns, bool big, int K) {
-  const int bm = big ? BB : BM, bn = big ? BB : BN;
-  const double rate = big ? 12.5 : 21.0;
-  const double kspl = std::ceil((double)K / BK / ns) * BK;  // K per split
-  const double copy = (double)(bm + bn) * kspl * 2.0 / rate;
-  const double mfma = 2.0 * bm * bn * kspl / (4.0 * 1024.0) / 0.9;
+// or at the MFMA rate if that is lower.  Workgroups run in rounds of one per
+// CU; with split K each workgroup also writes its partial tile and the last
+// of a tile's workgroups reads all of them, each at the slower of a CU's
+// stream (about 24 B/clk) and its share of HBM (about 2 KB/clk for the chip).
+double plan_cost(int tiles, int ns, int shape, int K) {
+  const TileShape& t = kShapes[shape];
+  const double kspl = std::ceil((double)K / t.bk / ns) * t.bk;  // K per split
+  const double copy = (double)(t.bm + t.bn) * kspl * 2.0 / t.rate;
+  const double mfma = 2.0 * t.bm * t.bn * kspl / (4.0 * 1024.0) / 0.9;
   const double rounds = std::ceil((double)tiles * ns / kCUs);
-  const double tile_bytes = (double)bm * bn * 4.0;
+  const double tile_bytes = (double)t.bm * t.bn * 4.0;
   if (ns == 1) return rounds * std::max(copy, mfma) + 1500.0;
   const double hbm = 2080.0;  // B/clk, the whole chip
   const double wgs = (double)tiles * ns;
@@ -677,34 +932,36 @@ double plan_cost(int tiles, int ns, bool big, int K) {
   return rounds * (std::max(copy, mfma) + write) + reduce + 1500.0;
 }
 
-// Split K when the tiles alone leave CUs idle: the split count and tile size
-// of least modelled cost; at least 8 stages of K per split, at most 256 MB of
-// partials and one arrival counter per tile.
+// Split K when the tiles alone leave CUs idle: the tile shape and split
+// count of least modelled cost; at least 8 stages of 64 K per split, at
+// most 256 MB of partials and one arrival counter per tile.  The 256-row
+// shapes need M >= 384 (enough rows to fill most of a tile).
 constexpr double kMaxPartialBytes = 256.0 * 1024 * 1024;
 Plan make_plan(int M, int N, int K, bool swiglu) {
   Plan best_pl;
   double best = 1e300;
-  const int kst = (K + BK - 1) / BK;  // K stages in all
-  const int max_ns = std::max(1, std::min(16, kst / 8));
-  for (int big = 0; big < 2; ++big) {
-    if (big && M < 384) continue;
-    const int bm = big ? BB : BM, bn = big ? BB : BN;
-    const int cols = swiglu ? bn / 2 : bn;
-    const int tiles = ((M + bm - 1) / bm) * ((N + cols - 1) / cols);
+  const int max_ns = std::max(1, std::min(16, (K + BK - 1) / BK / 8));
+  for (int shape = 0; shape < 3; ++shape) {
+    const TileShape& t = kShapes[shape];
+    if (t.bm > BM && M < 384) continue;
+    const int cols = swiglu ? t.bn / 2 : t.bn;
+    const int tiles = ((M + t.bm - 1) / t.bm) * ((N + cols - 1) / cols);
     for (int ns = 1; ns <= max_ns; ++ns) {
-      if (ns > 1 && ((double)ns * tiles * bm * bn * 4.0 > kMaxPartialBytes || tiles > kWsMaxCounters))
+      if (ns > 1 && ((double)ns * tiles * t.bm * t.bn * 4.0 > kMaxPartialBytes || tiles > kWsMaxCounters))
         break;
-      const double cost = plan_cost(tiles, ns, big, K);
+      const double cost = plan_cost(tiles, ns, shape, K);
       if (cost < best * (1.0 - 1e-9)) {
         best = cost;
-        best_pl.big = big;
+        best_pl.shape = shape;
         best_pl.tiles = tiles;
         best_pl.ns = ns;
       }
     }
   }
+  const int bk = kShapes[best_pl.shape].bk;
+  const int kst = (K + bk - 1) / bk;                    // K stages in all
   const int sps = (kst + best_pl.ns - 1) / best_pl.ns;  // stages per split
-  best_pl.kr = sps * BK;
+  best_pl.kr = sps * bk;
   best_pl.ns = (K + best_pl.kr - 1) / best_pl.kr;
   best_pl.grid = best_pl.tiles * best_pl.ns;
   return best_pl;
@@ -712,16 +969,17 @@ Plan make_plan(int M, int N, int K, bool swiglu) {
 
 size_t plan_bytes(const Plan& pl) {
   if (pl.ns <= 1) return 0;
-  const size_t te = pl.big ? (size_t)BB * BB : (size_t)BM * BN;
-  return kWsCounterBytes + (size_t)pl.ns * pl.tiles * te * sizeof(float);
+  const TileShape& t = kShapes[pl.shape];
+  return kWsCounterBytes + (size_t)pl.ns * pl.tiles * t.bm * t.bn * sizeof(float);
 }
 
 template <int EPI>
 hipError_t launch_plan(const Plan& pl, int M, int N, int K, const uint16_t* A, int64_t lda,
                        const uint16_t* W0, const uint16_t* W1, void* out, int64_t ldo,
                        void* workspace, hipStream_t stream) {
-  auto kern = pl.big ? gemm_big_kernel<EPI, 8> : gemm_kernel<EPI>;
-  const int threads = pl.big ? 8 * 64 : kThreads;
+  auto kern = pl.shape == kT256 ? gemm_big_kernel<EPI, 8>
+              : pl.shape == kTWide ? gemm_wide_kernel<EPI, kWideKB>
+                                   : gemm_kernel<EPI>;
   unsigned* counters = nullptr;
   float* part = nullptr;
   if (pl.ns > 1) {
@@ -729,8 +987,8 @@ hipError_t launch_plan(const Plan& pl, int M, int N, int K, const uint16_t* A, i
     counters = static_cast<unsigned*>(workspace);
     part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsCounterBytes);
   }
-  hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(threads), 0, stream, M, N, K, A, lda, W0,
-                     W1, out, ldo, pl.kr, counters, part);
+  hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(kThreads), 0, stream, M, N, K, A, lda, W0, W1,
+                     out, ldo, pl.kr, counters, part);
   return hipGetLastError();
 }
 

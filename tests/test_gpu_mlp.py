@@ -49,6 +49,11 @@ SMALL = [
     # ragged last K slice, down with a ragged last row block, a full grid
     (20, 1040, 2064, 1, 0, "bf16"), (9, 4104, 1032, 1, 0, "bf16"), (32, 1024, 4096, 1, 0, "bf16"),
     (4, 256, 512, 2, 0, "f32"), (11, 264, 200, 2, 1, "f32"), (3, 9216, 64, 1, 0, "f32"),
+    # 256 x 128 GEMM tiles (384 tokens and more): gate/up in one K range and
+    # split 3 ways with a ragged last M tile (390 = 256 + 134), down in one K
+    # range (K = 520, ragged last stage) and split 5 ways
+    (384, 1040, 6152, 1, 0, "bf16"), (390, 3080, 2064, 1, 0, "bf16"),
+    (390, 8200, 520, 1, 0, "bf16"), (390, 3080, 8200, 1, 0, "bf16"),
 ]
 
 
