@@ -209,14 +209,16 @@ def test_mlp_fp8_validation(lib):
 
 def test_workspace_queries_are_host_only(lib):
     # calls that split K (9..64 tokens on the streaming kernel, up to 256 on
-    # the tiled one) need counters + fp32 partials; few-token calls and
-    # prefill need none; invalid sizes report 0
+    # the tiled one, and the 512-token TP=8 gate/up on 256 x 128 tiles) need
+    # counters + fp32 partials; few-token calls need none; invalid sizes
+    # report 0
     ws = lib.tp_shard_mlp_workspace_size
     assert ws(32, 8192, 3584, tp.TP_BF16) > 0
     assert ws(256, 8192, 3584, tp.TP_BF16) > 0
     assert ws(64, 8192, 3584, tp.TP_BF16) >= ws(32, 8192, 3584, tp.TP_BF16) // 4
     assert ws(1, 8192, 3584, tp.TP_BF16) == 0
-    assert ws(512, 8192, 3584, tp.TP_BF16) == 0
+    # 8 KiB of counters + 2 K splits x 112 tiles of 256 x 128 fp32
+    assert ws(512, 8192, 3584, tp.TP_BF16) == 8192 + 2 * 112 * 256 * 128 * 4
     assert ws(32, 8192, 3584, tp.TP_F32) == 0
     assert ws(0, 8192, 3584, tp.TP_BF16) == 0 and ws(32, 0, 3584, tp.TP_BF16) == 0
     wa = lib.tp_shard_attn_proj_workspace_size

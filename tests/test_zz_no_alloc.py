@@ -67,7 +67,8 @@ def test_noalloc_matches_workspace_entry_point(orc, shards):
 
 def test_noalloc_rejects_sizes_beyond_its_array():
     """A call needing more scratch than the array holds (the unsharded
-    Llama-shaped MLP at 512 tokens needs 64 MiB) returns TP_ERR_WORKSPACE and
+    Llama-shaped MLP at 512 tokens needs 32 MiB of partials and 8 KiB of
+    counters) returns TP_ERR_WORKSPACE and
     launches nothing: the NaN canaries of H and P survive."""
     T = torch()
     I, D, F = 512, 8192, 28672
