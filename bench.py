@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--prefill-profile", action="store_true",
                     help="for rocprofv3: each 512-token prefill projection of a TP=8 rank "
                          "(MLP, QKV, o_proj) and the TP=1 MLP in phases of its own, no timing")
+    ap.add_argument("--decode-profile", action="store_true",
+                    help="for rocprofv3: the TP=8 rank's MLP at 1, 8 and 32 tokens with bf16, "
+                         "FP8 and int8 weights, each in a phase of its own, no timing")
     ap.add_argument("--ingest-prefill-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the FETCH_SIZE and WRITE_SIZE passes over --prefill-profile "
                          "into the 512-token MLP entry of profiles/traffic.json")
@@ -261,6 +264,53 @@ def prefill_profile(torch, tp, layer, reps=20):
     for _ in range(max(2, reps // 4)):
         tp.shard_mlp(X, *full, H1, Y1)
     T.cuda.synchronize()
+    log("profile phases done")
+
+
+def onebyte_ranks(T, kind):
+    """8 seeded TP=8 Llama MLP rank shares stored one byte per weight with one
+    fp32 scale per row: finite E4M3 codes with random signs (no 0x7F / 0xFF)
+    for "fp8", signed int8 codes for "int8"."""
+    Fl = F // TP
+    gen = T.Generator(device="cuda")
+    gen.manual_seed(8 if kind == "fp8" else 9)
+
+    def codes(n, k):
+        if kind == "int8":
+            return T.randint(-128, 128, (n, k), generator=gen, device="cuda",
+                             dtype=T.int32).to(T.int8)
+        c = T.randint(0, 0x7F, (n, k), generator=gen, device="cuda", dtype=T.int32)
+        c |= T.randint(0, 2, (n, k), generator=gen, device="cuda", dtype=T.int32) << 7
+        return c.to(T.uint8)
+
+    def scales(n):
+        return T.rand((n,), generator=gen, device="cuda") * 1e-3 + 1e-4
+
+    return [tuple((codes(n, k), scales(n)) for n, k in ((Fl, D), (Fl, D), (D, Fl)))
+            for _ in range(TP)]
+
+
+DECODE_PROFILE_I = (1, 8, 32)
+
+
+def decode_profile(torch, tp, layer, reps=16):
+    """For rocprofv3: the TP=8 rank's MLP at 1, 8 and 32 tokens with bf16,
+    FP8 and int8 weights, each in a phase of its own (reps calls rotating the
+    8 rank shares), so each kernel's dispatches can be told apart by order."""
+    T = torch
+    Fl = F // TP
+    phases = [("bf16", tp.shard_mlp, [R["mlp"] for R in layer.ranks])]
+    phases += [(kind, call, onebyte_ranks(T, kind))
+               for kind, call in (("fp8", tp.shard_mlp_fp8), ("int8", tp.shard_mlp_int8))]
+    for kind, call, ranks in phases:
+        for I in DECODE_PROFILE_I:
+            X = to_dev(T, datagen.gaussian("X", (I, D), 1.0, "bf16", 1300 + I))
+            H = T.empty((I, Fl), dtype=T.bfloat16, device="cuda")
+            P = T.empty((I, D), dtype=T.float32, device="cuda")
+            log(f"profile phase: {kind} MLP I={I}")
+            for k in range(reps):
+                call(X, *ranks[k % TP], H, P)
+            T.cuda.synchronize()
     log("profile phases done")
 
 
@@ -509,51 +559,24 @@ def detail(torch, tp, layer, calls):
             TFLOPs=round(m.flops() / (st["median_us"] * 1e-6) / 1e12, 1),
             tokens_per_s=round(I / (st["median_us"] * 1e-6)))
     # the same rank shares with weight-only FP8 storage (E4M3 codes + one fp32
-    # scale per row): 8 seeded random shares, one byte per weight
+    # scale per row), then with int8 storage (signed codes + one fp32 scale per
+    # row): 8 seeded random shares each, one byte per weight
     Fl = F // TP
-    gen = T.Generator(device="cuda")
-    gen.manual_seed(8)
-
-    def codes(n, k):  # finite E4M3 codes with random signs (no 0x7F / 0xFF)
-        c = T.randint(0, 0x7F, (n, k), generator=gen, device="cuda", dtype=T.int32)
-        c |= T.randint(0, 2, (n, k), generator=gen, device="cuda", dtype=T.int32) << 7
-        return c.to(T.uint8)
-
-    def scales(n):
-        return T.rand((n,), generator=gen, device="cuda") * 1e-3 + 1e-4
-
-    fp8_ranks = [((codes(Fl, D), scales(Fl)), (codes(Fl, D), scales(Fl)),
-                  (codes(D, Fl), scales(D))) for _ in range(TP)]
-    for I in (1, 8, 32):
-        X = to_dev(T, datagen.gaussian("X", (I, D), 1.0, "bf16", 1100 + I))
-        H = T.empty((I, Fl), dtype=T.bfloat16, device="cuda")
-        P = T.empty((I, D), dtype=T.float32, device="cuda")
-        fns = [(lambda w=w: tp.shard_mlp_fp8(X, *w, H, P)) for w in fp8_ranks]
-        st = stats(time_calls(T, fns, calls))
-        nbytes = 3 * D * Fl + 4 * (2 * Fl + D) + 2 * I * D + 4 * I * D
-        gbs = nbytes / (st["median_us"] * 1e-6) / 1e9
-        log(f"FP8 MLP TP=8 decode I={I}: {st['median_us']} us")
-        out[f"llama70b_mlp_fp8_tp8_decode_I{I}"] = dict(
-            **st, bytes_per_call=nbytes, GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM, 3),
-            tokens_per_s=round(I / (st["median_us"] * 1e-6)))
-    del fp8_ranks
-    # and with weight-only int8 storage (signed codes + one fp32 scale per row)
-    i8_ranks = [tuple((T.randint(-128, 128, shp, generator=gen, device="cuda",
-                                 dtype=T.int32).to(T.int8), scales(shp[0]))
-                      for shp in ((Fl, D), (Fl, D), (D, Fl))) for _ in range(TP)]
-    for I in (1, 8, 32):
-        X = to_dev(T, datagen.gaussian("X", (I, D), 1.0, "bf16", 1200 + I))
-        H = T.empty((I, Fl), dtype=T.bfloat16, device="cuda")
-        P = T.empty((I, D), dtype=T.float32, device="cuda")
-        fns = [(lambda w=w: tp.shard_mlp_int8(X, *w, H, P)) for w in i8_ranks]
-        st = stats(time_calls(T, fns, calls))
-        nbytes = 3 * D * Fl + 4 * (2 * Fl + D) + 2 * I * D + 4 * I * D
-        gbs = nbytes / (st["median_us"] * 1e-6) / 1e9
-        log(f"int8 MLP TP=8 decode I={I}: {st['median_us']} us")
-        out[f"llama70b_mlp_int8_tp8_decode_I{I}"] = dict(
-            **st, bytes_per_call=nbytes, GBps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM, 3),
-            tokens_per_s=round(I / (st["median_us"] * 1e-6)))
-    del i8_ranks
+    for kind, call, seed in (("fp8", tp.shard_mlp_fp8, 1100), ("int8", tp.shard_mlp_int8, 1200)):
+        ranks = onebyte_ranks(T, kind)
+        for I in (1, 8, 32):
+            X = to_dev(T, datagen.gaussian("X", (I, D), 1.0, "bf16", seed + I))
+            H = T.empty((I, Fl), dtype=T.bfloat16, device="cuda")
+            P = T.empty((I, D), dtype=T.float32, device="cuda")
+            fns = [(lambda w=w: call(X, *w, H, P)) for w in ranks]
+            st = stats(time_calls(T, fns, calls))
+            nbytes = 3 * D * Fl + 4 * (2 * Fl + D) + 2 * I * D + 4 * I * D
+            gbs = nbytes / (st["median_us"] * 1e-6) / 1e9
+            log(f"{'FP8' if kind == 'fp8' else 'int8'} MLP TP=8 decode I={I}: {st['median_us']} us")
+            out[f"llama70b_mlp_{kind}_tp8_decode_I{I}"] = dict(
+                **st, bytes_per_call=nbytes, GBps=round(gbs, 1),
+                frac_hbm=round(gbs / PEAK_HBM, 3), tokens_per_s=round(I / (st["median_us"] * 1e-6)))
+        del ranks
     # the attention projections of the layer's rank shares at decode 32
     I = 32
     nql, nkl = NQ // TP, NKV // TP
@@ -803,6 +826,9 @@ def main():
         return
     if args.prefill_profile:
         prefill_profile(torch, tp, layer)
+        return
+    if args.decode_profile:
+        decode_profile(torch, tp, layer)
         return
     Xh = datagen.gaussian("X", (I, D), 1.0, "bf16", 42)
     X = to_dev(torch, Xh)
