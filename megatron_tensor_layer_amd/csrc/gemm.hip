@@ -1,7 +1,7 @@
 // Projections for many tokens: C[M, N] = A[M, K] . W[N, K]^T on bf16 MFMA
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulation), in three tile shapes chosen
-// per call by a cost model: 128 x 128 (described here), 256 x 256 and 256 x
-// 128 (described at their kernels below).
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation), in two tile shapes chosen
+// per call by a cost model: 128 x 128 (described here) and 256 x 128
+// (described at its kernel below).
 //
 // Prefill and large decode batches are the compute-heavy side of the layer
 // (lecture "Distributed Serving", §3.4: 2·B·D·F/n FLOPs per rank); the kernel
@@ -183,7 +183,7 @@ __device__ __forceinline__ void finish_splits(const __amdgpu_buffer_rsrc_t pr, i
   }
 }
 
-// One launch: grid = tiles * ns workgroups of 512 threads, 128 KB static LDS.
+// One launch: grid = tiles * ns workgroups of 512 threads, 160 KB of static LDS.
 //   KR: K elements per split (multiple of BK); ns = ceil(K / KR).
 //   counters/part: split-K workspace (unused when ns == 1).
 template <int EPI>
@@ -378,275 +378,6 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
   }
 }
 
-// ---------------------------------------------------------------- 256 x 256
-// The same product with 256 x 256 workgroup tiles for many tokens (M >= 384):
-// per K element a CU copies 2 x 256 rows for 2 x 256 x 256 FLOPs, twice the
-// FLOPs per copied byte of the 128 x 128 tile.  At these shapes the global
-// -> LDS copy stream of a CU runs at about 24-26 B/clk however deep the
-// pipeline (the L1's misses in flight over their latency), which caps a
-// 128 x 128 tile near 41 % of MFMA peak and a 256 x 256 tile near 75 %.
-//   * eight waves in a 2 x 4 grid of 128 x 64 wave tiles (4 x 2 MFMA
-//     fragments, 128 fp32 accumulators per lane), no K groups;
-//   * K stages of 32 (64-byte tile rows, 32 KB per stage), five stages (all
-//     160 KB of LDS), four in flight; 16-byte chunk c of row r sits in slot
-//     c ^ ((r / 4) % 4), so each 16-lane phase of an operand read covers all
-//     64 banks once;
-//   * SwiGLU: the W tile is 128 gate rows then the same 128 up rows, and
-//     each wave holds 32 gate and the matching 32 up columns;
-//   * split K and the XCD-aware order as in the 128 x 128 kernel.
-constexpr int BB = 256;                          // tile rows of A and of W
-constexpr int BKB = 32;                          // K per stage
-constexpr int kRowBB = BKB * 2;                  // 64-byte tile rows
-constexpr int kStageBA = BB * kRowBB;            // 16 KB
-constexpr int kStageB = 2 * kStageBA;            // 32 KB
-constexpr int SB = 5;
-constexpr int kLdsB = SB * kStageB;              // 160 KB
-
-__device__ __forceinline__ int lds_off64(int row, int chunk) {
-  return row * kRowBB + ((chunk ^ ((row >> 2) & 3)) << 4);
-}
-
-// NWB waves: 8 in a 2 x 4 grid of 128 x 64 wave tiles (used), or 4 in a
-// 2 x 2 grid of 128 x 128 -- a third fewer LDS bytes per MFMA at one wave per
-// SIMD, but measured 3-4 % slower at 512 tokens (TP=1 gate/up 605 us
-// against 582), so only the 8-wave form is launched.
-template <int EPI, int NWB>
-__global__ void __launch_bounds__(NWB * 64)
-gemm_big_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
-                const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
-                void* __restrict__ out, int64_t ldo, int KR, unsigned* __restrict__ counters,
-                float* __restrict__ part) {
-  // S stages of (A tile, W tile); after the K loop the first word holds the
-  // split-K arrival flag
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsB];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int WNW = NWB / 2;              // waves along N
-  constexpr int NF = 8 / WNW;               // 32-column fragments per wave: 2 or 4
-  constexpr int kInstB = 32 / NWB;          // copy instructions per wave per stage
-  constexpr int kThr = NWB * 64;
-  const int wm = wave / WNW, wn = wave % WNW;
-
-  const int mt_n = (M + BB - 1) / BB;
-  constexpr int kCols = (EPI == EPI_SWIGLU) ? BB / 2 : BB;  // output columns per tile
-  const int nt_n = (N + kCols - 1) / kCols;
-  const int tiles = mt_n * nt_n;
-  const int ns = (K + KR - 1) / KR;
-  const int G = tiles * ns;
-  int b = blockIdx.x;
-  const int G8 = G & ~7;
-  if (b < G8) b = (b & 7) * (G8 >> 3) + (b >> 3);
-  const int split = b / tiles;
-  const int tile = b % tiles;
-  const int tm = tile % mt_n, tn = tile / mt_n;
-  const int m0 = tm * BB, c0 = tn * kCols;
-  const int kb = split * KR, ke = min(K, kb + KR);
-
-  const u32x4_t ra = rsrc_words(A + (int64_t)m0 * lda, (uint32_t)min(BB, M - m0) * (uint32_t)lda * 2u);
-  const int wrows = min(kCols, N - c0);
-  const u32x4_t rw0 = rsrc_words(W0 + (int64_t)c0 * K, (uint32_t)wrows * (uint32_t)K * 2u);
-  const u32x4_t rw1 = rsrc_words((EPI == EPI_SWIGLU ? W1 : W0) + (int64_t)c0 * K,
-                                 (uint32_t)wrows * (uint32_t)K * 2u);
-
-  // Stage st into buffer buf: 32 instructions of 1 KB (16 tile rows each),
-  // 16 for A then 16 for W; wave w issues instructions w, w + NWB, ...
-  // Lane l fills slot l % 4 of row 16 q + l / 4 with the logical chunk that
-  // lds_off64 places there.
-  const int rr = lane >> 2, sl = lane & 3;
-  const uint32_t lsm = lds_addr(smem);
-  auto issue = [&](int st, int buf) {
-    const uint32_t la = lsm + buf * kStageB;
-    const int k0 = kb + st * BKB;
-#pragma unroll
-    for (int h = 0; h < kInstB; ++h) {
-      const int q = wave + h * NWB;           // 0..31; q < 16: A rows, else W rows
-      const int r = (q & 15) * 16 + rr;       // row in its 256-row tile
-      const int c = sl ^ ((r >> 2) & 3);
-      const int k = k0 + c * 8;
-      const bool kin = k < ke;
-      if (h < kInstB / 2) {
-        const uint32_t oa = (kin && m0 + r < M) ? (uint32_t)r * (uint32_t)lda * 2u + (uint32_t)k * 2u
-                                                : kOob;
-        lds_dma16(ra, oa, la + q * 1024);
-      } else {
-        const int wr = (EPI == EPI_SWIGLU) ? (r & 127) : r;
-        const uint32_t ow = (kin && wr < wrows) ? (uint32_t)wr * (uint32_t)K * 2u + (uint32_t)k * 2u
-                                                : kOob;
-        lds_dma16((EPI == EPI_SWIGLU && r >= 128) ? rw1 : rw0, ow, la + q * 1024);
-      }
-    }
-  };
-
-  // W tile rows of this wave's fragments.  SwiGLU: the first NF/2 are gate
-  // rows of F = c0 + wn (128/WNW) + 32 j + lane%32, the last NF/2 the up
-  // rows of the same F.
-  int brow[NF];
-#pragma unroll
-  for (int j = 0; j < NF; ++j) {
-    if constexpr (EPI == EPI_SWIGLU)
-      brow[j] = (j < NF / 2 ? 0 : 128) + wn * (128 / WNW) + (j % (NF / 2)) * 32;
-    else
-      brow[j] = wn * (256 / WNW) + j * 32;
-  }
-
-  f32x16_t acc[4][NF];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NF; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  // Operands of one 16-wide K step (ks) of a stage, read one step ahead of
-  // the MFMAs that use them.
-  bf16x8_t af[2][4], bw[2][NF];
-  auto read_ops = [&](int buf, int ks, bf16x8_t (&a)[4], bf16x8_t (&w)[NF]) {
-    const unsigned char* sa = smem + buf * kStageB;
-    const unsigned char* sb = sa + kStageBA;
-    const int c = ks * 2 + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const bf16x8_t*>(sa + lds_off64(wm * 128 + i * 32 + (lane & 31), c));
-#pragma unroll
-    for (int j = 0; j < NF; ++j)
-      w[j] = *reinterpret_cast<const bf16x8_t*>(sb + lds_off64(brow[j] + (lane & 31), c));
-  };
-  auto mfmas = [&](const bf16x8_t (&a)[4], const bf16x8_t (&w)[NF]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < NF; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], w[j], acc[i][j], 0, 0, 0);
-  };
-
-  // All SB buffers hold stages in flight: stage kt + SB is copied into the
-  // buffer of stage kt once every wave has its last operands of stage kt in
-  // registers.  The barrier sits between the two K steps' MFMAs of a stage:
-  // the pipe drains the first step's MFMAs while the waves meet, and the
-  // second step's run while the next stage's first operands are read.
-  const int NT = (ke - kb + BKB - 1) / BKB;
-#pragma unroll
-  for (int st = 0; st < SB; ++st)
-    if (st < NT) issue(st, st);
-  if (NT >= SB)
-    wait_vmcnt<(SB - 1) * kInstB>();  // stage 0 has landed
-  else
-    wait_vmcnt<0>();
-  __syncthreads();
-  read_ops(0, 0, af[0], bw[0]);
-  int buf = 0;  // kt % SB
-  // The two K steps of stage kt: the next step's 4 + NF operand reads are
-  // issued ahead of the current step's 4 NF MFMAs (the scheduler is held to
-  // that order).
-  auto first_half = [&]() {
-    read_ops(buf, 1, af[1], bw[1]);
-    mfmas(af[0], bw[0]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 + NF, 0);  // DS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NF, 0);  // MFMA
-    __builtin_amdgcn_sched_barrier(0);                  // nothing moves past here
-  };
-  auto second_half = [&]() {
-    buf = buf == SB - 1 ? 0 : buf + 1;
-    read_ops(buf, 0, af[0], bw[0]);
-    mfmas(af[1], bw[1]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 + NF, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NF, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  int kt = 0;
-  // steady state: stage kt + 1 has landed once the SB - 2 stages after it
-  // are the only ones in flight; stage kt + SB refills stage kt's buffer
-  for (; kt < NT - SB; ++kt) {
-    first_half();
-    wait_vmcnt<(SB - 2) * kInstB>();
-    wait_lgkmcnt0();  // this wave's reads of stage kt are in registers
-    __syncthreads();  // everyone's have; stage kt + 1 is in LDS
-    if constexpr (EPI == EPI_SWIGLU) {
-      // refill after the second half's MFMAs: TP=1 gate/up 547-551 -> 527-537
-      // us on one box; the fp32 down product measured 5 % slower this way
-      const int ib = buf;
-      second_half();
-      issue(kt + SB, ib);
-    } else {
-      issue(kt + SB, buf);
-      second_half();
-    }
-  }
-  // the last stages: nothing more to copy
-  for (; kt < NT - 1; ++kt) {
-    first_half();
-    if (kt + SB - 1 < NT)
-      wait_vmcnt<(SB - 2) * kInstB>();
-    else
-      wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    __syncthreads();
-    second_half();
-  }
-  read_ops(buf, 1, af[1], bw[1]);
-  mfmas(af[0], bw[0]);
-  mfmas(af[1], bw[1]);
-
-  if (ns == 1) {
-    if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-      for (int j = 0; j < NF / 2; ++j) {
-        const int col = c0 + wn * (128 / WNW) + j * 32 + (lane & 31);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = m0 + wm * 128 + i * 32 + acc_row32(r, lane);
-            if (m < M && col < N)
-              store_out<EPI_DT>(out, ldo, m, col, silu(acc[i][j][r]) * acc[i][j + NF / 2][r]);
-          }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NF; ++j) {
-          const int col = c0 + wn * (256 / WNW) + j * 32 + (lane & 31);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = m0 + wm * 128 + i * 32 + acc_row32(r, lane);
-            if (m < M && col < N) store_out<EPI>(out, ldo, m, col, acc[i][j][r]);
-          }
-        }
-    }
-    return;
-  }
-
-  // ---- split K: partial tile [BB][BB] in W-tile row order, then arrival
-  const int64_t tile_elems = (int64_t)BB * BB;
-  const __amdgpu_buffer_rsrc_t pr =
-      make_rsrc(part, (uint32_t)((int64_t)ns * tiles * tile_elems * 4));
-  const int64_t tbase = (int64_t)tile * tile_elems;
-  const int64_t plane = (int64_t)tiles * tile_elems;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NF; ++j) {
-      const int tc = brow[j] + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tr = wm * 128 + i * 32 + acc_row32(r, lane);
-        const float v = acc[i][j][r];
-        __builtin_amdgcn_raw_buffer_store_b32(
-            __builtin_bit_cast(uint32_t, v), pr,
-            (uint32_t)((split * plane + tbase + tr * BB + tc) * 4), 0, kAuxSys);
-      }
-    }
-  int* is_last = reinterpret_cast<int*>(smem);  // the stages are consumed
-  wait_vmcnt<0>();  // partial stores have reached memory
-  __syncthreads();
-  if (tid == 0) *is_last = arrive_last(counters + tile, (unsigned)ns);
-  __syncthreads();
-  if (!*is_last) return;
-  finish_splits<EPI, BB, BB, kThr, 4>(pr, tbase, plane, ns, m0, c0, M, N, out, ldo, tid, -1,
-                                      nullptr, nullptr);
-}
-
 // ---------------------------------------------------------------- 256 x 128
 // The same product with 256 x 128 workgroup tiles (256 activation rows, 128
 // weight rows): per K element a CU copies 384 rows for 2 x 256 x 128 FLOPs, a
@@ -656,58 +387,36 @@ gemm_big_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda
 // to fill the chip.
 //   * eight waves: a 2 x 2 grid of 128 x 64 wave tiles (4 x 2 MFMA
 //     fragments, 128 fp32 accumulators per lane), twice -- the two groups of
-//     four waves take alternate halves of every stage's 16-wide K steps, so
-//     the LDS bytes read per MFMA are those of the 256 x 256 tile;
-//   * KB K per stage: 64 (128-byte tile rows, the 128 x 128 kernel's
-//     layout, three 48 KB stages, two in flight) or 32 (64-byte rows, the
-//     256 x 256 kernel's layout, six 24 KB stages, five in flight);
+//     four waves take alternate pairs of every stage's 16-wide K steps, so
+//     the LDS bytes read per MFMA are those of a 256 x 256 tile;
+//   * 64 K per stage in 128-byte tile rows (the 128 x 128 kernel's layout):
+//     three 48 KB stages, two in flight.  Stages of 32 K (64-byte rows, six
+//     24 KB stages) request each 128-byte line in two halves one stage apart
+//     and were much slower: the TP=1 MLP at 512 tokens took 927 us against
+//     723.  A 256 x 256 kernel with such rows (12.5 B/clk per CU) was
+//     replaced by this one;
 //   * after the K loop the second group's accumulators go to one row-major
 //     [256][128] fp32 tile in LDS and the first group adds its own in place,
 //     then the epilogue (or the split-K partial store) reads that tile;
 //   * SwiGLU, split K and the XCD-aware order as in the 128 x 128 kernel.
-constexpr int WM = 256, WN = 128;
+constexpr int WM = 256, WN = 128, WK = 64;
+constexpr int kRowW = WK * 2;                 // 128-byte tile rows
+constexpr int kStageWA = WM * kRowW;          // 32 KB
+constexpr int kStageW = (WM + WN) * kRowW;    // 48 KB
+constexpr int SW = 3;                         // stages
+constexpr int kLdsW = SW * kStageW;           // 144 KB
+constexpr int kInstWA = WM / 8 / 8;           // A copy instructions per wave and stage (8 rows each)
+constexpr int kInstWW = WN / 8 / 8;           // W copy instructions per wave and stage
+constexpr int kInstW = kInstWA + kInstWW;
+static_assert(WM * WN * 4 + 4 <= kLdsW, "the K-group tile and the arrival flag fit");
 
-template <int KB>
-struct WideCfg {
-  static constexpr int kRow = KB * 2;               // bytes per LDS tile row
-  static constexpr int kRowsPerInst = 1024 / kRow;  // tile rows one 1 KB copy fills
-  static constexpr int kLanesPerRow = kRow / 16;
-  static constexpr int kStageA = WM * kRow;
-  static constexpr int kStage = (WM + WN) * kRow;   // 24 KB or 48 KB
-  static constexpr int kS = KB == 64 ? 3 : 6;       // stages
-  static constexpr int kLds = kS * kStage;          // 144 KB
-  static constexpr int kInstA = WM / kRowsPerInst / 8;  // per wave and stage
-  static constexpr int kInstW = WN / kRowsPerInst / 8;
-  static constexpr int kInst = kInstA + kInstW;
-  static constexpr int kStepsPerGroup = KB / 32;    // 16-wide K steps of a group per stage
-  // byte offset of (row, logical 16-byte chunk): chunk c of row r sits in slot
-  // c ^ ((r / 2) % 8) (128-byte rows) or c ^ ((r / 4) % 4) (64-byte rows), so
-  // the 32 rows of one operand read cover all 64 banks
-  static __device__ __forceinline__ int off(int row, int chunk) {
-    if constexpr (KB == 64)
-      return row * kRow + ((chunk ^ ((row >> 1) & 7)) << 4);
-    else
-      return row * kRow + ((chunk ^ ((row >> 2) & 3)) << 4);
-  }
-  static __device__ __forceinline__ int slot_chunk(int row, int slot) {
-    if constexpr (KB == 64)
-      return slot ^ ((row >> 1) & 7);
-    else
-      return slot ^ ((row >> 2) & 3);
-  }
-  static_assert(WM * WN * 4 + 4 <= kLds, "the K-group tile and the arrival flag fit");
-  static_assert(kInstA * 8 * kRowsPerInst == WM && kInstW * 8 * kRowsPerInst == WN,
-                "whole copy instructions per wave");
-};
-
-template <int EPI, int KB>
+template <int EPI>
 __global__ void __launch_bounds__(kThreads)
 gemm_wide_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
                  const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
                  void* __restrict__ out, int64_t ldo, int KR, unsigned* __restrict__ counters,
                  float* __restrict__ part) {
-  using C = WideCfg<KB>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLds];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsW];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = wave >> 2;  // K group
@@ -734,35 +443,34 @@ gemm_wide_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t ld
   const u32x4_t rw1 = rsrc_words((EPI == EPI_SWIGLU ? W1 : W0) + (int64_t)c0 * K,
                                  (uint32_t)wrows * (uint32_t)K * 2u);
 
-  // Stage st into buffer buf: 1 KB copy instructions, first the A rows, then
-  // the W rows; wave w issues A instructions w, w + 8, ... and W instructions
-  // likewise.  Lane l fills slot l % kLanesPerRow of row
-  // kRowsPerInst q + l / kLanesPerRow with the logical chunk that C::off
-  // places there; past the K range, M or N the offset is out of range and
-  // the slot is zero-filled.
-  const int rr = lane / C::kLanesPerRow, sl = lane % C::kLanesPerRow;
+  // Stage st into buffer buf: 1 KB copy instructions of 8 tile rows, first
+  // the A rows, then the W rows; wave w issues A instructions w, w + 8, ...
+  // and W instructions likewise.  Lane l fills slot l % 8 of row 8 q + l / 8
+  // with the logical chunk that lds_off places there; past the K range, M or
+  // N the offset is out of range and the slot is zero-filled.
+  const int rr = lane >> 3, sl = lane & 7;
   const uint32_t lsm = lds_addr(smem);
   auto issue = [&](int st, int buf) {
-    const uint32_t la = lsm + buf * C::kStage;
-    const int k0 = kb + st * KB;
+    const uint32_t la = lsm + buf * kStageW;
+    const int k0 = kb + st * WK;
 #pragma unroll
-    for (int h = 0; h < C::kInstA; ++h) {
+    for (int h = 0; h < kInstWA; ++h) {
       const int q = wave + h * 8;
-      const int r = q * C::kRowsPerInst + rr;
-      const int k = k0 + C::slot_chunk(r, sl) * 8;
+      const int r = q * 8 + rr;
+      const int k = k0 + (sl ^ ((r >> 1) & 7)) * 8;
       const uint32_t oa = (k < ke && m0 + r < M) ? (uint32_t)r * (uint32_t)lda * 2u + (uint32_t)k * 2u
                                                  : kOob;
       lds_dma16(ra, oa, la + q * 1024);
     }
 #pragma unroll
-    for (int h = 0; h < C::kInstW; ++h) {
+    for (int h = 0; h < kInstWW; ++h) {
       const int q = wave + h * 8;
-      const int r = q * C::kRowsPerInst + rr;  // W tile row
-      const int k = k0 + C::slot_chunk(r, sl) * 8;
+      const int r = q * 8 + rr;  // W tile row
+      const int k = k0 + (sl ^ ((r >> 1) & 7)) * 8;
       const int wr = (EPI == EPI_SWIGLU) ? (r & 63) : r;  // SwiGLU: 64 gate rows, then 64 up
       const uint32_t ow = (k < ke && wr < wrows) ? (uint32_t)wr * (uint32_t)K * 2u + (uint32_t)k * 2u
                                                  : kOob;
-      lds_dma16((EPI == EPI_SWIGLU && r >= 64) ? rw1 : rw0, ow, la + C::kStageA + q * 1024);
+      lds_dma16((EPI == EPI_SWIGLU && r >= 64) ? rw1 : rw0, ow, la + kStageWA + q * 1024);
     }
   };
 
@@ -784,26 +492,26 @@ gemm_wide_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t ld
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int NT = (ke - kb + KB - 1) / KB;
+  const int NT = (ke - kb + WK - 1) / WK;
 #pragma unroll
-  for (int st = 0; st < C::kS - 1; ++st) issue(st, st);
+  for (int st = 0; st < SW - 1; ++st) issue(st, st);
 
-  int buf = 0;  // kt % kS
+  int buf = 0;  // kt % SW
   for (int kt = 0; kt < NT; ++kt) {
-    wait_vmcnt<(C::kS - 2) * C::kInst>();  // this wave's part of stage kt has landed
-    __syncthreads();                       // everyone's has; stage kt - 1 is consumed
-    const unsigned char* sa = smem + buf * C::kStage;
-    const unsigned char* sb = sa + C::kStageA;
+    wait_vmcnt<(SW - 2) * kInstW>();  // this wave's part of stage kt has landed
+    __syncthreads();                  // everyone's has; stage kt - 1 is consumed
+    const unsigned char* sa = smem + buf * kStageW;
+    const unsigned char* sb = sa + kStageWA;
 #pragma unroll
-    for (int h = 0; h < C::kStepsPerGroup; ++h) {
-      const int c = (g * C::kStepsPerGroup + h) * 2 + (lane >> 5);  // 16-byte chunk
+    for (int h = 0; h < 2; ++h) {
+      const int c = (2 * g + h) * 2 + (lane >> 5);  // 16-wide K step 2g + h
       bf16x8_t af[4], bw[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + C::off(wm * 128 + i * 32 + (lane & 31), c));
+        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + lds_off(wm * 128 + i * 32 + (lane & 31), c));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        bw[j] = *reinterpret_cast<const bf16x8_t*>(sb + C::off(brow[j] + (lane & 31), c));
+        bw[j] = *reinterpret_cast<const bf16x8_t*>(sb + lds_off(brow[j] + (lane & 31), c));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -811,8 +519,9 @@ gemm_wide_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t ld
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bw[j], acc[i][j], 0, 0, 0);
     }
     // refill stage kt - 1's buffer after this stage's MFMAs are issued
-    issue(kt + C::kS - 1, buf == 0 ? C::kS - 1 : buf - 1);
-    buf = buf == C::kS - 1 ? 0 : buf + 1;
+    // (issuing it before them measured slower: the copy issue stalls them)
+    issue(kt + SW - 1, buf == 0 ? SW - 1 : buf - 1);
+    buf = buf == SW - 1 ? 0 : buf + 1;
   }
 
   wait_vmcnt<0>();  // zero-fill loads of stages past the end have landed
@@ -883,9 +592,7 @@ gemm_wide_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t ld
   }
 }
 
-constexpr int kWideKB = 64;  // K per stage of the launched 256 x 128 kernel
-
-enum Tile { kT128 = 0, kT256 = 1, kTWide = 2 };  // 128 x 128, 256 x 256, 256 x 128
+enum Tile { kT128 = 0, kTWide = 1 };  // 128 x 128, 256 x 128
 
 struct Plan {
   int shape = kT128;
@@ -902,14 +609,10 @@ struct TileShape {
 };
 
 // Measured on this chip at the prefill shapes with every CU busy: the 128 x
-// 128 kernel's copies run at about 21 B/clk per CU, the 256 x 128 kernel's at
-// about 19 and the 256 x 256 kernel's at 12.5.  The two 256-row kernels copy
-// the same bytes per FLOP from the weights; the 256 x 256 kernel's 64-byte
-// tile rows request each 128-byte line in two halves, one stage apart, and
-// the 256 x 128 kernel with such rows was as slow (TP=1 MLP at 512 tokens:
-// 927 us with 64-byte rows, 723 with 128-byte rows, 751 on 256 x 256 tiles).
-constexpr TileShape kShapes[3] = {
-    {BM, BN, BK, 21.0}, {BB, BB, BKB, 12.5}, {WM, WN, kWideKB, 19.0}};
+// 128 kernel's copies run at about 21 B/clk per CU next to its MFMA work,
+// the 256 x 128 kernel's at about 19.
+constexpr int kNumShapes = 2;
+constexpr TileShape kShapes[kNumShapes] = {{BM, BN, BK, 21.0}, {WM, WN, WK, 19.0}};
 
 // Cost model (CU cycles) for a tile shape and split count.  A workgroup's
 // main loop runs at the rate its copy stream reaches next to the MFMA work,
@@ -935,13 +638,13 @@ double plan_cost(int tiles, int ns, int shape, int K) {
 // Split K when the tiles alone leave CUs idle: the tile shape and split
 // count of least modelled cost; at least 8 stages of 64 K per split, at
 // most 256 MB of partials and one arrival counter per tile.  The 256-row
-// shapes need M >= 384 (enough rows to fill most of a tile).
+// shape needs M >= 384 (enough rows to fill most of a tile).
 constexpr double kMaxPartialBytes = 256.0 * 1024 * 1024;
 Plan make_plan(int M, int N, int K, bool swiglu) {
   Plan best_pl;
   double best = 1e300;
   const int max_ns = std::max(1, std::min(16, (K + BK - 1) / BK / 8));
-  for (int shape = 0; shape < 3; ++shape) {
+  for (int shape = 0; shape < kNumShapes; ++shape) {
     const TileShape& t = kShapes[shape];
     if (t.bm > BM && M < 384) continue;
     const int cols = swiglu ? t.bn / 2 : t.bn;
@@ -977,9 +680,7 @@ template <int EPI>
 hipError_t launch_plan(const Plan& pl, int M, int N, int K, const uint16_t* A, int64_t lda,
                        const uint16_t* W0, const uint16_t* W1, void* out, int64_t ldo,
                        void* workspace, hipStream_t stream) {
-  auto kern = pl.shape == kT256 ? gemm_big_kernel<EPI, 8>
-              : pl.shape == kTWide ? gemm_wide_kernel<EPI, kWideKB>
-                                   : gemm_kernel<EPI>;
+  auto kern = pl.shape == kTWide ? gemm_wide_kernel<EPI> : gemm_kernel<EPI>;
   unsigned* counters = nullptr;
   float* part = nullptr;
   if (pl.ns > 1) {
