@@ -37,7 +37,8 @@ The printed JSON line also carries
                 the layer at prefill 512, the partial reduce, the residual
                 update + RMSNorm after a block, the layer as a pre-norm block
                 with those at decode 32, the MLP with weight-only FP8
-                storage at decode 1, 8 and 32, the same with int8 storage,
+                storage at 1, 8, 32, 128 and 512 tokens, the same with int8
+                storage,
                 and decode attention over a
                 rank's KV cache); calls rotating over weight sets are timed
                 in groups of back-to-back calls, one per set, with one event
@@ -82,8 +83,8 @@ def parse():
                     help="for rocprofv3: each 512-token prefill projection of a TP=8 rank "
                          "(MLP, QKV, o_proj) and the TP=1 MLP in phases of its own, no timing")
     ap.add_argument("--decode-profile", action="store_true",
-                    help="for rocprofv3: the TP=8 rank's MLP at 1, 8 and 32 tokens with bf16, "
-                         "FP8 and int8 weights, each in a phase of its own, no timing")
+                    help="for rocprofv3: the TP=8 rank's MLP at 1, 8, 32, 128 and 512 tokens "
+                         "with bf16, FP8 and int8 weights, each in a phase of its own, no timing")
     ap.add_argument("--ingest-prefill-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the FETCH_SIZE and WRITE_SIZE passes over --prefill-profile "
                          "into the 512-token MLP entry of profiles/traffic.json")
@@ -290,13 +291,14 @@ def onebyte_ranks(T, kind):
             for _ in range(TP)]
 
 
-DECODE_PROFILE_I = (1, 8, 32)
+DECODE_PROFILE_I = (1, 8, 32, 128, 512)
 
 
 def decode_profile(torch, tp, layer, reps=16):
-    """For rocprofv3: the TP=8 rank's MLP at 1, 8 and 32 tokens with bf16,
-    FP8 and int8 weights, each in a phase of its own (reps calls rotating the
-    8 rank shares), so each kernel's dispatches can be told apart by order."""
+    """For rocprofv3: the TP=8 rank's MLP at 1, 8, 32, 128 and 512 tokens
+    with bf16, FP8 and int8 weights, each in a phase of its own (reps calls
+    rotating the 8 rank shares), so each kernel's dispatches can be told
+    apart by order."""
     T = torch
     Fl = F // TP
     phases = [("bf16", tp.shard_mlp, [R["mlp"] for R in layer.ranks])]
@@ -564,7 +566,7 @@ def detail(torch, tp, layer, calls):
     Fl = F // TP
     for kind, call, seed in (("fp8", tp.shard_mlp_fp8, 1100), ("int8", tp.shard_mlp_int8, 1200)):
         ranks = onebyte_ranks(T, kind)
-        for I in (1, 8, 32):
+        for I in (1, 8, 32, 128, 512):
             X = to_dev(T, datagen.gaussian("X", (I, D), 1.0, "bf16", seed + I))
             H = T.empty((I, Fl), dtype=T.bfloat16, device="cuda")
             P = T.empty((I, D), dtype=T.float32, device="cuda")
@@ -573,9 +575,12 @@ def detail(torch, tp, layer, calls):
             nbytes = 3 * D * Fl + 4 * (2 * Fl + D) + 2 * I * D + 4 * I * D
             gbs = nbytes / (st["median_us"] * 1e-6) / 1e9
             log(f"{'FP8' if kind == 'fp8' else 'int8'} MLP TP=8 decode I={I}: {st['median_us']} us")
-            out[f"llama70b_mlp_{kind}_tp8_decode_I{I}"] = dict(
+            m = wl.MlpShape(I, D, Fl)
+            tf = m.flops() / (st["median_us"] * 1e-6) / 1e12
+            out[f"llama70b_mlp_{kind}_tp8_{'decode' if I <= 256 else 'prefill'}_I{I}"] = dict(
                 **st, bytes_per_call=nbytes, GBps=round(gbs, 1),
-                frac_hbm=round(gbs / PEAK_HBM, 3), tokens_per_s=round(I / (st["median_us"] * 1e-6)))
+                frac_hbm=round(gbs / PEAK_HBM, 3), TFLOPs=round(tf, 1),
+                frac_mfma=round(tf / PEAK_BF16, 3), tokens_per_s=round(I / (st["median_us"] * 1e-6)))
         del ranks
     # the attention projections of the layer's rank shares at decode 32
     I = 32

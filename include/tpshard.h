@@ -103,7 +103,10 @@ size_t tp_shard_mlp_workspace_size(int64_t I, int64_t D, int64_t F_local, tp_dty
  *           undefined.  Two calls in flight at once (other streams) need
  *           separate workspaces.
  * Errors: TP_ERR_INVALID, TP_ERR_MISALIGNED (D or F_local not a multiple of 8,
- * a pointer not 16-byte aligned), TP_ERR_WORKSPACE, TP_ERR_LAUNCH.
+ * a pointer not 16-byte aligned), TP_ERR_UNSUPPORTED (fp32 with D or F_local
+ * above the few-token kernel's K range; a projection that falls on the MFMA
+ * GEMM with a contraction length above 2^22), TP_ERR_WORKSPACE,
+ * TP_ERR_LAUNCH.
  */
 tp_status_t tp_shard_mlp(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt,
                          const void* X, const void* W_gate, const void* W_up,
@@ -111,7 +114,7 @@ tp_status_t tp_shard_mlp(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * tp_shard_mlp with weight-only FP8 storage, for decode (1..64 tokens).  The
+ * tp_shard_mlp with weight-only FP8 storage, for any token count.  The
  * pages' cost frontier is FP8 throughout but they give no storage convention;
  * the one used here: every weight is one byte in the OCP E4M3 ("fn") encoding
  * (sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, 0x7F and
@@ -127,10 +130,12 @@ tp_status_t tp_shard_mlp(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt,
  *   W_down  [D, F_local]  E4M3 codes, s_down [D] fp32 (scales per output row)
  *   H       [I, F_local]  bf16 written; P [I, D] fp32 overwritten
  *   workspace as tp_shard_mlp: tp_shard_mlp_fp8_workspace_size bytes (0 for
- *           up to 4 tokens), counter area zero before first use, left zero
+ *           up to 4 tokens, and where the GEMM does not split K), counter
+ *           area zero before first use, left zero
  * D and F_local multiples of 16.  Up to 4 tokens (D, F_local at most 16384)
  * the weights stream through VALU dot products; 5..64 tokens (or larger K)
- * through the split-K MFMA kernel; otherwise TP_ERR_UNSUPPORTED.  Scales
+ * through the split-K MFMA kernel; more tokens through the one-byte MFMA
+ * GEMM (TP_ERR_UNSUPPORTED there for D or F_local above 2^22).  Scales
  * 4-byte aligned, every other pointer 16-byte aligned.
  * Errors: TP_ERR_INVALID, TP_ERR_MISALIGNED, TP_ERR_UNSUPPORTED,
  * TP_ERR_WORKSPACE, TP_ERR_LAUNCH.
@@ -211,8 +216,8 @@ tp_status_t tp_partial_reduce(int32_t t, int64_t n, const float* partials,
  * matrix carries one fp32 scale, W[n, k] = s[n] * c[n, k].  Activations, H
  * and P keep the dtypes of the bf16 path; the int8 values are exact in bf16,
  * so the products are those of the dequantized weights.  Arguments, shapes,
- * alignment, workspace, supported sizes (1..64 tokens) and errors as
- * tp_shard_mlp_fp8, with W_gate, W_up, W_down holding int8 codes.
+ * alignment, workspace, supported sizes and errors as tp_shard_mlp_fp8,
+ * with W_gate, W_up, W_down holding int8 codes.
  */
 size_t tp_shard_mlp_int8_workspace_size(int64_t I, int64_t D, int64_t F_local);
 tp_status_t tp_shard_mlp_int8(int64_t I, int64_t D, int64_t F_local, const void* X,

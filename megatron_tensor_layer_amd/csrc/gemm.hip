@@ -98,6 +98,15 @@ __device__ __forceinline__ void store_out4(void* out, int64_t ldo, int m, int co
   }
 }
 
+// Scales of output columns col .. col + n - 1 (n <= 4; the rest 0).
+__device__ __forceinline__ f32x4_t col_scales(const float* S, int col, int n) {
+  f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (e < n) v[e] = S[col + e];
+  return v;
+}
+
 // Split-K finish, run by the last of a tile's ns workgroups: the ns fp32
 // partial tiles (TM x TN, W-tile row order, plane `plane` apart; for SwiGLU
 // the up partial of column c sits at column c + TN / 2) are summed in split
@@ -111,12 +120,16 @@ __device__ __forceinline__ void store_out4(void* out, int64_t ldo, int m, int co
 // an out-of-range lane offset, splits past ns are not loaded.  When the
 // finishing workgroup's own partial is still in LDS (own >= 0: the sum of
 // the row-major tiles own0 and own1, or own0 alone when own1 is null), that
-// split is taken from there.
+// split is taken from there.  With one-byte weights, S0 (and S1, the up
+// rows') hold the fp32 scale of each output column, applied to the sums
+// before the epilogue.
 template <int EPI, int TM, int TN, int THREADS, int IQ>
 __device__ __forceinline__ void finish_splits(const __amdgpu_buffer_rsrc_t pr, int64_t tbase,
                                               int64_t plane, int ns, int m0, int c0, int M,
                                               int N, void* out, int64_t ldo, int tid, int own,
-                                              const f32x4_t* own0, const f32x4_t* own1) {
+                                              const f32x4_t* own0, const f32x4_t* own1,
+                                              const float* S0 = nullptr,
+                                              const float* S1 = nullptr) {
   constexpr int kNQ = (EPI == EPI_SWIGLU) ? 2 : 1;  // gate and up
   constexpr int kCols = TN / kNQ;                   // output columns of the tile
   constexpr int kQ = kCols / 4;                     // items per tile row
@@ -172,12 +185,14 @@ __device__ __forceinline__ void finish_splits(const __amdgpu_buffer_rsrc_t pr, i
     for (int i = 0; i < kIP; ++i) {
       const int m = m0 + tr[i];
       if (m >= M) continue;
+      const int n = min(4, N - (c0 + tc[i]));
       f32x4_t v = s[i][0];
+      if (S0) v *= col_scales(S0, c0 + tc[i], n);
       if constexpr (EPI == EPI_SWIGLU) {
-        const f32x4_t u = s[i][1];
+        f32x4_t u = s[i][1];
+        if (S1) u *= col_scales(S1, c0 + tc[i], n);
         v = f32x4_t{silu(v.x) * u.x, silu(v.y) * u.y, silu(v.z) * u.z, silu(v.w) * u.w};
       }
-      const int n = min(4, N - (c0 + tc[i]));
       store_out4<EPI == EPI_F32 ? EPI_F32 : EPI_DT>(out, ldo, m, c0 + tc[i], n, v);
     }
   }
@@ -592,6 +607,236 @@ gemm_wide_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t ld
   }
 }
 
+// ---------------------------------------------------------------- one-byte weights
+// The product with weight-only one-byte codes (OCP E4M3 or signed int8) and
+// one fp32 scale per weight row, bf16 activations, for more tokens than the
+// streaming kernels take: the 128 x 128 kernel's tiles, waves and K groups,
+// with 128 K per stage so that a stage's code rows are whole 128-byte lines
+// (activation rows are 256 bytes).  A weight tile then copies half the bytes
+// of its bf16 form: 48 KB per stage for 2 x 128 x 128 x 128 FLOPs, against
+// 64 KB.
+//   * three 48 KB stages, two in flight; activation rows are 16 chunks of 16
+//     bytes with chunk c of row r in slot c ^ (r % 16), code rows 8 chunks
+//     laid out as the 128 x 128 kernel's operand rows (c ^ ((r / 2) % 8)),
+//     so each 16-lane phase of an operand read covers all 64 banks once;
+//   * a lane reads one whole 16-code chunk and decodes it exactly to two
+//     8-element bf16 chunks (every E4M3 and int8 value is a bf16 value).
+//     The two feed two MFMAs: lane half h of chunk pair p takes code chunk
+//     2p + h, its low 8 codes in the first MFMA and its high 8 in the
+//     second, and reads the activations of the same K (chunks 4p + 2h and
+//     4p + 2h + 1 of its row) -- a fixed permutation of K within each MFMA,
+//     which leaves the sums' terms unchanged;
+//   * each output column's scale multiplies its sum in the epilogue (or in
+//     the split-K finish), before silu(g) * u.
+constexpr int QBK = 128;                         // K per stage
+constexpr int kRowQA = QBK * 2;                  // 256-byte activation rows
+constexpr int kRowQW = QBK;                      // 128-byte code rows
+constexpr int kStageQA = BM * kRowQA;            // 32 KB
+constexpr int kStageQ = kStageQA + BN * kRowQW;  // 48 KB
+constexpr int SQ = 3;                            // stages
+constexpr int kLdsQ = SQ * kStageQ;              // 144 KB
+constexpr int kInstQA = BM * kRowQA / 1024 / 8;  // activation copy instructions per wave and stage
+constexpr int kInstQW = BN * kRowQW / 1024 / 8;  // code copy instructions per wave and stage
+constexpr int kInstQ = kInstQA + kInstQW;
+static_assert(kRowQW == kRowB, "code rows use the 128 x 128 kernel's row layout");
+static_assert(2 * BM * BN * 4 + 4 <= kLdsQ, "both K groups' tiles and the arrival flag fit");
+
+__device__ __forceinline__ int lds_off_qa(int row, int chunk) {
+  return row * kRowQA + ((chunk ^ (row & 15)) << 4);
+}
+
+template <int EPI, int WF>
+__global__ void __launch_bounds__(kThreads)
+gemm_q8_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
+               const uint8_t* __restrict__ W0, const float* __restrict__ S0,
+               const uint8_t* __restrict__ W1, const float* __restrict__ S1,
+               void* __restrict__ out, int64_t ldo, int KR, unsigned* __restrict__ counters,
+               float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsQ];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wave >> 2;  // K group: chunk pairs 2g, 2g + 1 of each stage
+  const int wm = (wave >> 1) & 1, wn = wave & 1;
+
+  const int mt_n = (M + BM - 1) / BM;
+  constexpr int kCols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns per tile
+  const int nt_n = (N + kCols - 1) / kCols;
+  const int tiles = mt_n * nt_n;
+  const int ns = (K + KR - 1) / KR;
+  const int G = tiles * ns;
+  int b = blockIdx.x;
+  const int G8 = G & ~7;
+  if (b < G8) b = (b & 7) * (G8 >> 3) + (b >> 3);
+  const int split = b / tiles;
+  const int tile = b % tiles;
+  const int tm = tile % mt_n, tn = tile / mt_n;
+  const int m0 = tm * BM, c0 = tn * kCols;
+  const int kb = split * KR, ke = min(K, kb + KR);
+
+  const u32x4_t ra = rsrc_words(A + (int64_t)m0 * lda, (uint32_t)min(BM, M - m0) * (uint32_t)lda * 2u);
+  const int wrows = min(kCols, N - c0);
+  const u32x4_t rw0 = rsrc_words(W0 + (int64_t)c0 * K, (uint32_t)wrows * (uint32_t)K);
+  const u32x4_t rw1 = rsrc_words((EPI == EPI_SWIGLU ? W1 : W0) + (int64_t)c0 * K,
+                                 (uint32_t)wrows * (uint32_t)K);
+
+  // Stage st into buffer buf.  Activation copies: 4 rows x 256 bytes per 1 KB
+  // instruction, lane l filling slot l % 16 of row 4 q + l / 16; code copies:
+  // 8 rows x 128 bytes, lane l filling slot l % 8 of row 8 q + l / 8.  Each
+  // slot gets the logical chunk its layout places there; past the K range,
+  // M or N the offset is out of range and the slot is zero-filled.  With one
+  // M block and K a multiple of 2048 the stages start at tn % NT and wrap,
+  // as in the 128 x 128 kernel.
+  const uint32_t lsm = lds_addr(smem);
+  const int NT = (ke - kb + QBK - 1) / QBK;
+  const int rot = (mt_n == 1 && K % 2048 == 0) ? tn % NT : 0;
+  auto issue = [&](int st, int buf) {
+    const uint32_t la = lsm + buf * kStageQ, lb = la + kStageQA;
+    int sr = st + rot;  // stages past NT - 1 start at ke: zero-filled
+    if (sr >= NT) sr = st < NT ? sr - NT : NT;
+    const int k0 = kb + sr * QBK;
+#pragma unroll
+    for (int h = 0; h < kInstQA; ++h) {
+      const int q = wave + h * 8;
+      const int r = q * 4 + (lane >> 4);
+      const int k = k0 + ((lane & 15) ^ (r & 15)) * 8;
+      const uint32_t oa = (k < ke && m0 + r < M) ? (uint32_t)r * (uint32_t)lda * 2u + (uint32_t)k * 2u
+                                                 : kOob;
+      lds_dma16(ra, oa, la + q * 1024);
+    }
+#pragma unroll
+    for (int h = 0; h < kInstQW; ++h) {
+      const int q = wave + h * 8;
+      const int r = q * 8 + (lane >> 3);  // code tile row
+      const int k = k0 + ((lane & 7) ^ ((r >> 1) & 7)) * 16;
+      const int wr = (EPI == EPI_SWIGLU) ? (r & 63) : r;  // SwiGLU: 64 gate rows, then 64 up
+      const uint32_t ow = (k < ke && wr < wrows) ? (uint32_t)wr * (uint32_t)K + (uint32_t)k : kOob;
+      lds_dma16((EPI == EPI_SWIGLU && r >= 64) ? rw1 : rw0, ow, lb + q * 1024);
+    }
+  };
+
+  // code tile rows feeding this wave's two 32-column fragments
+  int brow[2];
+  if constexpr (EPI == EPI_SWIGLU) {
+    brow[0] = wn * 32;       // gate f = c0 + wn*32 + lane%32
+    brow[1] = 64 + wn * 32;  // up, same f
+  } else {
+    brow[0] = wn * 64;
+    brow[1] = wn * 64 + 32;
+  }
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+#pragma unroll
+  for (int st = 0; st < SQ - 1; ++st) issue(st, st);
+
+  const int hh = lane >> 5;  // lane half: code chunk 2p + hh of a chunk pair p
+  int buf = 0;               // kt % SQ
+  for (int kt = 0; kt < NT; ++kt) {
+    wait_vmcnt<(SQ - 2) * kInstQ>();  // this wave's part of stage kt has landed
+    __syncthreads();                  // everyone's has; stage kt - 1 is consumed
+    const unsigned char* sa = smem + buf * kStageQ;
+    const unsigned char* sb = sa + kStageQA;
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      const int p = 2 * g + pp;
+      bf16x8_t wlo[2], whi[2], alo[2], ahi[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4_t w =
+            *reinterpret_cast<const u32x4_t*>(sb + lds_off(brow[j] + (lane & 31), 2 * p + hh));
+        u32x4_t lo, hi;
+        if constexpr (WF == kWInt8)
+          decode16_i8(w, lo, hi);
+        else
+          decode16(w, lo, hi);
+        wlo[j] = __builtin_bit_cast(bf16x8_t, lo);
+        whi[j] = __builtin_bit_cast(bf16x8_t, hi);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = wm * 64 + i * 32 + (lane & 31);
+        alo[i] = *reinterpret_cast<const bf16x8_t*>(sa + lds_off_qa(row, 4 * p + 2 * hh));
+        ahi[i] = *reinterpret_cast<const bf16x8_t*>(sa + lds_off_qa(row, 4 * p + 2 * hh + 1));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[i], wlo[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[i], whi[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    // refill stage kt - 1's buffer after this stage's MFMAs are issued
+    issue(kt + SQ - 1, buf == 0 ? SQ - 1 : buf - 1);
+    buf = buf == SQ - 1 ? 0 : buf + 1;
+  }
+
+  wait_vmcnt<0>();  // zero-fill loads of stages past the end have landed
+  __syncthreads();
+
+  // ---- both K groups' accumulators as row-major [BM][BN] tiles in LDS
+  float* tg = reinterpret_cast<float*>(smem) + g * (BM * BN);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        tg[(wm * 64 + i * 32 + acc_row32(r, lane)) * BN + brow[j] + (lane & 31)] = acc[i][j][r];
+  __syncthreads();
+  const f32x4_t* t0 = reinterpret_cast<const f32x4_t*>(smem);
+  const f32x4_t* t1 = t0 + BM * BN / 4;
+
+  if (ns > 1) {
+    // ---- split K: unscaled partial tile [BM][BN], then arrival
+    const int64_t tile_elems = (int64_t)BM * BN;
+    const __amdgpu_buffer_rsrc_t pr =
+        make_rsrc(part, (uint32_t)((int64_t)ns * tiles * tile_elems * 4));
+    const int64_t tbase = (int64_t)tile * tile_elems;
+    const int64_t plane = (int64_t)tiles * tile_elems;
+#pragma unroll
+    for (int k = 0; k < BM * BN / 4 / kThreads; ++k) {
+      const int q = tid + k * kThreads;
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4_t, t0[q] + t1[q]), pr,
+          (uint32_t)((split * plane + tbase + 4 * q) * 4), 0, kAuxSys);
+    }
+    int* is_last = reinterpret_cast<int*>(smem + 2 * BM * BN * 4);  // past both tiles
+    wait_vmcnt<0>();  // partial stores have reached memory
+    __syncthreads();
+    if (tid == 0) *is_last = arrive_last(counters + tile, (unsigned)ns);
+    __syncthreads();
+    if (!*is_last) return;
+    finish_splits<EPI, BM, BN, kThreads, 8>(pr, tbase, plane, ns, m0, c0, M, N, out, ldo, tid,
+                                            split, t0, t1, S0, EPI == EPI_SWIGLU ? S1 : nullptr);
+    return;
+  }
+
+  // ---- direct epilogue: item = 4 output columns of one row
+  constexpr int kQ = kCols / 4;
+#pragma unroll
+  for (int k = 0; k < BM * kQ / kThreads; ++k) {
+    const int idx = tid + k * kThreads;
+    const int tr = idx / kQ, tc = (idx % kQ) * 4;
+    const int m = m0 + tr;
+    if (m >= M || c0 + tc >= N) continue;
+    const int n = min(4, N - (c0 + tc));
+    const int fi = (tr * BN + tc) / 4;
+    f32x4_t v = (t0[fi] + t1[fi]) * col_scales(S0, c0 + tc, n);
+    if constexpr (EPI == EPI_SWIGLU) {
+      const f32x4_t u = (t0[fi + 16] + t1[fi + 16]) * col_scales(S1, c0 + tc, n);
+      v = f32x4_t{silu(v.x) * u.x, silu(v.y) * u.y, silu(v.z) * u.z, silu(v.w) * u.w};
+    }
+    store_out4<EPI == EPI_F32 ? EPI_F32 : EPI_DT>(out, ldo, m, c0 + tc, n, v);
+  }
+}
+
 enum Tile { kT128 = 0, kTWide = 1 };  // 128 x 128, 256 x 128
 
 struct Plan {
@@ -600,19 +845,23 @@ struct Plan {
   int ns = 0;  // K splits
   int kr = 0;  // K per split
   int grid = 0;
+  int tile_elems = 0;
 };
 
 struct TileShape {
-  int bm, bn;   // activation rows, weight rows
-  int bk;       // K per stage
-  double rate;  // copy stream of a CU next to the MFMA work, B/clk
+  int bm, bn;     // activation rows, weight rows
+  int bk;         // K per stage
+  double rate;    // copy stream of a CU next to the MFMA work, B/clk
+  double wbytes;  // bytes per weight element
 };
 
 // Measured on this chip at the prefill shapes with every CU busy: the 128 x
 // 128 kernel's copies run at about 21 B/clk per CU next to its MFMA work,
-// the 256 x 128 kernel's at about 19.
+// the 256 x 128 kernel's at about 19.  The one-byte kernel is taken at the
+// 128 x 128 kernel's rate.
 constexpr int kNumShapes = 2;
-constexpr TileShape kShapes[kNumShapes] = {{BM, BN, BK, 21.0}, {WM, WN, WK, 19.0}};
+constexpr TileShape kShapes[kNumShapes] = {{BM, BN, BK, 21.0, 2.0}, {WM, WN, WK, 19.0, 2.0}};
+constexpr TileShape kShapeQ8 = {BM, BN, QBK, 21.0, 1.0};
 
 // Cost model (CU cycles) for a tile shape and split count.  A workgroup's
 // main loop runs at the rate its copy stream reaches next to the MFMA work,
@@ -620,10 +869,9 @@ constexpr TileShape kShapes[kNumShapes] = {{BM, BN, BK, 21.0}, {WM, WN, WK, 19.0
 // CU; with split K each workgroup also writes its partial tile and the last
 // of a tile's workgroups reads all of them, each at the slower of a CU's
 // stream (about 24 B/clk) and its share of HBM (about 2 KB/clk for the chip).
-double plan_cost(int tiles, int ns, int shape, int K) {
-  const TileShape& t = kShapes[shape];
+double plan_cost(int tiles, int ns, const TileShape& t, int K) {
   const double kspl = std::ceil((double)K / t.bk / ns) * t.bk;  // K per split
-  const double copy = (double)(t.bm + t.bn) * kspl * 2.0 / t.rate;
+  const double copy = (t.bm * 2.0 + t.bn * t.wbytes) * kspl / t.rate;
   const double mfma = 2.0 * t.bm * t.bn * kspl / (4.0 * 1024.0) / 0.9;
   const double rounds = std::ceil((double)tiles * ns / kCUs);
   const double tile_bytes = (double)t.bm * t.bn * 4.0;
@@ -636,23 +884,23 @@ double plan_cost(int tiles, int ns, int shape, int K) {
 }
 
 // Split K when the tiles alone leave CUs idle: the tile shape and split
-// count of least modelled cost; at least 8 stages of 64 K per split, at
-// most 256 MB of partials and one arrival counter per tile.  The 256-row
-// shape needs M >= 384 (enough rows to fill most of a tile).
+// count of least modelled cost; at least 8 stages per split, at most 256 MB
+// of partials and one arrival counter per tile.  The 256-row shape needs
+// M >= 384 (enough rows to fill most of a tile).
 constexpr double kMaxPartialBytes = 256.0 * 1024 * 1024;
-Plan make_plan(int M, int N, int K, bool swiglu) {
+Plan make_plan_over(const TileShape* shapes, int nshapes, int M, int N, int K, bool swiglu) {
   Plan best_pl;
   double best = 1e300;
-  const int max_ns = std::max(1, std::min(16, (K + BK - 1) / BK / 8));
-  for (int shape = 0; shape < kNumShapes; ++shape) {
-    const TileShape& t = kShapes[shape];
+  for (int shape = 0; shape < nshapes; ++shape) {
+    const TileShape& t = shapes[shape];
     if (t.bm > BM && M < 384) continue;
     const int cols = swiglu ? t.bn / 2 : t.bn;
     const int tiles = ((M + t.bm - 1) / t.bm) * ((N + cols - 1) / cols);
+    const int max_ns = std::max(1, std::min(16, (K + t.bk - 1) / t.bk / 8));
     for (int ns = 1; ns <= max_ns; ++ns) {
       if (ns > 1 && ((double)ns * tiles * t.bm * t.bn * 4.0 > kMaxPartialBytes || tiles > kWsMaxCounters))
         break;
-      const double cost = plan_cost(tiles, ns, shape, K);
+      const double cost = plan_cost(tiles, ns, t, K);
       if (cost < best * (1.0 - 1e-9)) {
         best = cost;
         best_pl.shape = shape;
@@ -661,19 +909,38 @@ Plan make_plan(int M, int N, int K, bool swiglu) {
       }
     }
   }
-  const int bk = kShapes[best_pl.shape].bk;
-  const int kst = (K + bk - 1) / bk;                    // K stages in all
+  const TileShape& t = shapes[best_pl.shape];
+  const int kst = (K + t.bk - 1) / t.bk;                // K stages in all
   const int sps = (kst + best_pl.ns - 1) / best_pl.ns;  // stages per split
-  best_pl.kr = sps * bk;
+  best_pl.kr = sps * t.bk;
   best_pl.ns = (K + best_pl.kr - 1) / best_pl.kr;
   best_pl.grid = best_pl.tiles * best_pl.ns;
+  best_pl.tile_elems = t.bm * t.bn;
   return best_pl;
+}
+
+Plan make_plan(int M, int N, int K, bool swiglu) {
+  return make_plan_over(kShapes, kNumShapes, M, N, K, swiglu);
+}
+
+Plan make_plan_q8(int M, int N, int K, bool swiglu) {
+  return make_plan_over(&kShapeQ8, 1, M, N, K, swiglu);
 }
 
 size_t plan_bytes(const Plan& pl) {
   if (pl.ns <= 1) return 0;
-  const TileShape& t = kShapes[pl.shape];
-  return kWsCounterBytes + (size_t)pl.ns * pl.tiles * t.bm * t.bn * sizeof(float);
+  return kWsCounterBytes + (size_t)pl.ns * pl.tiles * pl.tile_elems * sizeof(float);
+}
+
+// The split-K workspace of a plan: arrival counters, then the fp32 partials.
+hipError_t split_buffers(const Plan& pl, void* workspace, unsigned** counters, float** part) {
+  *counters = nullptr;
+  *part = nullptr;
+  if (pl.ns <= 1) return hipSuccess;
+  if (workspace == nullptr || pl.tiles > kWsMaxCounters) return hipErrorInvalidValue;
+  *counters = static_cast<unsigned*>(workspace);
+  *part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsCounterBytes);
+  return hipSuccess;
 }
 
 template <int EPI>
@@ -681,13 +948,9 @@ hipError_t launch_plan(const Plan& pl, int M, int N, int K, const uint16_t* A, i
                        const uint16_t* W0, const uint16_t* W1, void* out, int64_t ldo,
                        void* workspace, hipStream_t stream) {
   auto kern = pl.shape == kTWide ? gemm_wide_kernel<EPI> : gemm_kernel<EPI>;
-  unsigned* counters = nullptr;
-  float* part = nullptr;
-  if (pl.ns > 1) {
-    if (workspace == nullptr || pl.tiles > kWsMaxCounters) return hipErrorInvalidValue;
-    counters = static_cast<unsigned*>(workspace);
-    part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsCounterBytes);
-  }
+  unsigned* counters;
+  float* part;
+  if (split_buffers(pl, workspace, &counters, &part) != hipSuccess) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(kThreads), 0, stream, M, N, K, A, lda, W0, W1,
                      out, ldo, pl.kr, counters, part);
   return hipGetLastError();
@@ -707,6 +970,33 @@ hipError_t gemm_launch(int M, int N, int K, const uint16_t* A, int64_t lda, cons
   if (pl.grid == 0) return hipErrorInvalidValue;
   return launch_plan<EPI>(pl, M, N, K, A, lda, W0, W1, out, ldo, workspace, stream);
 }
+
+size_t gemm_q8_workspace_bytes(int M, int N, int K, bool swiglu) {
+  return plan_bytes(make_plan_q8(M, N, K, swiglu));
+}
+
+template <int EPI>
+hipError_t gemm_q8_launch(int M, int N, int K, const uint16_t* A, int64_t lda, const uint8_t* W0,
+                          const float* S0, const uint8_t* W1, const float* S1, void* out,
+                          int64_t ldo, void* workspace, int fmt, hipStream_t stream) {
+  const Plan pl = make_plan_q8(M, N, K, EPI == EPI_SWIGLU);
+  if (pl.grid == 0 || K % 16) return hipErrorInvalidValue;
+  unsigned* counters;
+  float* part;
+  if (split_buffers(pl, workspace, &counters, &part) != hipSuccess) return hipErrorInvalidValue;
+  auto kern = fmt == kFmtInt8 ? gemm_q8_kernel<EPI, kWInt8> : gemm_q8_kernel<EPI, kWE4M3>;
+  hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(kThreads), 0, stream, M, N, K, A, lda, W0, S0, W1,
+                     S1, out, ldo, pl.kr, counters, part);
+  return hipGetLastError();
+}
+
+template hipError_t gemm_q8_launch<EPI_F32>(int, int, int, const uint16_t*, int64_t,
+                                            const uint8_t*, const float*, const uint8_t*,
+                                            const float*, void*, int64_t, void*, int, hipStream_t);
+template hipError_t gemm_q8_launch<EPI_SWIGLU>(int, int, int, const uint16_t*, int64_t,
+                                               const uint8_t*, const float*, const uint8_t*,
+                                               const float*, void*, int64_t, void*, int,
+                                               hipStream_t);
 
 template hipError_t gemm_launch<EPI_F32>(int, int, int, const uint16_t*, int64_t,
                                          const uint16_t*, const uint16_t*, void*, int64_t, void*,

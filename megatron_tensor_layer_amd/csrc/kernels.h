@@ -93,15 +93,28 @@ hipError_t rowstream_fp8_launch(int I, int K, int N, const uint16_t* X, const ui
                                 const float* S0, const uint8_t* W1, const float* S1, void* out,
                                 int64_t ldo, int fmt, hipStream_t stream);
 
-// Same product on bf16 MFMA for any M (128 x 128 tiles).  When the tiles
-// cannot fill the chip, K is split over workgroups and `workspace`
-// (gemm_workspace_bytes, 0 when not split) holds the arrival counters and
-// the fp32 partial tiles (layout above).
+// Same product on bf16 MFMA for any M (128 x 128 or 256 x 128 tiles, by a
+// cost model).  When the tiles cannot fill the chip, K is split over
+// workgroups and `workspace` (gemm_workspace_bytes, 0 when not split) holds
+// the arrival counters and the fp32 partial tiles (layout above).
 size_t gemm_workspace_bytes(int M, int N, int K, bool swiglu);
+// Largest K of the GEMM kernels: a tile's operand rows (up to 256 x K bf16)
+// are addressed with 32-bit byte offsets.
+constexpr int64_t kGemmMaxK = int64_t(1) << 22;
 template <int EPI>
 hipError_t gemm_launch(int M, int N, int K, const uint16_t* A, int64_t lda, const uint16_t* W0,
                        const uint16_t* W1, void* out, int64_t ldo, void* workspace,
                        hipStream_t stream);
+
+// The same GEMM with one-byte weight codes of format fmt (kFmtE4M3 or
+// kFmtInt8) and one fp32 scale per weight row (S0; S1 for the up rows of
+// EPI_SWIGLU), bf16 activations, 128 x 128 tiles; K a multiple of 16.
+// Workspace as gemm_launch (gemm_q8_workspace_bytes).
+size_t gemm_q8_workspace_bytes(int M, int N, int K, bool swiglu);
+template <int EPI>
+hipError_t gemm_q8_launch(int M, int N, int K, const uint16_t* A, int64_t lda, const uint8_t* W0,
+                          const float* S0, const uint8_t* W1, const float* S1, void* out,
+                          int64_t ldo, void* workspace, int fmt, hipStream_t stream);
 
 // Read-only stream of `bytes` (a multiple of 1 KB, at most 2 GiB) with the
 // decode kernels' access pattern; one word per thread of the grid

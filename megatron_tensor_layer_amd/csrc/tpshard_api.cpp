@@ -65,6 +65,11 @@ Path bf16_path(int64_t I, int64_t K, int64_t N, bool swiglu) {
   return gemv_ok ? Path::Gemv : Path::Gemm;
 }
 
+// A projection the GEMM would take with a K beyond its 32-bit operand offsets.
+bool gemm_k_too_long(int64_t I, int64_t K, int64_t N, bool swiglu, tp_dtype_t dt) {
+  return dt == TP_BF16 && K > tpk::kGemmMaxK && bf16_path(I, K, N, swiglu) == Path::Gemm;
+}
+
 // Workspace of one projection (split-K partial sums; 0 when not split).
 size_t proj_workspace(int64_t I, int64_t K, int64_t N, bool swiglu, tp_dtype_t dt) {
   if (dt != TP_BF16 || I < 1) return 0;
@@ -167,6 +172,8 @@ tp_status_t mlp_args_status(int64_t I, int64_t D, int64_t F_local, tp_dtype_t dt
   if (overlap(rH, rP)) return TP_ERR_INVALID;
   if (dt == TP_F32 && (D > tpk::kGemvMaxK32 || F_local > tpk::kGemvMaxK32))
     return TP_ERR_UNSUPPORTED;
+  if (gemm_k_too_long(I, D, F_local, true, dt) || gemm_k_too_long(I, F_local, D, false, dt))
+    return TP_ERR_UNSUPPORTED;
   return TP_OK;
 }
 }  // namespace
@@ -252,6 +259,8 @@ tp_status_t tp_shard_attn_proj(tp_attn_phase_t phase, int64_t I, int64_t D, int6
   const int64_t osz = (phase == TP_ATTN_O) ? 4 : es;
   const Range rIn = rng(in, I * K * es), rW = rng(W, N * K * es), rO = rng(out, I * N * osz);
   if (overlap(rO, rIn) || overlap(rO, rW)) return TP_ERR_INVALID;
+  if (dt == TP_F32 && K > tpk::kGemvMaxK32) return TP_ERR_UNSUPPORTED;
+  if (gemm_k_too_long(I, K, N, false, dt)) return TP_ERR_UNSUPPORTED;
   const size_t need =
       tp_shard_attn_proj_workspace_size(phase, I, D, n_q_local, n_kv_local, head_dim, dt);
   if (need > 0) {
@@ -260,7 +269,6 @@ tp_status_t tp_shard_attn_proj(tp_attn_phase_t phase, int64_t I, int64_t D, int6
     const Range rWs = rng(workspace, (int64_t)need);
     if (overlap(rWs, rIn) || overlap(rWs, rW) || overlap(rWs, rO)) return TP_ERR_INVALID;
   }
-  if (dt == TP_F32 && K > tpk::kGemvMaxK32) return TP_ERR_UNSUPPORTED;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
@@ -286,12 +294,12 @@ tp_status_t tp_partial_reduce(int32_t t, int64_t n, const float* partials, tp_dt
 }
 
 namespace {
-// The FP8 path for I tokens: the few-token VALU kernel up to 4 tokens (K
-// within kFp8MaxK), the split-K MFMA kernel from 5 to 64 (measured on the
+// The one-byte path for I tokens: the few-token VALU kernel up to 4 tokens
+// (K within kFp8MaxK), the split-K MFMA kernel from 5 to 64 (measured on the
 // Llama-3.1-70B TP=8 share: 27.0 us against about 33 at 4 tokens, 36.8
-// against about 33 at 5), the VALU kernel up to 8 tokens when no split-K plan
-// fits; None = unsupported.
-enum class Fp8Path { None, Gemv, SplitK };
+// against about 33 at 5), and the one-byte GEMM for more tokens or when no
+// split-K plan fits (the VALU kernel up to 8 tokens).
+enum class Fp8Path { None, Gemv, SplitK, Gemm };
 Fp8Path fp8_path(int64_t I, int64_t D, int64_t F_local) {
   if (I < 1) return Fp8Path::None;
   const bool gemv_ok = I <= tpk::kFp8MaxTokens && D <= tpk::kFp8MaxK && F_local <= tpk::kFp8MaxK;
@@ -299,7 +307,7 @@ Fp8Path fp8_path(int64_t I, int64_t D, int64_t F_local) {
   if (I <= tpk::kSplitKMaxTokens && tpk::splitk_plannable((int)I, (int)D, (int)F_local, true) &&
       tpk::splitk_plannable((int)I, (int)F_local, (int)D, false))
     return Fp8Path::SplitK;
-  return gemv_ok ? Fp8Path::Gemv : Fp8Path::None;
+  return gemv_ok ? Fp8Path::Gemv : Fp8Path::Gemm;
 }
 
 // On the MFMA path (from 5 tokens), the FP8 down projection streams whole K
@@ -315,7 +323,11 @@ bool fp8_down_rowstream(int64_t I, int64_t D, int64_t F_local) {
 size_t tp_shard_mlp_fp8_workspace_size(int64_t I, int64_t D, int64_t F_local) {
   if (I < 1 || I > kMaxDim || !dims_ok(D) || !dims_ok(F_local) || (D % 16) || (F_local % 16))
     return 0;
-  if (fp8_path(I, D, F_local) != Fp8Path::SplitK) return 0;
+  const Fp8Path path = fp8_path(I, D, F_local);
+  if (path == Fp8Path::Gemm)
+    return std::max(tpk::gemm_q8_workspace_bytes((int)I, (int)F_local, (int)D, true),
+                    tpk::gemm_q8_workspace_bytes((int)I, (int)D, (int)F_local, false));
+  if (path != Fp8Path::SplitK) return 0;
   const size_t down = fp8_down_rowstream(I, D, F_local)
                           ? 0
                           : tpk::splitk_workspace_bytes((int)I, (int)F_local, (int)D, false);
@@ -351,6 +363,8 @@ tp_status_t mlp_bytew(int fmt, int64_t I, int64_t D, int64_t F_local, const void
   if (overlap(rH, rP)) return TP_ERR_INVALID;
   const Fp8Path path = fp8_path(I, D, F_local);
   if (path == Fp8Path::None) return TP_ERR_UNSUPPORTED;
+  if (path == Fp8Path::Gemm && (D > tpk::kGemmMaxK || F_local > tpk::kGemmMaxK))
+    return TP_ERR_UNSUPPORTED;
   const size_t need = tp_shard_mlp_fp8_workspace_size(I, D, F_local);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return TP_ERR_WORKSPACE;
@@ -372,6 +386,14 @@ tp_status_t mlp_bytew(int fmt, int64_t I, int64_t D, int64_t F_local, const void
     if (e != hipSuccess) return TP_ERR_LAUNCH;
     return launched(tpk::gemv_fp8_launch<tpk::EPI_F32>((int)I, (int)F_local, (int)D, Hb, d8,
                                                        s_down, nullptr, nullptr, P, D, fmt, s));
+  }
+  if (path == Fp8Path::Gemm) {
+    e = tpk::gemm_q8_launch<tpk::EPI_SWIGLU>((int)I, (int)F_local, (int)D, Xb, D, g8, s_gate, u8,
+                                             s_up, H, F_local, workspace, fmt, s);
+    if (e != hipSuccess) return TP_ERR_LAUNCH;
+    return launched(tpk::gemm_q8_launch<tpk::EPI_F32>((int)I, (int)D, (int)F_local, Hb, F_local,
+                                                      d8, s_down, nullptr, nullptr, P, D,
+                                                      workspace, fmt, s));
   }
   e = tpk::splitk_fp8_launch<tpk::EPI_SWIGLU>((int)I, (int)D, (int)F_local, Xb, g8, s_gate, u8,
                                               s_up, H, F_local, workspace, fmt, s);

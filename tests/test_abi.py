@@ -82,6 +82,10 @@ def test_mlp_validation(lib):
     assert mlp(lib, ptrs=p) == INVALID
     # fp32 beyond the few-token kernel's K range
     assert mlp(lib, D=32768, dt=tp.TP_F32) == UNSUPPORTED
+    # a GEMM-size call (300 tokens) whose down K is past the GEMM's 32-bit
+    # operand offsets (2^22); the same K at 4 tokens streams on VALU
+    assert mlp(lib, I=300, D=64, F=(1 << 22) + 8) == UNSUPPORTED
+    assert mlp(lib, I=300, D=64, F=1 << 22, ws=None) == WORKSPACE
 
 
 def test_attn_validation(lib):
@@ -96,6 +100,8 @@ def test_attn_validation(lib):
     assert f(tp.TP_ATTN_O, 4, 256, 2, 1, 128, tp.TP_BF16, P[0], P[1],
              ctypes.c_void_p(P[2].value + 4)) == MISALIGNED
     assert f(tp.TP_ATTN_O, 4, 256, 2, 1, 128, tp.TP_BF16, P[0], P[1], P[0]) == INVALID
+    # o_proj at 300 tokens with K = n_q_local * head_dim past the GEMM's 2^22
+    assert f(tp.TP_ATTN_O, 300, 8, (1 << 15) + 1, 1, 128, tp.TP_BF16, *P) == UNSUPPORTED
 
 
 def test_reduce_validation(lib):
@@ -181,14 +187,18 @@ def test_mlp_fp8_validation(lib):
     args = [fake(k) for k in range(9)] + [None, 0, None]
     assert m(0, 64, 128, *args) == OK
     assert m(-1, 64, 128, *args) == INVALID
-    assert m(65, 64, 128, *args) == UNSUPPORTED                      # decode only: I <= 64
+    assert m(65, 64, (1 << 22) + 16, *args) == UNSUPPORTED           # GEMM K past 2^22
     assert m(9, 64, 128, *args) == WORKSPACE                         # split K: needs one
     assert m(1, 24, 128, *args) == MISALIGNED                        # D not a multiple of 16
     assert m(1, 32768, 128, *args) == WORKSPACE                      # K above 16384: split K
     assert lib.tp_shard_mlp_fp8_workspace_size(4, 8192, 3584) == 0     # VALU kernel
     assert lib.tp_shard_mlp_fp8_workspace_size(5, 8192, 3584) > 0      # split K from 5
     need = lib.tp_shard_mlp_fp8_workspace_size(32, 8192, 3584)
-    assert need > 8192 and lib.tp_shard_mlp_fp8_workspace_size(65, 8192, 3584) == 0
+    assert need > 8192
+    # more than 64 tokens: the one-byte GEMM; at 65 tokens its 56 gate/up
+    # tiles split K 4 ways (224 workgroups)
+    assert lib.tp_shard_mlp_fp8_workspace_size(65, 8192, 3584) == 8192 + 4 * 56 * 128 * 128 * 4
+    assert lib.tp_shard_mlp_int8_workspace_size(65, 8192, 3584) == 8192 + 4 * 56 * 128 * 128 * 4
     small = lib.tp_shard_mlp_fp8_workspace_size(32, 64, 128)
     ws = list(args)
     ws[9], ws[10] = ctypes.c_void_p(FAKE + 9 * STEP + 8), small

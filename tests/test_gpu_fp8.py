@@ -1,7 +1,8 @@
 """GPU parity of tp_shard_mlp_fp8 (weight-only FP8 storage, OCP E4M3 with a
 fp32 scale per output row; bf16 activations) against the fp64 oracle on the
-dequantized weights: the few-token kernel (1..8 tokens) and the split-K MFMA
-kernel (9..64).  Bar: normwise 2e-2 (bf16 inputs and H, fp32 sums)."""
+dequantized weights: the few-token kernel (1..8 tokens), the split-K MFMA
+kernel (9..64) and the one-byte GEMM (more tokens).  Bar: normwise 2e-2
+(bf16 inputs and H, fp32 sums)."""
 import numpy as np
 import pytest
 
@@ -72,6 +73,34 @@ def test_llama_rank_share_split_k(orc, llama_fp8, I):
     assert normwise_err(P, P_ref) <= TOL
 
 
+@pytest.mark.parametrize("I", [65, 128, 512])
+def test_llama_rank_share_gemm(orc, llama_fp8, I):
+    """More than 64 tokens: the one-byte GEMM (gate/up split K at 65 and 128
+    tokens, unsplit at 512); every row against the oracle."""
+    D = 8192
+    X = datagen.gaussian("X", (I, D), 1.0, "bf16", 660 + I)
+    H, P = _run(X, llama_fp8)
+    H_ref, P_ref = _reference(orc, X, llama_fp8)
+    assert normwise_err(H, H_ref) <= TOL
+    assert normwise_err(P, P_ref) <= TOL
+
+
+@pytest.mark.parametrize("I,D,Fl", [(65, 16, 16), (70, 1040, 272), (130, 272, 1040),
+                                    (300, 528, 400), (100, 4112, 272), (520, 1536, 4480)])
+def test_gemm_ragged_shapes(orc, I, D, Fl):
+    """The one-byte GEMM on a K of one 16-code chunk, ragged K stages (1040 =
+    8 x 128 + 16), ragged weight tiles (272 = 4 x 64 + 16 gate/up columns),
+    a ragged last M tile (130, 300, 520 tokens), a long K over few tiles
+    (split K with a ragged last range) and the Qwen2.5-1.5B TP=2 share at 520
+    tokens."""
+    shards = _shards(D, Fl, 64)
+    X = datagen.gaussian("X", (I, D), 1.0, "bf16", 650 + I)
+    H, P = _run(X, shards)
+    H_ref, P_ref = _reference(orc, X, shards)
+    assert normwise_err(H, H_ref) <= TOL
+    assert normwise_err(P, P_ref) <= TOL
+
+
 @pytest.mark.parametrize("I", [1, 8, 24])
 def test_qwen_tp2_partials_sum_to_layer(orc, I):
     """Qwen2.5-1.5B MLP (D = 1536, F = 8960) at TP=2: each rank's FP8 share
@@ -108,16 +137,12 @@ def test_small_and_ragged_shapes(orc, I, D, Fl):
     assert normwise_err(P, P_ref) <= TOL
 
 
-def test_deterministic_and_unsupported(orc):
+def test_deterministic(orc):
+    """Bitwise the same twice: the few-token kernel, split K (fixed summation
+    order) and the one-byte GEMM with split K."""
     D, Fl = 1536, 4480
     shards = _shards(D, Fl, 63)
-    X = datagen.gaussian("X", (8, D), 1.0, "bf16", 630)
-    a, b = _run(X, shards), _run(X, shards)
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
-    X33 = datagen.gaussian("X", (33, D), 1.0, "bf16", 632)  # split K: fixed summation order
-    a, b = _run(X33, shards), _run(X33, shards)
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
-    X65 = to_dev(datagen.gaussian("X", (65, D), 1.0, "bf16", 631), "bf16")
-    with pytest.raises(tp.TPError, match="UNSUPPORTED"):
-        tp.shard_mlp_fp8(X65, *(_dev_fp8(s) for s in shards), empty((65, Fl), "bf16"),
-                         empty((65, D), "f32"))
+    for I, seed in ((8, 630), (33, 632), (65, 631)):
+        X = datagen.gaussian("X", (I, D), 1.0, "bf16", seed)
+        a, b = _run(X, shards), _run(X, shards)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), I

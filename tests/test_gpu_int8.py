@@ -1,7 +1,8 @@
 """GPU parity of tp_shard_mlp_int8 (weight-only int8 storage: a signed code
 and a fp32 scale per output row; bf16 activations) against the fp64 oracle on
 the dequantized weights, through every kernel the call uses: the few-token
-kernel (1..4 tokens), split-K gate/up with whole-K or split-K down (5..64).
+kernel (1..4 tokens), split-K gate/up with whole-K or split-K down (5..64),
+the one-byte GEMM (more tokens).
 Bar: normwise 2e-2 (bf16 inputs and H, fp32 sums)."""
 import numpy as np
 import pytest
@@ -58,7 +59,7 @@ def llama_i8():
     return _shards(8192, 3584, 70)
 
 
-@pytest.mark.parametrize("I", [1, 2, 4, 5, 8, 16, 32, 64])
+@pytest.mark.parametrize("I", [1, 2, 4, 5, 8, 16, 32, 64, 65, 256, 512])
 def test_llama_rank_share(orc, llama_i8, I):
     """One Llama-3.1-70B TP=8 MLP rank share (D = 8192, F_local = 3584),
     every row against the oracle."""
@@ -69,7 +70,8 @@ def test_llama_rank_share(orc, llama_i8, I):
     assert normwise_err(P, P_ref) <= TOL
 
 
-@pytest.mark.parametrize("I,D,Fl", [(3, 528, 272), (12, 1040, 400), (40, 2064, 528)])
+@pytest.mark.parametrize("I,D,Fl", [(3, 528, 272), (12, 1040, 400), (40, 2064, 528),
+                                    (70, 1040, 272), (130, 272, 1040), (300, 528, 400)])
 def test_ragged_shapes(orc, I, D, Fl):
     """Contraction lengths and row counts that are not multiples of the
     kernels' tiles (multiples of 16 only)."""
