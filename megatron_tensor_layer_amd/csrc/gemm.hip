@@ -396,10 +396,13 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
 // ---------------------------------------------------------------- 256 x 128
 // The same product with 256 x 128 workgroup tiles (256 activation rows, 128
 // weight rows): per K element a CU copies 384 rows for 2 x 256 x 128 FLOPs, a
-// quarter fewer bytes per FLOP than the 128 x 128 tile.  Where the copy
-// stream of a CU is the limit (the 512-token rank shapes) that is the gain;
-// the per-rank shapes then give half as many tiles, and K is split in two
-// to fill the chip.
+// quarter fewer bytes per FLOP than the 128 x 128 tile.  The per-rank shapes
+// give half as many tiles, so K is split in two to fill the chip.  Its
+// copies alone take a fifth less time than the 128 x 128 kernel's, but its
+// MFMA and LDS work overlaps them less: measured, it ties the 128 x 128
+// kernel on the TP=8 gate/up at 512 tokens (75-77 us against 80) and beats
+// the 256 x 256 kernel it replaced on the TP=1 down (263-277 us split 2 ways
+// against 304 split 4 ways).
 //   * eight waves: a 2 x 2 grid of 128 x 64 wave tiles (4 x 2 MFMA
 //     fragments, 128 fp32 accumulators per lane), twice -- the two groups of
 //     four waves take alternate pairs of every stage's 16-wide K steps, so
@@ -628,6 +631,10 @@ gemm_wide_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t ld
 //     which leaves the sums' terms unchanged;
 //   * each output column's scale multiplies its sum in the epilogue (or in
 //     the split-K finish), before silu(g) * u.
+// Measured on the Llama TP=8 share it is not copy-bound: the decode keeps
+// the VALU busy for about a third of the wave-cycles, and copies, MFMAs and
+// decodes of a stage overlap only in part.  It runs at the bf16 GEMM's rate
+// at 128 tokens and about 15 % below it at 512.
 constexpr int QBK = 128;                         // K per stage
 constexpr int kRowQA = QBK * 2;                  // 256-byte activation rows
 constexpr int kRowQW = QBK;                      // 128-byte code rows
