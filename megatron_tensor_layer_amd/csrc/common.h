@@ -26,8 +26,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, b);
 }
 
+// Two floats to packed bf16 (lo in bits 0..15), round to nearest even: one
+// v_cvt_pk_bf16_f32 (two scalar conversions and a shift-or otherwise).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){lo, hi}, bf16x2v));
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
@@ -121,15 +125,17 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // 16 OCP E4M3 codes -> two 8-element bf16 chunks (K 0..7, K 8..15), exact:
-// every E4M3 value is a bf16 value; v_cvt_pk_f32_fp8 decodes two codes.
+// every E4M3 value is a bf16 value.  v_cvt_scalef32_pk_bf16_fp8 with scale 1
+// decodes two codes straight to packed bf16; on all 256 codes it gives the
+// bits of v_cvt_pk_f32_fp8 followed by a bf16 conversion (NaN codes too).
 __device__ __forceinline__ void decode16(const u32x4_t& w, u32x4_t& lo, u32x4_t& hi) {
   uint32_t p[8];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], false);  // bytes 0, 1
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[q], true);   // bytes 2, 3
-    p[2 * q] = pack_bf16x2(a[0], a[1]);
-    p[2 * q + 1] = pack_bf16x2(b[0], b[1]);
+    p[2 * q] = __builtin_bit_cast(uint32_t,  // bytes 0, 1
+                                  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q], 1.0f, false));
+    p[2 * q + 1] = __builtin_bit_cast(uint32_t,  // bytes 2, 3
+                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q], 1.0f, true));
   }
   lo = u32x4_t{p[0], p[1], p[2], p[3]};
   hi = u32x4_t{p[4], p[5], p[6], p[7]};

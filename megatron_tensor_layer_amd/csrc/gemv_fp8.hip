@@ -6,9 +6,9 @@
 // Serving", §1.1 and §3.4); one byte per weight halves that stream.  The
 // kernel is the bf16 few-token kernel with a different chunk: a lane's
 // 16-byte weight chunk holds 16 K values, so it pairs with two 16-byte chunks
-// of each token's activations.  gfx950's v_cvt_pk_f32_fp8 decodes the OCP
-// E4M3 codes; every E4M3 value is exact in bf16, so the decoded pairs feed
-// v_dot2_f32_bf16 unchanged (fp32 sums).  The per-row scale multiplies the
+// of each token's activations.  gfx950's v_cvt_scalef32_pk_bf16_fp8 decodes
+// two OCP E4M3 codes straight to packed bf16 (every E4M3 value is exact in
+// bf16), and the decoded pairs feed v_dot2_f32_bf16 (fp32 sums).  The per-row scale multiplies the
 // finished dot product once, in the epilogue.
 #include "common.h"
 #include "kernels.h"
