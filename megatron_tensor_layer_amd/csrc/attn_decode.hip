@@ -10,16 +10,20 @@
 //
 // Work split: one workgroup of NWV waves per (sequence, KV group, chunk of
 // the positions); the chunks fill the chip when the sequences alone cannot.
-// Inside a chunk the waves take interleaved blocks of 32 positions on bf16
-// MFMA (v_mfma_f32_32x32x16_bf16) with the same transposed formulation as
-// the attention core: S^T = K Q^T with the group's query heads as the 32
-// columns (all heads of a group share each K and V read), online softmax
-// per head with one cross-half exchange per block, O^T += V^T P^T with P^T
-// taken from registers.  The V cache is stored transposed ([head_dim,
-// positions] per sequence and group), and the K rows of a block are loaded in
-// an order that makes each lane's S^T accumulator hold consecutive positions,
-// so the V^T operand -- 8 positions of one head_dim row -- is one 16-byte
-// load straight from memory, with no transpose through LDS.
+// Inside a chunk the waves take rounds of 32 NWV positions, one block of 32
+// per wave, on bf16 MFMA (v_mfma_f32_32x32x16_bf16) with the same transposed
+// formulation as the attention core: S^T = K Q^T with the group's query
+// heads as the 32 columns (all heads of a group share each K and V read),
+// online softmax per head with one cross-half exchange per block, O^T +=
+// V^T P^T with P^T taken from registers.  The V cache is stored transposed
+// ([head_dim, positions] per sequence and group).
+// A round's K rows and V^T rows are staged in LDS by direct global->LDS
+// copies of whole cache lines (16-byte slots XOR-swizzled by row, so the
+// MFMA operand reads are conflict-free), two rounds in flight: every wave has
+// its next block requested while it computes, without holding it in
+// registers.  The K rows of a block are read in an order that makes each
+// lane's S^T accumulator hold consecutive positions, so the V^T operand -- 8
+// positions of one head_dim row -- is one 16-byte LDS read.
 // The waves merge through LDS; with several chunks, each workgroup writes
 // its softmax state (max, sum, unnormalised O) to the workspace and the last
 // of the sequence-group's chunks to arrive (one atomic) merges them.
@@ -37,6 +41,16 @@ constexpr int kMaxChunks = 32;  // position chunks per (sequence, group)
 // one per CU: measured faster than two per CU (fewer chunk states to write
 // and merge) -- B = 32, L = 2048: 21.2 us against 22.9; L = 8192: 37.8 against 41.6
 constexpr int kTargetWgs = 256;
+constexpr int kRP = 32 * NWV;   // positions per round: one block of 32 per wave
+constexpr int kRowB = 256;      // LDS bytes per staged row: 16 slots of 16 bytes
+
+// One round's stage: kRP K rows (head_dim padded to 128), then 32 HDT V^T
+// rows of kRP positions.  Two stages; after the loop the space holds the
+// waves' partial O^T for the merge.
+template <int HDT>
+constexpr int stage_bytes() { return (kRP + 32 * HDT) * kRowB; }
+template <int HDT>
+constexpr int dyn_lds_bytes() { return 2 * stage_bytes<HDT>(); }
 
 __device__ __forceinline__ int acc_row32(int r, int lane) {
   return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
@@ -55,8 +69,8 @@ __device__ __forceinline__ int key_pos(int i) {
 __host__ __device__ __forceinline__ int64_t rec_floats(int hdp) { return 32 * (int64_t)hdp + 64; }
 
 template <int HDT>
-// two waves per SIMD (the compiler then keeps O^T in VGPRs), so two
-// workgroups share a CU
+// register budget of two waves per SIMD (the compiler then keeps O^T in
+// VGPRs); the staging LDS leaves one workgroup per CU
 __global__ void __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(2)))
 attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ lens,
                    const uint16_t* __restrict__ qkv, uint16_t* __restrict__ Kc,
@@ -64,11 +78,13 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
                    unsigned* __restrict__ counters, float* __restrict__ part) {
   constexpr int KS = 2 * HDT;
   constexpr int HDP = 32 * HDT;  // head_dim padded to the O^T tiles
+  constexpr int SB = stage_bytes<HDT>();
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // the two stages
   __shared__ float fw[(kMaxChunks + 1) * 32];  // chunk merge weights, then 1/L
   __shared__ float mls[NWV][2][64];
-  __shared__ float ots[NWV - 1][HDT][16][64];
   __shared__ int is_last;
   __shared__ u32x4_t qs[KS][64];  // the Q operand, lane-linear
+  __shared__ u32x4_t knew[64];    // the new token: k chunks 0..15, v chunks 16..31
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -79,36 +95,30 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
   const int len = min(max(lens[b], 1), Lmax);
   const float scale = 1.0f / sqrtf((float)hd);
 
-  // new-token row of qkv and this group's cache rows
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qkv + (int64_t)b * N, (uint32_t)N * 2u);
+  // this group's cache rows, and the columns of its k and v in the qkv row
   const int64_t cache0 = ((int64_t)b * nkv + g) * Lmax * hd;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kc + cache0, (uint32_t)Lmax * (uint32_t)hd * 2u);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vc + cache0, (uint32_t)Lmax * (uint32_t)hd * 2u);
   const int kcol = (nq + g) * hd, vcol = (nq + nkv + g) * hd;
-
-  // ---- the new token's k and v into cache slot len-1 (chunk 0's first wave)
-  if (c == 0 && w == 0) {
-    for (int ch = lane; ch < hd / 8; ch += 64) {  // k: one row of the K cache
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qkv + (int64_t)b * N + kcol + ch * 8);
-      *reinterpret_cast<u32x4_t*>(Kc + cache0 + (int64_t)(len - 1) * hd + ch * 8) = v;
-    }
-    for (int d = lane; d < hd; d += 64)  // v: one column of the transposed V cache
-      Vc[cache0 + (int64_t)d * Lmax + (len - 1)] = qkv[(int64_t)b * N + vcol + d];
-  }
 
   // Q as the B operand: head h = lane % 32 of the group, chunk 2 ks + lane/32.
   // It is the same for every wave and every block, so it waits in LDS (wave
-  // 0 stages it) and is read again per block instead of holding registers.
+  // 0 copies it there) and is read again per block instead of holding
+  // registers.  Chunk 0's wave 1 copies the new token's k and v the same way.
+  // Both copies are issued ahead of the cache stream and waited on with it.
   const int h = lane & 31;
+  const u32x4_t qw = rsrc_words(qkv + (int64_t)b * N, (uint32_t)N * 2u);
   if (w == 0) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int ch = 2 * ks + (lane >> 5);
-      const uint32_t off = (h < G && ch * 8 < hd) ? (uint32_t)((g * G + h) * hd + ch * 8) * 2u : kOob;
-      qs[ks][lane] = buf_load16(rq, off);
+      lds_dma16(qw, (h < G && ch * 8 < hd) ? (uint32_t)((g * G + h) * hd + ch * 8) * 2u : kOob,
+                lds_addr(&qs[ks][0]));
     }
   }
-  __syncthreads();
+  if (w == 1 && c == 0) {
+    const int ch = lane & 15;
+    lds_dma16(qw, lane < 32 && ch * 8 < hd ? (uint32_t)((lane < 16 ? kcol : vcol) + ch * 8) * 2u : kOob,
+              lds_addr(&knew[0]));
+  }
 
   f32x16_t ot[HDT];
 #pragma unroll
@@ -120,35 +130,39 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
   // this chunk's cache positions [k0, k1); the new token at len-1 is folded
   // in after the loop
   const int k0 = c * Lc, k1 = min(k0 + Lc, len - 1);
-  // this wave's blocks kb = k0 + 32 w, + 32 NWV, ...; the next block's K and
-  // V are loaded while the current one is processed (past k1: zero)
-  auto load_k = [&](int kb, bf16x8_t (&kf)[KS]) {
-    const int p = kb + key_pos(lane & 31);
+  const int R = k1 > k0 ? (k1 - k0 + kRP - 1) / kRP : 0;  // rounds
+
+  // Round r into stage r & 1, every wave a share of the copies (positions at
+  // or past k1, chunks past head_dim: zero-filled, nothing fetched).  K: row
+  // i = position k0 + kRP r + i, slot j holds 16-byte chunk j ^ (i & 15).
+  // V^T: row d, slot j holds positions 8 (j ^ (d & 15)) .. + 7 of the
+  // round; a group of 8 that runs past len-2 is masked down to its cache
+  // positions when it is used (the rest of the slot may hold anything).
+  constexpr int NIK = kRP * 16 / (64 * NWV);  // K copies per wave and round
+  constexpr int NIV = HDP * 16 / (64 * NWV);  // V^T copies per wave and round
+  const u32x4_t kr = rsrc_words(Kc + cache0, (uint32_t)Lmax * (uint32_t)hd * 2u);
+  const u32x4_t vr = rsrc_words(Vc + cache0, (uint32_t)Lmax * (uint32_t)hd * 2u);
+  const uint32_t l0 = lds_addr(lds);
+  const int chn = hd / 8;
+  auto issue_round = [&](int r) {
+    const int P0 = k0 + kRP * r;
+    const uint32_t base = l0 + (uint32_t)((r & 1) * SB);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int ch = 2 * ks + (lane >> 5);
-      const uint32_t off = (kb < k1 && p < len - 1 && ch * 8 < hd)
-                               ? ((uint32_t)p * (uint32_t)hd + ch * 8) * 2u : kOob;
-      kf[ks] = __builtin_bit_cast(bf16x8_t, buf_load16(rk, off));
+    for (int i = 0; i < NIK; ++i) {
+      const int q = w + NWV * i;  // 1 KB of the stage: slots 64 q .. 64 q + 63
+      const int sl = q * 64 + lane;
+      const int row = sl >> 4, ch = (sl & 15) ^ (row & 15);
+      const int p = P0 + row;
+      lds_dma16(kr, p < k1 && ch < chn ? ((uint32_t)p * (uint32_t)hd + ch * 8) * 2u : kOob,
+                base + q * 1024);
     }
-  };
-  // V^T operand of 16-position step ks, tile t: head_dim row d = t*32 +
-  // lane%32, positions kb + 16 ks + 8 (lane/32) + 0..7 -- the key order of
-  // the S^T accumulator; past k1 or head_dim, zero.  A group of 8 that runs
-  // past len-2 is masked down to its cache positions when it is used (the
-  // rest of the slot may hold anything), so no load is waited on early.
-  auto load_v = [&](int kb, u32x4_t (&vr)[2][HDT]) {
-    const int half = lane >> 5;
 #pragma unroll
-    for (int t = 0; t < HDT; ++t) {
-      const int d = t * 32 + (lane & 31);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int p0 = kb + ks * 16 + half * 8;
-        const uint32_t off = (kb < k1 && d < hd && p0 < len - 1)
-                                 ? ((uint32_t)d * (uint32_t)Lmax + (uint32_t)p0) * 2u : kOob;
-        vr[ks][t] = buf_load16(rv, off);
-      }
+    for (int i = 0; i < NIV; ++i) {
+      const int q = w + NWV * i;
+      const int sl = q * 64 + lane;
+      const int d = sl >> 4, p0 = P0 + 8 * ((sl & 15) ^ (d & 15));
+      lds_dma16(vr, p0 < k1 && d < hd ? ((uint32_t)d * (uint32_t)Lmax + (uint32_t)p0) * 2u : kOob,
+                base + kRP * kRowB + q * 1024);
     }
   };
   auto v_mask = [&](int kb, int ks) {  // keep positions below len-1
@@ -158,17 +172,23 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
     for (int q = 0; q < 4; ++q) m[q] = nv >= 2 * q + 2 ? 0xffffffffu : nv == 2 * q + 1 ? 0xffffu : 0u;
     return m;
   };
-  // One block: S^T = K Q^T, online softmax, O^T += V^T P^T.  The next
-  // block's K and V are loaded before the current block is processed.
-  auto process = [&](int kb, const bf16x8_t (&kf)[KS], const u32x4_t (&vc)[2][HDT]) {
+  // One block (this wave's 32 positions of the stage): S^T = K Q^T, online
+  // softmax, O^T += V^T P^T.
+  auto process = [&](int kb, const unsigned char* stage) {
+    const unsigned char* sk = stage + 32 * w * kRowB;  // this wave's K rows
+    const unsigned char* sv = stage + kRP * kRowB;     // the round's V^T rows
     f32x16_t st;
 #pragma unroll
     for (int r = 0; r < 16; ++r) st[r] = 0.0f;
-    asm volatile("" ::: "memory");  // read Q from LDS again: do not hold it across blocks
+    const int krow = key_pos(lane & 31);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], __builtin_bit_cast(bf16x8_t, qs[ks][lane]),
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch = 2 * ks + (lane >> 5);
+      const bf16x8_t kv =
+          *reinterpret_cast<const bf16x8_t*>(sk + krow * kRowB + ((ch ^ (krow & 15)) << 4));
+      st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, __builtin_bit_cast(bf16x8_t, qs[ks][lane]),
                                                    st, 0, 0, 0);
+    }
     float x[16];
     float mx = -INFINITY;
 #pragma unroll
@@ -197,41 +217,60 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4_t vm = v_mask(kb, ks);
+      const int pc = 4 * w + 2 * ks + (lane >> 5);  // 8-position group within the round
 #pragma unroll
       for (int t = 0; t < HDT; ++t) {
-        const u32x4_t vv = vc[ks][t] & vm;
+        const int d = t * 32 + (lane & 31);
+        const u32x4_t vv =
+            *reinterpret_cast<const u32x4_t*>(sv + d * kRowB + ((pc ^ (d & 15)) << 4)) & vm;
         ot[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pb[ks],
                                                         ot[t], 0, 0, 0);
       }
     }
   };
-  constexpr int kStep = 32 * NWV;
-  bf16x8_t kf[KS];
-  u32x4_t vr[2][HDT];
-  load_k(k0 + 32 * w, kf);
-  load_v(k0 + 32 * w, vr);
-  for (int kb = k0 + 32 * w; kb < k1; kb += kStep) {
-    bf16x8_t kc[KS];
-    u32x4_t vc[2][HDT];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kc[ks] = kf[ks];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int t = 0; t < HDT; ++t) vc[ks][t] = vr[ks][t];
-    load_k(kb + kStep, kf);
-    load_v(kb + kStep, vr);
-    process(kb, kc, vc);
+  // Two rounds in flight.  A wave's copies are its only vector-memory
+  // operations here, so "round r has landed" is "at most the NIK + NIV
+  // copies of round r + 1 are outstanding", and Q and the new token (older
+  // than every round) have landed once the first rounds' copies alone are.
+  if (R > 0) issue_round(0);
+  if (R > 1) issue_round(1);
+  if (R > 1)
+    wait_vmcnt<2 * (NIK + NIV)>();
+  else if (R == 1)
+    wait_vmcnt<NIK + NIV>();
+  else
+    wait_vmcnt<0>();
+  __syncthreads();  // Q and the new token in LDS
+  for (int r = 0; r < R; ++r) {
+    if (r + 1 < R)
+      wait_vmcnt<NIK + NIV>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();  // round r staged by every wave
+    const int kb = k0 + kRP * r + 32 * w;
+    if (kb < k1) process(kb, lds + (r & 1) * SB);
+    __syncthreads();  // every wave is done with stage r & 1
+    if (r + 2 < R) issue_round(r + 2);
   }
 
   // ---- the new token (position len-1) into chunk 0's wave 0: one more
   //      online-softmax step with a single key, s = scale q.k_new per head
+  //      (chunk 0's wave 1 meanwhile stores its k row and v column into
+  //      cache slot len-1 for the next step; no copy above read that slot
+  //      unmasked)
+  if (c == 0 && w == 1) {
+    if (lane < hd / 8)  // k: one row of the K cache
+      *reinterpret_cast<u32x4_t*>(Kc + cache0 + (int64_t)(len - 1) * hd + lane * 8) = knew[lane];
+    const uint16_t* vn = reinterpret_cast<const uint16_t*>(&knew[16]);
+    for (int d = lane; d < hd; d += 64)  // v: one column of the transposed V cache
+      Vc[cache0 + (int64_t)d * Lmax + (len - 1)] = vn[d];
+  }
   if (c == 0 && w == 0) {
     float dot = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int ch = 2 * ks + (lane >> 5);
-      const u32x4_t kn = buf_load16(rq, ch * 8 < hd ? (uint32_t)(kcol + ch * 8) * 2u : kOob);
+      const u32x4_t kn = knew[ch];  // zero past head_dim
       const u32x4_t qq = qs[ks][lane];
 #pragma unroll
       for (int e = 0; e < 4; ++e) dot = dot2_bf16(qq[e], kn[e], dot);
@@ -246,9 +285,8 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
     for (int t = 0; t < HDT; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {  // rows t*32 + 8 j + 4 (lane/32) + {0..3}
-        const int d0 = t * 32 + 8 * j + 4 * (lane >> 5);
-        const u32x2_t vn = __builtin_amdgcn_raw_buffer_load_b64(
-            rq, d0 < hd ? (uint32_t)(vcol + d0) * 2u : kOob, 0, 0);
+        const u32x4_t vc = knew[16 + 4 * t + j];  // v_new[8 (4 t + j) ..], zero past head_dim
+        const u32x2_t vn = (lane >> 5) ? u32x2_t{vc[2], vc[3]} : u32x2_t{vc[0], vc[1]};
         const float vv[4] = {bf16_bits_to_f32(vn.x & 0xffffu), bf16_bits_to_f32(vn.x >> 16),
                              bf16_bits_to_f32(vn.y & 0xffffu), bf16_bits_to_f32(vn.y >> 16)};
 #pragma unroll
@@ -256,14 +294,19 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
       }
   }
 
-  // ---- merge the waves into wave 0
+  // ---- merge the waves into wave 0 (through the stage space: the loop's
+  //      last barrier follows the last copy's wait and every wave's reads)
+  f32x4_t (*ots)[HDT][4][64] = reinterpret_cast<f32x4_t (*)[HDT][4][64]>(lds);
+  static_assert((NWV - 1) * HDT * 4 * 64 * 16 <= 2 * SB, "the merge fits the stages");
   if (w > 0) {
     mls[w][0][lane] = m;
     mls[w][1][lane] = l;
 #pragma unroll
     for (int t = 0; t < HDT; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ots[w - 1][t][r][lane] = ot[t][r];
+      for (int q = 0; q < 4; ++q)
+        ots[w - 1][t][q][lane] =
+            f32x4_t{ot[t][4 * q], ot[t][4 * q + 1], ot[t][4 * q + 2], ot[t][4 * q + 3]};
   }
   __syncthreads();
   if (w == 0) {
@@ -282,7 +325,11 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
 #pragma unroll
       for (int t = 0; t < HDT; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ot[t][r] += ots[v - 1][t][r][lane] * f;
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t o4 = ots[v - 1][t][q][lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ot[t][4 * q + e] += o4[e] * f;
+        }
     }
     m = mm;
   }
@@ -347,8 +394,8 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
     o[e] = __builtin_amdgcn_raw_buffer_load_b128(
         pr, item && e < NC ? (uint32_t)((first + e * rec + hh0 * HDP + col0) * 4) : kOob, 0,
         kAuxSys);
-  float* mlp = &ots[0][0][0][0];  // [kMaxChunks][32] (max, sum) pairs
-  static_assert((NWV - 1) * HDT * 16 * 64 >= 2 * kMaxChunks * 32, "merge scratch fits");
+  float* mlp = reinterpret_cast<float*>(lds);  // [kMaxChunks][32] (max, sum) pairs
+  static_assert(2 * kMaxChunks * 32 * 4 <= 2 * SB, "merge scratch fits");
 #pragma unroll
   for (int j = 0; j < (kMaxChunks * 32) / (64 * NWV); ++j) {
     const int i = threadIdx.x + 64 * NWV * j;  // chunk i / 32, head i % 32
@@ -434,7 +481,16 @@ hipError_t launch_hdt(int B, int nq, int nkv, int hd, int Lmax, const int* lens,
   float* part = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                      kWsCounterBytes)
                           : nullptr;
-  hipLaunchKernelGGL(attn_decode_kernel<HDT>, dim3(B * nkv * pl.nc), dim3(64 * NWV), 0, stream,
+  static bool attr_set = false;  // raising the dynamic-LDS limit once per process is enough
+  if (!attr_set) {
+    const hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(attn_decode_kernel<HDT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, dyn_lds_bytes<HDT>());
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(attn_decode_kernel<HDT>, dim3(B * nkv * pl.nc), dim3(64 * NWV),
+                     dyn_lds_bytes<HDT>(), stream,
                      nq, nkv, hd, Lmax, lens, qkv, Kc, Vc, A, pl.nc, pl.lc, counters, part);
   return hipGetLastError();
 }
