@@ -54,6 +54,10 @@ def _run(qkv, Kc, Vc, lens, nq, nkv, hd, workspace=None):
     (3, 8, 2, 64, 104, 3),       # two groups of 4 heads
     (5, 4, 4, 32, 72, 4),        # one head per group
     (7, 4, 1, 40, 8, 5),         # head_dim not a multiple of 32, a cache of 8 positions
+    (4, 8, 1, 128, 192, 6),      # chunks of 96 positions: a round with one wave idle
+    (2, 8, 1, 128, 1000, 7),     # the last chunk's round partly past the cache
+    (32, 8, 1, 128, 2144, 8),    # three rounds per chunk, the last one a single block
+    (16, 8, 2, 64, 1600, 9),     # two groups, rounds of 128 and 96 positions
 ])
 def test_attn_decode(orc, B, nq, nkv, hd, Lmax, seed):
     rng = np.random.default_rng(seed)
