@@ -14,9 +14,11 @@
 //     query's 32 scores and lane ^ 32 the other 16, so the running max and
 //     sum need one exchange each per key block;
 //   * O^T += V^T P^T: P^T comes straight from the score registers (rounded
-//     to bf16) as the B operand; V is staged transposed in LDS, keys in the
-//     accumulator's order, so the A operand is one 16-byte read; the per-query
-//     rescale is lane-local;
+//     to bf16) as the B operand; the key block's V rows are staged in LDS as
+//     they are loaded (16-byte chunks XOR-swizzled by key, conflict-free
+//     writes), and each lane gathers its V^T operand -- 8 keys of one
+//     head_dim column, in the accumulator's key order -- with 2-byte reads
+//     that are conflict-free too; the per-query rescale is lane-local;
 //   * head_dim up to 256 in 32-row tiles of O^T (HDT of them); columns past
 //     head_dim read zero and are not stored;
 //   * the next key block's K and V are loaded while the current one is
@@ -31,7 +33,6 @@ namespace tpk {
 namespace {
 
 constexpr uint32_t kOob = 0x80000000u;  // buffer offset past any record: reads zero
-constexpr int kVStride = 40;            // bf16 per LDS row of V^T (32 keys + pad)
 
 // Row (query within the block) of accumulator element r held by `lane`; the
 // column (key, or output column) is lane % 32.
@@ -39,31 +40,23 @@ __device__ __forceinline__ int acc_row32(int r, int lane) {
   return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
 }
 
-__device__ __forceinline__ float half_wave_max(float v) {
-#pragma unroll
-  for (int m = 1; m < 32; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
-}
-__device__ __forceinline__ float half_wave_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < 32; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
 
 template <int HDT, int NWV>
 __global__ void __launch_bounds__(64 * NWV)
 attn_core_kernel(int I, int S, int nq, int nkv, int hd, const uint16_t* __restrict__ qkv,
                  uint16_t* __restrict__ A) {
   constexpr int KS = 2 * HDT;  // 16-wide steps along head_dim
-  constexpr int kVt = 32 * HDT * kVStride;  // bf16 per wave's V^T tile
-  __shared__ __attribute__((aligned(16))) uint16_t Vts[NWV * kVt];
+  // a wave's key block of V: 32 rows of CPR 16-byte chunk slots; chunk c of
+  // key k sits in slot c ^ (k mod CPR)
+  constexpr int CPR = 4 * HDT <= 16 ? 16 : 32;
+  __shared__ u32x4_t Vrs[NWV][32 * CPR];
   // partial results of waves 1.. for the merge: max and sum, then O^T tiles
   __shared__ float mls[NWV][2][64];
   __shared__ float ots[NWV > 1 ? NWV - 1 : 1][HDT][16][64];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // key blocks w, w + NWV, ...
-  uint16_t* Vt = Vts + w * kVt;
+  u32x4_t* Vr = Vrs[w];
   const int i0 = blockIdx.x * 32;
   const int j = blockIdx.y;
   const int g = (j * nkv) / nq;  // KV group of local head j
@@ -126,20 +119,12 @@ attn_core_kernel(int I, int S, int nq, int nkv, int hd, const uint16_t* __restri
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], st, 0, 0, 0);
-    // ---- V^T of the key block into LDS.  Key k of the block sits at
-    //      position k with bits 2 and 3 swapped: the order in which the S^T
-    //      accumulator holds keys, so that one 16-byte read gives the A
-    //      operand matching the P^T fragment taken from the accumulator.
+    // ---- the key block's V rows into LDS, 16 bytes per lane and chunk
 #pragma unroll
     for (int u = 0; u < 2 * HDT; ++u) {
       const int q = lane + 64 * u;
       const int key = q / (4 * HDT), c = q % (4 * HDT);
-      const int pos = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(c * 8 + 2 * e) * kVStride + pos] = (uint16_t)(vr[u][e] & 0xffffu);
-        Vt[(c * 8 + 2 * e + 1) * kVStride + pos] = (uint16_t)(vr[u][e] >> 16);
-      }
+      Vr[key * CPR + (c ^ (key & (CPR - 1)))] = vr[u];
     }
     // this wave's next block's loads (past the last block they read zero)
     const int nb = kb + 32 * NWV <= last ? kb + 32 * NWV : I;
@@ -176,13 +161,29 @@ attn_core_kernel(int I, int S, int nq, int nkv, int hd, const uint16_t* __restri
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- O^T += V^T P^T: A = V^T[32 columns][16 keys], B = P^T[16 keys][query]
+    // ---- O^T += V^T P^T: A = V^T[32 columns][16 keys], B = P^T[16 keys][query].
+    //      Element e of a lane's P^T fragment for step ks holds key
+    //      16 ks + 8 (e / 4) + 4 (lane / 32) + e % 4 (the accumulator's
+    //      order), so the A operand's element e is V[that key][column].
+    const uint16_t* Vh = reinterpret_cast<const uint16_t*>(Vr);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int t = 0; t < HDT; ++t) {
-        const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(
-            &Vt[(t * 32 + (lane & 31)) * kVStride + ks * 16 + (lane >> 5) * 8]);
+        const int d = t * 32 + (lane & 31);
+        uint32_t v2[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t half[2];
+#pragma unroll
+          for (int b2 = 0; b2 < 2; ++b2) {
+            const int e = 2 * i + b2;
+            const int key = 16 * ks + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            half[b2] = Vh[(key * CPR + ((d >> 3) ^ (key & (CPR - 1)))) * 8 + (d & 7)];
+          }
+          v2[i] = half[0] | (half[1] << 16);
+        }
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{v2[0], v2[1], v2[2], v2[3]});
         ot[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ks], ot[t], 0, 0, 0);
       }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
