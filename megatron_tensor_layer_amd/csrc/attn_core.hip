@@ -52,7 +52,6 @@ attn_core_kernel(int I, int S, int nq, int nkv, int hd, const uint16_t* __restri
   __shared__ u32x4_t Vrs[NWV][32 * CPR];
   // partial results of waves 1.. for the merge: max and sum, then O^T tiles
   __shared__ float mls[NWV][2][64];
-  __shared__ float ots[NWV > 1 ? NWV - 1 : 1][HDT][16][64];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // key blocks w, w + NWV, ...
@@ -191,36 +190,47 @@ attn_core_kernel(int I, int S, int nq, int nkv, int hd, const uint16_t* __restri
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // ---- merge the waves' partial softmax states into wave 0:
-  //      O = sum_w O_w e^(m_w - M), l = sum_w l_w e^(m_w - M), M = max_w m_w
+  // ---- merge the waves' partial softmax states into wave 0 in halving
+  //      steps (wave w takes wave w + h, h = NWV/2 .. 1):
+  //      O = O_a e^(m_a - M) + O_b e^(m_b - M), l likewise, M = max(m_a, m_b).
+  //      The partial O^T tiles pass through the V staging space, free once
+  //      every wave has left the key loop.
   if constexpr (NWV > 1) {
-    if (w > 0) {
-      mls[w][0][lane] = m;
-      mls[w][1][lane] = l;
+    f32x4_t (*ots)[HDT][4][64] = reinterpret_cast<f32x4_t (*)[HDT][4][64]>(&Vrs[0][0]);
+    static_assert((NWV / 2) * HDT * 4 * 64 * 16 <= (int)sizeof(Vrs), "the merge fits the V space");
+    __syncthreads();  // every wave is done with its V tile
 #pragma unroll
-      for (int t = 0; t < HDT; ++t)
+    for (int h = NWV / 2; h >= 1; h /= 2) {
+      if (w >= h && w < 2 * h) {
+        mls[w][0][lane] = m;
+        mls[w][1][lane] = l;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ots[w - 1][t][r][lane] = ot[t][r];
+        for (int t = 0; t < HDT; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            ots[w - h][t][q][lane] =
+                f32x4_t{ot[t][4 * q], ot[t][4 * q + 1], ot[t][4 * q + 2], ot[t][4 * q + 3]};
+      }
+      __syncthreads();
+      if (w < h) {
+        const float m2 = mls[w + h][0][lane];
+        const float mm = fmaxf(m, m2);
+        const float base = (mm == -INFINITY) ? 0.0f : mm;
+        const float f1 = expf(m - base), f2 = expf(m2 - base);
+        l = l * f1 + mls[w + h][1][lane] * f2;
+        m = mm;
+#pragma unroll
+        for (int t = 0; t < HDT; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4_t o2 = ots[w][t][q][lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ot[t][4 * q + e] = ot[t][4 * q + e] * f1 + o2[e] * f2;
+          }
+      }
+      __syncthreads();  // slots and sums are free for the next step
     }
-    __syncthreads();
     if (w > 0) return;
-    float mm = m;
-#pragma unroll
-    for (int v = 1; v < NWV; ++v) mm = fmaxf(mm, mls[v][0][lane]);
-    const float base = (mm == -INFINITY) ? 0.0f : mm;
-    const float f0 = expf(m - base);
-    l *= f0;
-#pragma unroll
-    for (int t = 0; t < HDT; ++t) ot[t] *= f0;
-#pragma unroll
-    for (int v = 1; v < NWV; ++v) {
-      const float f = expf(mls[v][0][lane] - base);
-      l += mls[v][1][lane] * f;
-#pragma unroll
-      for (int t = 0; t < HDT; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ot[t][r] += ots[v - 1][t][r][lane] * f;
-    }
   }
 
   // ---- A[query][column] = O / l, bf16
@@ -255,8 +265,10 @@ attn_single_key_kernel(int I, int nq, int nkv, int hd, const uint16_t* __restric
   }
 }
 
-// Waves per workgroup: 4 (2 above head_dim 128, for LDS), or 1 when every
-// sequence fits one key block.
+// Waves per workgroup: 4, 8 from sequences of 1024 tokens (the longest query
+// blocks have 32 and more key blocks: 87 against 103 us at 2048 tokens of a
+// TP=8 Llama-70B rank, while 512 tokens take 21.2 against 20.0 us), 2 above
+// head_dim 128 (for LDS), or 1 when every sequence fits one key block.
 template <int HDT>
 hipError_t launch_hdt(int I, int S, int nq, int nkv, int hd, const uint16_t* qkv, uint16_t* A,
                       hipStream_t stream) {
@@ -264,10 +276,15 @@ hipError_t launch_hdt(int I, int S, int nq, int nkv, int hd, const uint16_t* qkv
   if (S <= 32) {
     hipLaunchKernelGGL((attn_core_kernel<HDT, 1>), grid, dim3(64), 0, stream, I, S, nq, nkv, hd,
                        qkv, A);
+  } else if (HDT > 4) {
+    hipLaunchKernelGGL((attn_core_kernel<HDT, 2>), grid, dim3(128), 0, stream, I, S, nq, nkv, hd,
+                       qkv, A);
+  } else if (S >= 1024) {
+    hipLaunchKernelGGL((attn_core_kernel<HDT, 8>), grid, dim3(512), 0, stream, I, S, nq, nkv, hd,
+                       qkv, A);
   } else {
-    constexpr int NWV = HDT <= 4 ? 4 : 2;
-    hipLaunchKernelGGL((attn_core_kernel<HDT, NWV>), grid, dim3(64 * NWV), 0, stream, I, S, nq,
-                       nkv, hd, qkv, A);
+    hipLaunchKernelGGL((attn_core_kernel<HDT, 4>), grid, dim3(256), 0, stream, I, S, nq, nkv, hd,
+                       qkv, A);
   }
   return hipGetLastError();
 }
