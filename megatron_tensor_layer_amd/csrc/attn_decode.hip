@@ -294,57 +294,63 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
       }
   }
 
-  // ---- merge the waves into wave 0 (through the stage space: the loop's
-  //      last barrier follows the last copy's wait and every wave's reads)
+  // ---- merge the waves: each leaves its (max, sum) and its O^T tiles in the
+  //      stage space (free: the loop's last barrier follows the last copy's
+  //      wait and every wave's reads), then wave w merges tiles t = w mod NWV
+  //      of all waves, in wave order, and keeps them in its registers
   f32x4_t (*ots)[HDT][4][64] = reinterpret_cast<f32x4_t (*)[HDT][4][64]>(lds);
-  static_assert((NWV - 1) * HDT * 4 * 64 * 16 <= 2 * SB, "the merge fits the stages");
-  if (w > 0) {
-    mls[w][0][lane] = m;
-    mls[w][1][lane] = l;
+  static_assert(NWV * HDT * 4 * 64 * 16 <= 2 * SB, "the merge fits the stages");
+  mls[w][0][lane] = m;
+  mls[w][1][lane] = l;
 #pragma unroll
-    for (int t = 0; t < HDT; ++t)
+  for (int t = 0; t < HDT; ++t)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        ots[w - 1][t][q][lane] =
-            f32x4_t{ot[t][4 * q], ot[t][4 * q + 1], ot[t][4 * q + 2], ot[t][4 * q + 3]};
-  }
+    for (int q = 0; q < 4; ++q)
+      ots[w][t][q][lane] = f32x4_t{ot[t][4 * q], ot[t][4 * q + 1], ot[t][4 * q + 2], ot[t][4 * q + 3]};
   __syncthreads();
-  if (w == 0) {
-    float mm = m;
+  {
+    float mm = mls[0][0][lane];
 #pragma unroll
     for (int v = 1; v < NWV; ++v) mm = fmaxf(mm, mls[v][0][lane]);
     const float base = (mm == -INFINITY) ? 0.0f : mm;
-    const float f0 = expf(m - base);
-    l *= f0;
+    float fv[NWV];
 #pragma unroll
-    for (int t = 0; t < HDT; ++t) ot[t] *= f0;
+    for (int v = 0; v < NWV; ++v) fv[v] = expf(mls[v][0][lane] - base);
+    l = mls[0][1][lane] * fv[0];
 #pragma unroll
-    for (int v = 1; v < NWV; ++v) {
-      const float f = expf(mls[v][0][lane] - base);
-      l += mls[v][1][lane] * f;
-#pragma unroll
-      for (int t = 0; t < HDT; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4_t o4 = ots[v - 1][t][q][lane];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ot[t][4 * q + e] += o4[e] * f;
-        }
-    }
+    for (int v = 1; v < NWV; ++v) l += mls[v][1][lane] * fv[v];
     m = mm;
+#pragma unroll
+    for (int t = 0; t < HDT; ++t) {
+      if (t % NWV != w) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4_t o4 = ots[0][t][q][lane] * fv[0];
+#pragma unroll
+        for (int v = 1; v < NWV; ++v) {
+          const f32x4_t ov = ots[v][t][q][lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] += ov[e] * fv[v];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ot[t][4 * q + e] = o4[e];
+      }
+    }
   }
 
-  if (NC == 1) {  // ---- the one chunk: A = O / l
-    if (w == 0 && h < G) {
+  if (NC == 1) {  // ---- the one chunk: A = O / l, each wave its tiles
+    if (h < G) {
       const float inv = 1.0f / l;
 #pragma unroll
-      for (int t = 0; t < HDT; ++t)
+      for (int t = 0; t < HDT; ++t) {
+        if (t % NWV != w) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int col = t * 32 + acc_row32(r, lane);
           if (col < hd)
             A[(int64_t)b * (nq * hd) + (g * G + h) * hd + col] = f32_to_bf16_bits(ot[t][r] * inv);
         }
+      }
     }
     return;
   }
@@ -354,10 +360,12 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
   const int64_t nrec = (int64_t)gridDim.x;
   const __amdgpu_buffer_rsrc_t pr = make_rsrc(part, (uint32_t)(nrec * rec * 4));
   const int64_t my = (int64_t)blockIdx.x * rec;
-  if (w == 0 && h < G) {  // lanes of padding heads (h >= G) store nothing
-    // lane holds head h, rows t*32 + 8 j + 4 (lane/32) + {0..3}: 16 bytes each
+  if (h < G) {  // lanes of padding heads (h >= G) store nothing
+    // each wave its merged tiles; lane holds head h, rows t*32 + 8 j +
+    // 4 (lane/32) + {0..3}: 16 bytes each
 #pragma unroll
-    for (int t = 0; t < HDT; ++t)
+    for (int t = 0; t < HDT; ++t) {
+      if (t % NWV != w) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4_t v = f32x4_t{ot[t][4 * j], ot[t][4 * j + 1], ot[t][4 * j + 2], ot[t][4 * j + 3]};
@@ -365,7 +373,8 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
             __builtin_bit_cast(u32x4_t, v), pr,
             (uint32_t)((my + h * HDP + t * 32 + 8 * j + 4 * (lane >> 5)) * 4), 0, kAuxSys);
       }
-    if (lane < 32) {
+    }
+    if (w == 0 && lane < 32) {
       const u32x2_t ml = u32x2_t{__builtin_bit_cast(uint32_t, m), __builtin_bit_cast(uint32_t, l)};
       __builtin_amdgcn_raw_buffer_store_b64(ml, pr,
                                             (uint32_t)((my + 32 * HDP + 2 * h) * 4), 0, kAuxSys);
