@@ -155,8 +155,12 @@ attn_core_kernel(int I, int S, int nq, int nkv, int hd, const uint16_t* __restri
     ps += __shfl_xor(ps, 32, 64);
     l = l * corr + ps;
     m = mnew;
+    // O^T is rescaled by e^(m_old - m_new) only when some lane's max moved:
+    // otherwise the factor is exactly 1 in every lane (a wave-uniform test)
+    if (__builtin_amdgcn_ballot_w64(corr != 1.0f) != 0) {
 #pragma unroll
-    for (int t = 0; t < HDT; ++t) ot[t] *= corr;
+      for (int t = 0; t < HDT; ++t) ot[t] *= corr;
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -234,14 +238,17 @@ attn_core_kernel(int I, int S, int nq, int nkv, int hd, const uint16_t* __restri
   }
 
   // ---- A[query][column] = O / l, bf16
-  if (qi < I) {
+  if (qi < I) {  // elements 4 a .. 4 a + 3 of a tile are 4 adjacent columns: one 8-byte store
     const float inv = 1.0f / l;
 #pragma unroll
     for (int t = 0; t < HDT; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int col = t * 32 + acc_row32(r, lane);
-        if (col < hd) A[(int64_t)qi * (nq * hd) + j * hd + col] = f32_to_bf16_bits(ot[t][r] * inv);
+      for (int a = 0; a < 4; ++a) {
+        const int col = t * 32 + acc_row32(4 * a, lane);
+        if (col < hd)  // head_dim is a multiple of 8: the 4 columns are all in or all out
+          *reinterpret_cast<u32x2_t*>(A + (int64_t)qi * (nq * hd) + j * hd + col) =
+              u32x2_t{pack_bf16x2(ot[t][4 * a] * inv, ot[t][4 * a + 1] * inv),
+                      pack_bf16x2(ot[t][4 * a + 2] * inv, ot[t][4 * a + 3] * inv)};
       }
   }
 }
@@ -265,10 +272,9 @@ attn_single_key_kernel(int I, int nq, int nkv, int hd, const uint16_t* __restric
   }
 }
 
-// Waves per workgroup: 4, 8 from sequences of 1024 tokens (the longest query
-// blocks have 32 and more key blocks: 87 against 103 us at 2048 tokens of a
-// TP=8 Llama-70B rank, while 512 tokens take 21.2 against 20.0 us), 2 above
-// head_dim 128 (for LDS), or 1 when every sequence fits one key block.
+// Waves per workgroup: 4 (8 measured no faster: each wave's block loop is
+// bound by its own instruction stream, which two waves per SIMD share), 2
+// above head_dim 128 (for LDS), or 1 when every sequence fits one key block.
 template <int HDT>
 hipError_t launch_hdt(int I, int S, int nq, int nkv, int hd, const uint16_t* qkv, uint16_t* A,
                       hipStream_t stream) {
@@ -278,9 +284,6 @@ hipError_t launch_hdt(int I, int S, int nq, int nkv, int hd, const uint16_t* qkv
                        qkv, A);
   } else if (HDT > 4) {
     hipLaunchKernelGGL((attn_core_kernel<HDT, 2>), grid, dim3(128), 0, stream, I, S, nq, nkv, hd,
-                       qkv, A);
-  } else if (S >= 1024) {
-    hipLaunchKernelGGL((attn_core_kernel<HDT, 8>), grid, dim3(512), 0, stream, I, S, nq, nkv, hd,
                        qkv, A);
   } else {
     hipLaunchKernelGGL((attn_core_kernel<HDT, 4>), grid, dim3(256), 0, stream, I, S, nq, nkv, hd,

@@ -212,8 +212,12 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
     ps += __shfl_xor(ps, 32, 64);
     l = l * corr + ps;
     m = mnew;
+    // O^T is rescaled by e^(m_old - m_new) only when some lane's max moved:
+    // otherwise the factor is exactly 1 in every lane (a wave-uniform test)
+    if (__builtin_amdgcn_ballot_w64(corr != 1.0f) != 0) {
 #pragma unroll
-    for (int t = 0; t < HDT; ++t) ot[t] *= corr;
+      for (int t = 0; t < HDT; ++t) ot[t] *= corr;
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4_t vm = v_mask(kb, ks);
@@ -345,10 +349,12 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
       for (int t = 0; t < HDT; ++t) {
         if (t % NWV != w) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int col = t * 32 + acc_row32(r, lane);
+        for (int a = 0; a < 4; ++a) {  // 4 adjacent columns per 8-byte store
+          const int col = t * 32 + acc_row32(4 * a, lane);
           if (col < hd)
-            A[(int64_t)b * (nq * hd) + (g * G + h) * hd + col] = f32_to_bf16_bits(ot[t][r] * inv);
+            *reinterpret_cast<u32x2_t*>(A + (int64_t)b * (nq * hd) + (g * G + h) * hd + col) =
+                u32x2_t{pack_bf16x2(ot[t][4 * a] * inv, ot[t][4 * a + 1] * inv),
+                        pack_bf16x2(ot[t][4 * a + 2] * inv, ot[t][4 * a + 3] * inv)};
         }
       }
     }
