@@ -9,7 +9,8 @@
 //   * S^T = K Q^T per block of 32 keys: K rows (A operand) and the block's Q
 //     (B operand, kept in registers) are both read as 16-byte chunks along
 //     head_dim, as the QKV projection writes them;
-//   * scale 1/sqrt(hd), causal mask inside each sequence (query i sees keys
+//   * scale 1/sqrt(hd) (scores kept in base 2, so each exponential is one
+//     exp2), causal mask inside each sequence (query i sees keys
 //     s0(i)..i, s0 = the first row of its sequence); the lane holds 16 of its
 //     query's 32 scores and lane ^ 32 the other 16, so the running max and
 //     sum need one exchange each per key block;
@@ -62,7 +63,9 @@ attn_core_kernel(int I, int S, int nq, int nkv, int hd, const uint16_t* __restri
   const int N = (nq + 2 * nkv) * hd;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(qkv, (uint32_t)I * (uint32_t)N * 2u);
   const int qcol = j * hd, kcol = (nq + g) * hd, vcol = (nq + nkv + g) * hd;
-  const float scale = 1.0f / sqrtf((float)hd);
+  // scores in base 2: s = log2(e) q.k / sqrt(hd), so every exponential is
+  // one exp2 (e^z = 2^(z log2 e))
+  const float scale = 1.4426950408889634f / sqrtf((float)hd);
 
   // 16-byte chunk c of row `row` of the head starting at `col0` (zero past
   // head_dim or past the last row)
@@ -133,29 +136,39 @@ attn_core_kernel(int I, int S, int nq, int nkv, int hd, const uint16_t* __restri
     //      16 of its keys here, the other 16 in lane ^ 32
     float x[16];
     float mx = -INFINITY;
+    // the mask is needed only where some lane's query does not see all 32
+    // keys of the block (the diagonal block, a sequence start, rows past I)
+    if (__builtin_amdgcn_ballot_w64(!(kb >= qlo && kb + 31 <= qi && qi < I)) != 0) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kb + acc_row32(r, lane);
-      const bool ok = key <= qi && key >= qlo && qi < I;
-      x[r] = ok ? st[r] * scale : -INFINITY;
-      mx = fmaxf(mx, x[r]);
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb + acc_row32(r, lane);
+        const bool ok = key <= qi && key >= qlo && qi < I;
+        x[r] = ok ? st[r] * scale : -INFINITY;
+        mx = fmaxf(mx, x[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        x[r] = st[r] * scale;
+        mx = fmaxf(mx, x[r]);
+      }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mnew = fmaxf(m, mx);
     const float base = (mnew == -INFINITY) ? 0.0f : mnew;  // no key seen yet
-    const float corr = expf(m - base);
+    const float corr = exp2f(m - base);
     float ps = 0.0f;
     bf16x8_t pb[2];  // P^T as the B operand: 8 keys per 16-key step
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = expf(x[r] - base);
+      const float p = exp2f(x[r] - base);
       ps += p;
       pb[r >> 3][r & 7] = (__bf16)p;
     }
     ps += __shfl_xor(ps, 32, 64);
     l = l * corr + ps;
     m = mnew;
-    // O^T is rescaled by e^(m_old - m_new) only when some lane's max moved:
+    // O^T is rescaled by 2^(m_old - m_new) only when some lane's max moved:
     // otherwise the factor is exactly 1 in every lane (a wave-uniform test)
     if (__builtin_amdgcn_ballot_w64(corr != 1.0f) != 0) {
 #pragma unroll
@@ -196,7 +209,7 @@ attn_core_kernel(int I, int S, int nq, int nkv, int hd, const uint16_t* __restri
 
   // ---- merge the waves' partial softmax states into wave 0 in halving
   //      steps (wave w takes wave w + h, h = NWV/2 .. 1):
-  //      O = O_a e^(m_a - M) + O_b e^(m_b - M), l likewise, M = max(m_a, m_b).
+  //      O = O_a 2^(m_a - M) + O_b 2^(m_b - M), l likewise, M = max(m_a, m_b).
   //      The partial O^T tiles pass through the V staging space, free once
   //      every wave has left the key loop.
   if constexpr (NWV > 1) {
@@ -220,7 +233,7 @@ attn_core_kernel(int I, int S, int nq, int nkv, int hd, const uint16_t* __restri
         const float m2 = mls[w + h][0][lane];
         const float mm = fmaxf(m, m2);
         const float base = (mm == -INFINITY) ? 0.0f : mm;
-        const float f1 = expf(m - base), f2 = expf(m2 - base);
+        const float f1 = exp2f(m - base), f2 = exp2f(m2 - base);
         l = l * f1 + mls[w + h][1][lane] * f2;
         m = mm;
 #pragma unroll

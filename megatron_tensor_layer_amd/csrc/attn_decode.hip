@@ -93,7 +93,9 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
   const int G = nq / nkv;  // query heads per group
   const int N = (nq + 2 * nkv) * hd;
   const int len = min(max(lens[b], 1), Lmax);
-  const float scale = 1.0f / sqrtf((float)hd);
+  // scores in base 2: s = log2(e) q.k / sqrt(hd), so every exponential is
+  // one exp2 (e^z = 2^(z log2 e)); the chunk states keep their maxima in it
+  const float scale = 1.4426950408889634f / sqrtf((float)hd);
 
   // this group's cache rows, and the columns of its k and v in the qkv row
   const int64_t cache0 = ((int64_t)b * nkv + g) * Lmax * hd;
@@ -200,19 +202,19 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mnew = fmaxf(m, mx);
     const float base = (mnew == -INFINITY) ? 0.0f : mnew;
-    const float corr = expf(m - base);
+    const float corr = exp2f(m - base);
     float ps = 0.0f;
     bf16x8_t pb[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = expf(x[r] - base);
+      const float p = exp2f(x[r] - base);
       ps += p;
       pb[r >> 3][r & 7] = (__bf16)p;
     }
     ps += __shfl_xor(ps, 32, 64);
     l = l * corr + ps;
     m = mnew;
-    // O^T is rescaled by e^(m_old - m_new) only when some lane's max moved:
+    // O^T is rescaled by 2^(m_old - m_new) only when some lane's max moved:
     // otherwise the factor is exactly 1 in every lane (a wave-uniform test)
     if (__builtin_amdgcn_ballot_w64(corr != 1.0f) != 0) {
 #pragma unroll
@@ -282,7 +284,7 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
     dot += __shfl_xor(dot, 32, 64);
     const float sn = dot * scale;
     const float mnew = fmaxf(m, sn);
-    const float corr = expf(m - mnew), pn = expf(sn - mnew);
+    const float corr = exp2f(m - mnew), pn = exp2f(sn - mnew);
     l = l * corr + pn;
     m = mnew;
 #pragma unroll
@@ -319,7 +321,7 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
     const float base = (mm == -INFINITY) ? 0.0f : mm;
     float fv[NWV];
 #pragma unroll
-    for (int v = 0; v < NWV; ++v) fv[v] = expf(mls[v][0][lane] - base);
+    for (int v = 0; v < NWV; ++v) fv[v] = exp2f(mls[v][0][lane] - base);
     l = mls[0][1][lane] * fv[0];
 #pragma unroll
     for (int v = 1; v < NWV; ++v) l += mls[v][1][lane] * fv[v];
@@ -395,7 +397,7 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
   // ---- the last chunk to arrive merges the NC states.  One memory round
   //      trip: each thread first issues the loads of its (head, 4 columns)
   //      item over the first 16 chunks, then the (max, sum) pairs of every
-  //      chunk and real head go to LDS; per head the weights e^(m_c - M) and
+  //      chunk and real head go to LDS; per head the weights 2^(m_c - M) and
   //      1/sum follow, and each thread sums its columns over the chunks in
   //      chunk order (chunks past 16, if any, in further batches).
   const int64_t first = (int64_t)bg * NC * rec;
@@ -430,7 +432,7 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
     const float base = (mm == -INFINITY) ? 0.0f : mm;
     float den = 0.0f;
     for (int k = 0; k < NC; ++k) {
-      const float f = expf(mlp[2 * (k * 32 + hh)] - base);
+      const float f = exp2f(mlp[2 * (k * 32 + hh)] - base);
       fw[k * 32 + hh] = f;
       den += mlp[2 * (k * 32 + hh) + 1] * f;
     }
