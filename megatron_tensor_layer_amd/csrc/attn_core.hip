@@ -187,19 +187,14 @@ attn_core_kernel(int I, int S, int nq, int nkv, int hd, const uint16_t* __restri
 #pragma unroll
       for (int t = 0; t < HDT; ++t) {
         const int d = t * 32 + (lane & 31);
-        uint32_t v2[4];
+        typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+        u16x8_t v8;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t half[2];
-#pragma unroll
-          for (int b2 = 0; b2 < 2; ++b2) {
-            const int e = 2 * i + b2;
-            const int key = 16 * ks + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            half[b2] = Vh[(key * CPR + ((d >> 3) ^ (key & (CPR - 1)))) * 8 + (d & 7)];
-          }
-          v2[i] = half[0] | (half[1] << 16);
+        for (int e = 0; e < 8; ++e) {
+          const int key = 16 * ks + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          v8[e] = Vh[(key * CPR + ((d >> 3) ^ (key & (CPR - 1)))) * 8 + (d & 7)];
         }
-        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, u32x4_t{v2[0], v2[1], v2[2], v2[3]});
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, v8);
         ot[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ks], ot[t], 0, 0, 0);
       }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
