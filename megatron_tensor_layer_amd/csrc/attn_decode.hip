@@ -202,12 +202,12 @@ attn_decode_kernel(int nq, int nkv, int hd, int Lmax, const int* __restrict__ le
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mnew = fmaxf(m, mx);
     const float base = (mnew == -INFINITY) ? 0.0f : mnew;
-    const float corr = exp2f(m - base);
+    const float corr = __builtin_amdgcn_exp2f(m - base);
     float ps = 0.0f;
     bf16x8_t pb[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = exp2f(x[r] - base);
+      const float p = __builtin_amdgcn_exp2f(x[r] - base);
       ps += p;
       pb[r >> 3][r & 7] = (__bf16)p;
     }
