@@ -49,7 +49,10 @@ CORE = [(12, 4, 4, 2, 64), (7, 7, 2, 1, 136), (16, 16, 8, 1, 128), (5, 1, 4, 4, 
         # sequences straddling the 32-row query blocks, head_dim of 3 column tiles
         (96, 48, 4, 2, 64), (70, 35, 3, 1, 72),
         # one causal sequence of 512 tokens at the Llama-70B TP=8 head layout
-        (512, 512, 8, 1, 128)]
+        (512, 512, 8, 1, 128),
+        # blocks wholly below the diagonal (no mask) between sequence starts
+        # aligned to the key blocks, and a 1024-token sequence
+        (384, 128, 4, 2, 64), (1024, 1024, 8, 1, 128)]
 
 
 @pytest.mark.parametrize("I,S,nq,nkv,hd", CORE)
