@@ -198,7 +198,14 @@ def sample_clocks(torch, fns, samples=3):
             for f in fns:
                 f()
         torch.cuda.synchronize()
-    for _ in range(samples):
+    for k in range(samples):
+        if k:  # the clock readings refresh about once a second: space the samples
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < 1.0:
+                for _ in range(8):
+                    for f in fns:
+                        f()
+                torch.cuda.synchronize()
         proc = subprocess.Popen([exe, "metric", "-c", "--json"], stdout=subprocess.PIPE,
                                 stderr=subprocess.DEVNULL, text=True)
         t0 = time.perf_counter()
@@ -230,7 +237,8 @@ def sample_clocks(torch, fns, samples=3):
         return None
     return dict(sclk_mhz_per_xcd=sclk, mclk_mhz=mclk, sclk_spec_mhz=2400,
                 how="amd-smi metric -c --json (each sample: the 8 XCDs' current GFX "
-                    "clocks) while the 512-token TP=8 MLP calls run back to back")
+                    "clocks; samples at least 1 s apart) while the 512-token TP=8 MLP calls "
+                    "run back to back")
 
 
 def prefill_profile(torch, tp, layer, reps=20):
