@@ -498,14 +498,10 @@ hipError_t launch_hdt(int B, int nq, int nkv, int hd, int Lmax, const int* lens,
   float* part = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                      kWsCounterBytes)
                           : nullptr;
-  static bool attr_set = false;  // raising the dynamic-LDS limit once per process is enough
-  if (!attr_set) {
-    const hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(attn_decode_kernel<HDT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, dyn_lds_bytes<HDT>());
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_raised{0};
+  const hipError_t e = dyn_lds_once(reinterpret_cast<const void*>(attn_decode_kernel<HDT>),
+                                    dyn_lds_bytes<HDT>(), lds_raised);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_decode_kernel<HDT>, dim3(B * nkv * pl.nc), dim3(64 * NWV),
                      dyn_lds_bytes<HDT>(), stream,
                      nq, nkv, hd, Lmax, lens, qkv, Kc, Vc, A, pl.nc, pl.lc, counters, part);

@@ -6,9 +6,25 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 namespace tpk {
+
+// Raise a kernel's dynamic-LDS limit to `bytes` on the current device, once
+// per device: the attribute belongs to the kernel on each device.  `done`
+// keeps one bit per device already raised (a device index past 63 is raised
+// on every call).
+inline hipError_t dyn_lds_once(const void* kern, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+  if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_relaxed);
+  return e;
+}
 
 // Split-K workspace layout shared by every kernel that splits K: a fixed
 // area of 32-bit arrival counters (zero before the first use; each completed

@@ -265,12 +265,11 @@ hipError_t launch_mt(int I, int K, int N, const uint16_t* X, const void* W0, con
   // bf16: 2 groups of 128 K in flight per wave (4 measured slower); FP8: 4,
   // the same bytes in flight
   auto kern = rowstream_kernel<MT, EPI, F8 ? 4 : 2, WF>;
-  static bool attr_set = false;  // raising the dynamic-LDS limit once per process is enough
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes<MT>());
+  static std::atomic<uint64_t> lds_raised{0};
+  {
+    const hipError_t e = dyn_lds_once(reinterpret_cast<const void*>(kern), lds_bytes<MT>(),
+                                      lds_raised);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int KS = rowstream_slice(K);
   const int rpt = rowstream_rows(N, EPI == EPI_SWIGLU);

@@ -386,12 +386,11 @@ hipError_t launch_plan(const Plan& pl, int I, int K, int N, const uint16_t* X, c
   const bool small = pl.nw <= 4;
   auto kern = small ? splitk_kernel<MT, F8 ? 4 : 2, EPI, WF, 256>
                     : splitk_kernel<MT, F8 ? 4 : 2, EPI, WF, 1024>;
-  static bool attr_set[2] = {false, false};  // raising the dynamic-LDS limit once is enough
-  if (!attr_set[small]) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+  static std::atomic<uint64_t> lds_raised[2];  // per variant, one bit per device
+  {
+    const hipError_t e = dyn_lds_once(reinterpret_cast<const void*>(kern), kLdsMax,
+                                      lds_raised[small]);
     if (e != hipSuccess) return e;
-    attr_set[small] = true;
   }
   if (pl.rbs > kWsMaxCounters) return hipErrorInvalidValue;
   auto* counters = static_cast<unsigned*>(workspace);
