@@ -58,6 +58,7 @@ def _run(qkv, Kc, Vc, lens, nq, nkv, hd, workspace=None):
     (2, 8, 1, 128, 1000, 7),     # the last chunk's round partly past the cache
     (32, 8, 1, 128, 2144, 8),    # three rounds per chunk, the last one a single block
     (16, 8, 2, 64, 1600, 9),     # two groups, rounds of 128 and 96 positions
+    (4, 32, 1, 128, 200, 10),    # 32 heads in one group and head_dim 128: the largest
 ])
 def test_attn_decode(orc, B, nq, nkv, hd, Lmax, seed):
     rng = np.random.default_rng(seed)

@@ -35,6 +35,8 @@ SMALL = [
     (1, 264, 200, 2, 1, "bf16"), (2, 264, 200, 2, 0, "bf16"), (3, 136, 72, 1, 0, "bf16"),
     (5, 520, 136, 4, 3, "bf16"), (8, 264, 200, 2, 1, "bf16"), (4, 16384, 64, 1, 0, "bf16"),
     (1, 24576, 32, 1, 0, "bf16"), (6, 24576, 32, 1, 0, "bf16"),
+    # the few-token kernel's longest K: 32768 (bf16) and 16384 (fp32)
+    (2, 32768, 16, 1, 0, "bf16"), (3, 16384, 16, 1, 0, "f32"),
     (9, 264, 200, 2, 1, "bf16"), (17, 520, 328, 1, 0, "bf16"), (40, 264, 200, 2, 0, "bf16"),
     (64, 136, 72, 2, 1, "bf16"), (65, 264, 200, 1, 0, "bf16"), (130, 520, 136, 2, 1, "bf16"),
     (257, 264, 200, 2, 1, "bf16"), (33, 72, 24, 2, 1, "bf16"), (48, 1000, 1000, 1, 0, "bf16"),
