@@ -248,8 +248,14 @@ splitk_kernel(int I, int K, int N, const uint16_t* __restrict__ X,
         for (int e = 0; e < n; ++e) o[e] = v[e];
       }
     } else {
+      // 4 columns as one 8-byte store where aligned (the finish ends the
+      // kernel, so its store count is on the critical path)
       uint16_t* o = static_cast<uint16_t*>(out) + (int64_t)m * ldo + cbase + c;
-      for (int e = 0; e < n; ++e) o[e] = f32_to_bf16_bits(v[e]);
+      if (n == 4 && ((reinterpret_cast<uintptr_t>(o) & 7) == 0)) {
+        *reinterpret_cast<u32x2_t*>(o) = u32x2_t{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+      } else {
+        for (int e = 0; e < n; ++e) o[e] = f32_to_bf16_bits(v[e]);
+      }
     }
   };
   if constexpr (MAXT <= 256 && EPI != EPI_SWIGLU && !F8) {
