@@ -29,6 +29,11 @@
 //     partials in split order (deterministic) and applies the epilogue.
 //     Partials cross XCDs, whose L2s are not coherent, so they are written
 //     and read system-coherent; the arrival counter is one device atomic;
+//   * with more than one round of tiles and a last round at most half full
+//     (the unsharded gate/up at 512 tokens: 896 tiles), the whole rounds run
+//     as one launch with K unsplit and the last round's tiles as a second
+//     launch with K split, so that it fills the chip; each launch takes its
+//     range of tiles (tile0, ntl);
 //   * workgroups go round-robin to the 8 XCDs; the block id is remapped so
 //     that each XCD runs a contiguous range of tiles, and tiles sharing a W
 //     block (same N block, other M blocks) are neighbours in that range.
@@ -206,7 +211,7 @@ __global__ void __launch_bounds__(kThreads)
 gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
             const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
             void* __restrict__ out, int64_t ldo, int KR, unsigned* __restrict__ counters,
-            float* __restrict__ part) {
+            float* __restrict__ part, int tile0, int ntl) {
   // S stages of (A tile, W tile); after the K loop the same memory holds
   // the K-group reduction and the split-K arrival flag
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLds];
@@ -218,16 +223,15 @@ gemm_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
   // ---- tile and split of this workgroup, XCD-aware
   const int mt_n = (M + BM - 1) / BM;
   constexpr int kCols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;  // output columns per tile
-  const int nt_n = (N + kCols - 1) / kCols;
-  const int tiles = mt_n * nt_n;
+  const int tiles = ntl;  // this launch's tiles: tile0 .. tile0 + ntl - 1 of the product
   const int ns = (K + KR - 1) / KR;
   const int G = tiles * ns;
   int b = blockIdx.x;
   const int G8 = G & ~7;
   if (b < G8) b = (b & 7) * (G8 >> 3) + (b >> 3);
   const int split = b / tiles;
-  const int tile = b % tiles;
-  const int tm = tile % mt_n, tn = tile / mt_n;
+  const int tile = b % tiles;  // within the launch: arrival counter and partial slot
+  const int tm = (tile0 + tile) % mt_n, tn = (tile0 + tile) / mt_n;
   const int m0 = tm * BM, c0 = tn * kCols;
   const int kb = split * KR, ke = min(K, kb + KR);
 
@@ -433,7 +437,7 @@ __global__ void __launch_bounds__(kThreads)
 gemm_wide_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t lda,
                  const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1,
                  void* __restrict__ out, int64_t ldo, int KR, unsigned* __restrict__ counters,
-                 float* __restrict__ part) {
+                 float* __restrict__ part, int tile0, int ntl) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsW];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -442,16 +446,15 @@ gemm_wide_kernel(int M, int N, int K, const uint16_t* __restrict__ A, int64_t ld
 
   const int mt_n = (M + WM - 1) / WM;
   constexpr int kCols = (EPI == EPI_SWIGLU) ? WN / 2 : WN;  // output columns per tile
-  const int nt_n = (N + kCols - 1) / kCols;
-  const int tiles = mt_n * nt_n;
+  const int tiles = ntl;  // this launch's tiles: tile0 .. tile0 + ntl - 1 of the product
   const int ns = (K + KR - 1) / KR;
   const int G = tiles * ns;
   int b = blockIdx.x;
   const int G8 = G & ~7;
   if (b < G8) b = (b & 7) * (G8 >> 3) + (b >> 3);
   const int split = b / tiles;
-  const int tile = b % tiles;
-  const int tm = tile % mt_n, tn = tile / mt_n;
+  const int tile = b % tiles;  // within the launch: arrival counter and partial slot
+  const int tm = (tile0 + tile) % mt_n, tn = (tile0 + tile) / mt_n;
   const int m0 = tm * WM, c0 = tn * kCols;
   const int kb = split * KR, ke = min(K, kb + KR);
 
@@ -853,6 +856,13 @@ struct Plan {
   int kr = 0;  // K per split
   int grid = 0;
   int tile_elems = 0;
+  // Split tail: with ns == 1 and more than one round of tiles, the last
+  // `tail` tiles may run as a second launch with K split tail_ns ways, so
+  // that a partial last round fills every CU (the first launch runs whole
+  // rounds).  0: one launch.
+  int tail = 0;
+  int tail_ns = 0;
+  int tail_kr = 0;
 };
 
 struct TileShape {
@@ -890,12 +900,21 @@ double plan_cost(int tiles, int ns, const TileShape& t, int K) {
   return rounds * (std::max(copy, mfma) + write) + reduce + 1500.0;
 }
 
+// K range of `ns` splits: whole stages, the last split possibly shorter.
+int split_kr(int K, int bk, int ns) {
+  const int kst = (K + bk - 1) / bk;
+  return (kst + ns - 1) / ns * bk;
+}
+
 // Split K when the tiles alone leave CUs idle: the tile shape and split
 // count of least modelled cost; at least 8 stages per split, at most 256 MB
 // of partials and one arrival counter per tile.  The 256-row shape needs
-// M >= 384 (enough rows to fill most of a tile).
+// M >= 384 (enough rows to fill most of a tile).  With `tail`, a plan of
+// whole rounds plus a partial one may split only the partial round's tiles
+// (a second launch), at the same limits.
 constexpr double kMaxPartialBytes = 256.0 * 1024 * 1024;
-Plan make_plan_over(const TileShape* shapes, int nshapes, int M, int N, int K, bool swiglu) {
+Plan make_plan_over(const TileShape* shapes, int nshapes, int M, int N, int K, bool swiglu,
+                    bool tail = false) {
   Plan best_pl;
   double best = 1e300;
   for (int shape = 0; shape < nshapes; ++shape) {
@@ -913,21 +932,42 @@ Plan make_plan_over(const TileShape* shapes, int nshapes, int M, int N, int K, b
         best_pl.shape = shape;
         best_pl.tiles = tiles;
         best_pl.ns = ns;
+        best_pl.tail = best_pl.tail_ns = 0;
+      }
+    }
+    const int rounds = (tiles + kCUs - 1) / kCUs;
+    const int rest = tiles - (rounds - 1) * kCUs;  // tiles of the last round
+    if (tail && rounds > 1 && 2 * rest <= kCUs && rest <= kWsMaxCounters) {
+      const double whole = plan_cost((rounds - 1) * kCUs, 1, t, K);
+      for (int ns = 2; ns <= max_ns && ns * rest <= kCUs; ++ns) {
+        if ((double)ns * rest * t.bm * t.bn * 4.0 > kMaxPartialBytes) break;
+        const double cost = whole + plan_cost(rest, ns, t, K);
+        if (cost < best * (1.0 - 1e-9)) {
+          best = cost;
+          best_pl.shape = shape;
+          best_pl.tiles = tiles;
+          best_pl.ns = 1;
+          best_pl.tail = rest;
+          best_pl.tail_ns = ns;
+        }
       }
     }
   }
   const TileShape& t = shapes[best_pl.shape];
-  const int kst = (K + t.bk - 1) / t.bk;                // K stages in all
-  const int sps = (kst + best_pl.ns - 1) / best_pl.ns;  // stages per split
-  best_pl.kr = sps * t.bk;
+  best_pl.kr = split_kr(K, t.bk, best_pl.ns);
   best_pl.ns = (K + best_pl.kr - 1) / best_pl.kr;
   best_pl.grid = best_pl.tiles * best_pl.ns;
   best_pl.tile_elems = t.bm * t.bn;
+  if (best_pl.tail) {
+    best_pl.tail_kr = split_kr(K, t.bk, best_pl.tail_ns);
+    best_pl.tail_ns = (K + best_pl.tail_kr - 1) / best_pl.tail_kr;
+    best_pl.grid = best_pl.tiles - best_pl.tail + best_pl.tail * best_pl.tail_ns;
+  }
   return best_pl;
 }
 
 Plan make_plan(int M, int N, int K, bool swiglu) {
-  return make_plan_over(kShapes, kNumShapes, M, N, K, swiglu);
+  return make_plan_over(kShapes, kNumShapes, M, N, K, swiglu, true);
 }
 
 Plan make_plan_q8(int M, int N, int K, bool swiglu) {
@@ -935,6 +975,7 @@ Plan make_plan_q8(int M, int N, int K, bool swiglu) {
 }
 
 size_t plan_bytes(const Plan& pl) {
+  if (pl.tail) return kWsCounterBytes + (size_t)pl.tail_ns * pl.tail * pl.tile_elems * sizeof(float);
   if (pl.ns <= 1) return 0;
   return kWsCounterBytes + (size_t)pl.ns * pl.tiles * pl.tile_elems * sizeof(float);
 }
@@ -943,8 +984,9 @@ size_t plan_bytes(const Plan& pl) {
 hipError_t split_buffers(const Plan& pl, void* workspace, unsigned** counters, float** part) {
   *counters = nullptr;
   *part = nullptr;
-  if (pl.ns <= 1) return hipSuccess;
-  if (workspace == nullptr || pl.tiles > kWsMaxCounters) return hipErrorInvalidValue;
+  if (pl.ns <= 1 && pl.tail == 0) return hipSuccess;
+  if (workspace == nullptr || (pl.tail ? pl.tail : pl.tiles) > kWsMaxCounters)
+    return hipErrorInvalidValue;
   *counters = static_cast<unsigned*>(workspace);
   *part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWsCounterBytes);
   return hipSuccess;
@@ -958,8 +1000,15 @@ hipError_t launch_plan(const Plan& pl, int M, int N, int K, const uint16_t* A, i
   unsigned* counters;
   float* part;
   if (split_buffers(pl, workspace, &counters, &part) != hipSuccess) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(kThreads), 0, stream, M, N, K, A, lda, W0, W1,
-                     out, ldo, pl.kr, counters, part);
+  const int head = pl.tiles - pl.tail;  // tiles of the first launch (K unsplit if tail)
+  hipLaunchKernelGGL(kern, dim3(head * pl.ns), dim3(kThreads), 0, stream, M, N, K, A, lda, W0,
+                     W1, out, ldo, pl.kr, counters, part, 0, head);
+  if (pl.tail) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(pl.tail * pl.tail_ns), dim3(kThreads), 0, stream, M, N, K, A,
+                       lda, W0, W1, out, ldo, pl.tail_kr, counters, part, head, pl.tail);
+  }
   return hipGetLastError();
 }
 

@@ -42,6 +42,19 @@ def test_qwen_attn_projections_tp2(orc, I):
     assert normwise_err(to_host(Y), orc.oproj_rank(A, Wo, n_q, hd)) <= TOL
 
 
+def test_qkv_split_tail(orc):
+    """A QKV projection of 320 GEMM tiles (130 tokens, N_qkv = 160 heads x
+    128): 256 tiles in one launch, the last 64 with K split in a second."""
+    I, D, n_q, n_kv, hd = 130, 1040, 144, 8, 128
+    X = datagen.gaussian("X", (I, D), 1.0, "bf16", 310)
+    Wq, Wk, Wv, _ = datagen.attn_weights(D, n_q, n_kv, hd, "bf16", 310)
+    W = datagen.qkv_rank_shard(Wq, Wk, Wv, n_q, n_kv, hd, 1, 0)
+    out = empty((I, W.shape[0]), "bf16")
+    tp.shard_attn_proj(tp.TP_ATTN_QKV, to_dev(X, "bf16"), to_dev(W, "bf16"), out, n_q, n_kv, hd)
+    torch().cuda.synchronize()
+    assert normwise_err(to_host(out), orc.qkv_rank(X, Wq, Wk, Wv, n_q, n_kv, hd, 1, 0)) <= TOL
+
+
 # (I, S, n_q_local, n_kv_local, head_dim): several sequences, GQA groups,
 # head_dim below one wavefront, and above two (lanes holding 3 elements)
 CORE = [(12, 4, 4, 2, 64), (7, 7, 2, 1, 136), (16, 16, 8, 1, 128), (5, 1, 4, 4, 32),

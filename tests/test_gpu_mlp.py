@@ -56,6 +56,10 @@ SMALL = [
     # range (K = 520, ragged last stage) and split 5 ways
     (384, 1040, 6152, 1, 0, "bf16"), (390, 3080, 2064, 1, 0, "bf16"),
     (390, 8200, 520, 1, 0, "bf16"), (390, 3080, 8200, 1, 0, "bf16"),
+    # more than one round of GEMM tiles with a partial last round: whole
+    # rounds in one launch, the last round's tiles split over K in a second
+    # (gate/up: 300 128 x 128 tiles, then 532 256 x 128 tiles)
+    (130, 1040, 9600, 1, 0, "bf16"), (390, 1040, 17000, 1, 0, "bf16"),
 ]
 
 
