@@ -39,7 +39,8 @@ constexpr int kAuxSys = 17;             // sc0 sc1: system coherent
 constexpr int NWV = 4;
 constexpr int kMaxChunks = 32;  // position chunks per (sequence, group)
 // one per CU: measured faster than two per CU (fewer chunk states to write
-// and merge) -- B = 32, L = 2048: 21.2 us against 22.9; L = 8192: 37.8 against 41.6
+// and merge) and than fewer -- B = 32 at L = 2048 / 8192: 14.7 / 31.6 us,
+// against 23.4 / 40.3 with 512 workgroups and 17.0 / 42.1 with 128
 constexpr int kTargetWgs = 256;
 constexpr int kRP = 32 * NWV;   // positions per round: one block of 32 per wave
 constexpr int kRowB = 256;      // LDS bytes per staged row: 16 slots of 16 bytes
