@@ -91,11 +91,10 @@ size_t tp_shard_mlp_workspace_size(int64_t I, int64_t D, int64_t F_local, tp_dty
  *   workspace, workspace_bytes: device scratch of at least
  *           tp_shard_mlp_workspace_size(...) bytes, 16-byte aligned, not
  *           overlapping any other argument (may be NULL when the size is 0).
- *           bf16 calls that split K over workgroups (from 9 tokens, by
- *           shape: wherever the tiles alone leave CUs idle, including
- *           prefill shapes) keep arrival counters and fp32 partial sums
- *           there.  The
- *           first 8 KiB (the counters) must be zero before the workspace's
+ *           bf16 calls that split K over workgroups (from 5 tokens, by
+ *           shape: wherever the tiles alone leave CUs idle, prefill shapes
+ *           included) keep arrival counters and fp32 partial sums there.
+ *           The first 8 KiB (the counters) must be zero before the workspace's
  *           first use (tp_workspace_reset, once after allocating it); every
  *           completed call leaves them zero again, so one workspace serves
  *           any sequence of calls on one stream.  Counters left non-zero (a
