@@ -255,6 +255,29 @@ def test_mlp_deterministic(llama_mlp):
         assert T.equal(outs[0][0], outs[1][0]) and T.equal(outs[0][1], outs[1][1]), I
 
 
+def test_split_tail_deterministic():
+    """The GEMM plan whose last partial round of tiles runs as a second,
+    split-K launch (130 tokens: 300 gate/up tiles) gives the same bits on
+    every call, with the binding's workspace and with a fresh one."""
+    T = torch()
+    I, D, F = 130, 1040, 9600
+    X = to_dev(datagen.gaussian("X", (I, D), 1.0, "bf16", 21), "bf16")
+    Wg, Wu, Wd = (to_dev(w, "bf16") for w in datagen.mlp_weights(D, F, "bf16", 21))
+    need = tp.mlp_workspace_bytes(I, D, F)
+    assert need > COUNTER_BYTES
+    fresh = T.zeros((need // 4 + 4,), dtype=T.int32, device="cuda")
+    outs = []
+    for ws in (None, None, fresh):
+        H = empty((I, F), "bf16")
+        P = empty((I, D), "f32")
+        tp.shard_mlp(X, Wg, Wu, Wd, H, P, workspace=ws)
+        outs.append((H, P))
+    T.cuda.synchronize()
+    for o in outs[1:]:
+        assert T.equal(outs[0][0], o[0]) and T.equal(outs[0][1], o[1])
+    assert int(fresh[:COUNTER_BYTES // 4].abs().sum()) == 0
+
+
 def test_mlp_empty_and_errors_touch_nothing():
     """I = 0 is a no-op; a rejected call launches nothing (canaries survive)."""
     T = torch()
