@@ -85,6 +85,10 @@ def parse():
     ap.add_argument("--decode-profile", action="store_true",
                     help="for rocprofv3: the TP=8 rank's MLP at 1, 8, 32, 128 and 512 tokens "
                          "with bf16, FP8 and int8 weights, each in a phase of its own, no timing")
+    ap.add_argument("--attn-profile", action="store_true",
+                    help="for rocprofv3: one calibration copy of COPY_MIB MiB, then decode "
+                         "attention of a TP=8 rank (B = 32) at 2048 and 8192 positions, "
+                         "each in a phase of its own, no timing")
     ap.add_argument("--ingest-prefill-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the FETCH_SIZE and WRITE_SIZE passes over --prefill-profile "
                          "into the 512-token MLP entry of profiles/traffic.json")
@@ -321,6 +325,41 @@ def decode_profile(torch, tp, layer, reps=16):
             for k in range(reps):
                 call(X, *ranks[k % TP], H, P)
             T.cuda.synchronize()
+    log("profile phases done")
+
+
+ATTN_PROFILE_L = (2048, 8192)
+
+
+def attn_profile(torch, tp, reps=8):
+    """For rocprofv3: a plain copy of known size (the FETCH_SIZE / WRITE_SIZE
+    calibration), then tp_attn_decode of a TP=8 rank (32 sequences, 8 query
+    heads, 1 KV group, head_dim 128) at full cache length, reps calls per
+    length rotating over cache copies larger than the Infinity Cache."""
+    T = torch
+    n = COPY_MIB * 2**20 // 4
+    src = T.ones(n, dtype=T.float32, device="cuda")
+    dst = T.empty_like(src)
+    T.cuda.synchronize()
+    T.mul(src, 1.0, out=dst)
+    T.cuda.synchronize()
+    del src, dst
+    B, nql, nkl = 32, NQ // TP, NKV // TP
+    qkv = to_dev(T, datagen.gaussian("A", (B, (nql + 2 * nkl) * HD), 1.0, "bf16", 4700))
+    A = T.empty((B, nql * HD), dtype=T.bfloat16, device="cuda")
+    for L in ATTN_PROFILE_L:
+        cache_b = B * nkl * L * HD * 2
+        copies = max(2, -(-300_000_000 // (2 * cache_b)))
+        caches = [(T.randn((B, nkl, L, HD), device="cuda").to(T.bfloat16),
+                   T.randn((B, nkl, HD, L), device="cuda").to(T.bfloat16)) for _ in range(copies)]
+        lens = T.full((B,), L, dtype=T.int32, device="cuda")
+        T.cuda.synchronize()
+        log(f"profile phase: decode attention B=32 L={L}")
+        for k in range(reps):
+            kv = caches[k % copies]
+            tp.attn_decode(lens, qkv, kv[0], kv[1], A, nql, nkl, HD)
+        T.cuda.synchronize()
+        del caches
     log("profile phases done")
 
 
@@ -852,6 +891,9 @@ def main():
         return
     if args.decode_profile:
         decode_profile(torch, tp, layer)
+        return
+    if args.attn_profile:
+        attn_profile(torch, tp)
         return
     Xh = datagen.gaussian("X", (I, D), 1.0, "bf16", 42)
     X = to_dev(torch, Xh)
